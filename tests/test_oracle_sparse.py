@@ -1,0 +1,146 @@
+"""Pins of the oracle's block-sparse edge forward (alice-llm sparse_attention_forward.wgsl).
+
+Merged over each (q_idx, h) group, the per-edge partials must equal dense softmax attention of
+the query over the union of its edges' mapped keys; torch SDPA in float64 is the reference.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from block_sparse_gqa_paged_amd import workloads as W
+
+
+def _sw(seed, all_blocks=False, unmapped=0.0, **kw):
+    args = dict(Tq=12, hkv=2, qhead=2, head_dim=32, block_size=16, page_size=4, batch=2,
+                key_capacity=96, window=2, p_random=0.3, unmapped_frac=unmapped,
+                all_blocks=all_blocks, name="tiny_sparse")
+    args.update(kw)
+    return W.sparse_workload(seed, **args)
+
+
+def _key_position_rows(sw, b, h):
+    """K, V rows [key_capacity, D] of batch b, kv head h in key-position order, plus a mapped
+    mask (page id >= 0)."""
+    ps, ppb = sw["page_size"], sw["pages_per_block"]
+    cap = sw["max_pages"] * ps
+    K = np.zeros((cap, sw["D"]))
+    V = np.zeros((cap, sw["D"]))
+    mapped = np.zeros(cap, dtype=bool)
+    for slot in range(sw["max_pages"]):
+        pid = sw["block_tables"][b, slot]
+        if pid < 0:
+            continue
+        K[slot * ps:(slot + 1) * ps] = sw["k_pages"][pid, h]
+        V[slot * ps:(slot + 1) * ps] = sw["v_pages"][pid, h]
+        mapped[slot * ps:(slot + 1) * ps] = True
+    del ppb
+    return K, V, mapped
+
+
+def _dense_reference(sw):
+    """For each (q, h) group: SDPA over the keys its edges cover (t < block_len of each edge's
+    block) that sit on mapped pages. Returns [Tq, hq, D] float64."""
+    out = np.zeros((sw["Tq"], sw["hq"], sw["D"]))
+    em = sw["edge_meta"]
+    gp = sw["group_ptr"]
+    bs = sw["block_size"]
+    cache = {}
+    for q in range(sw["Tq"]):
+        for h in range(sw["hkv"]):
+            edges = em[gp[q * sw["hkv"] + h]:gp[q * sw["hkv"] + h + 1]]
+            if len(edges) == 0:
+                continue
+            b = int(edges[0, 3])
+            if (b, h) not in cache:
+                cache[(b, h)] = _key_position_rows(sw, b, h)
+            K, V, mapped = cache[(b, h)]
+            sel = np.zeros(K.shape[0], dtype=bool)
+            for (_, _, blk, _, blen) in edges:
+                sel[blk * bs: blk * bs + max(0, blen)] = True
+            sel &= mapped
+            if not sel.any():
+                continue
+            qv = torch.from_numpy(sw["q_buf"][q, h * sw["qhead"]:(h + 1) * sw["qhead"]]
+                                  .astype(np.float64))[:, None, :]           # [qhead, 1, D]
+            k = torch.from_numpy(K[sel])[None].expand(sw["qhead"], -1, -1)
+            v = torch.from_numpy(V[sel])[None].expand(sw["qhead"], -1, -1)
+            o = F.scaled_dot_product_attention(qv, k, v, scale=sw["softmax_scale"])
+            out[q, h * sw["qhead"]:(h + 1) * sw["qhead"]] = o[:, 0].numpy()
+    return out
+
+
+def _merge(oracle, sw, o, m, l):
+    return oracle.split_combine(o, m, l, lanes=sw["qhead"], head_dim=sw["D"],
+                                group_ptr=sw["group_ptr"], out_dtype=np.float32)
+
+
+@pytest.mark.parametrize("all_blocks,unmapped", [(True, 0.0), (True, 0.2), (False, 0.0),
+                                                 (False, 0.15)])
+def test_merged_partials_equal_dense_attention(oracle, all_blocks, unmapped):
+    sw = _sw(50, all_blocks=all_blocks, unmapped=unmapped)
+    o, m, l = oracle.sparse_forward(sw)
+    merged = _merge(oracle, sw, o, m, l).reshape(sw["Tq"], sw["hq"], sw["D"])
+    ref = _dense_reference(sw)
+    assert np.allclose(merged, ref, rtol=1e-5, atol=1e-6)
+
+
+def test_zero_length_and_unmapped_blocks_give_sentinel(oracle):
+    sw = _sw(51, all_blocks=True)
+    em = sw["edge_meta"].copy()
+    em[0, 4] = 0           # block_len 0
+    em[1, 4] = -3          # negative block_len behaves as 0
+    bt = sw["block_tables"].copy()
+    b, blk = em[2, 3], em[2, 2]
+    ppb = sw["pages_per_block"]
+    bt[b, blk * ppb:(blk + 1) * ppb] = -1    # every page of edge 2's block unmapped
+    o, m, l = oracle.sparse_forward(sw, edge_meta=em, block_tables=bt)
+    for e in (0, 1, 2):
+        p = slice(e * sw["qhead"], (e + 1) * sw["qhead"])
+        assert np.all(m[p] == np.float32(-1e30))
+        assert np.all(l[p] == 0) and np.all(o[p] == 0)
+
+
+def test_single_key_block_returns_that_value(oracle):
+    """block_len = 1: m is that key's score, l = exp(0) = 1, o is its value row exactly."""
+    sw = _sw(52, all_blocks=True)
+    em = sw["edge_meta"].copy()
+    em[:, 4] = 1
+    o, m, l = oracle.sparse_forward(sw, edge_meta=em)
+    ps = sw["page_size"]
+    ppb = sw["pages_per_block"]
+    for e in range(0, em.shape[0], 7):
+        q_idx, h, blk, b, _ = em[e]
+        pid = sw["block_tables"][b, blk * ppb]
+        for qh in range(sw["qhead"]):
+            p = e * sw["qhead"] + qh
+            if pid < 0:
+                assert m[p] == np.float32(-1e30) and l[p] == 0
+                continue
+            assert l[p] == 1.0
+            assert np.array_equal(o[p], sw["v_pages"][pid, h, 0])
+            s = float(np.dot(sw["q_buf"][q_idx, h * sw["qhead"] + qh].astype(np.float64),
+                             sw["k_pages"][pid, h, 0].astype(np.float64))) * sw["softmax_scale"]
+            assert m[p] == np.float32(s)
+    del ps
+
+
+def test_partials_are_block_local(oracle):
+    """Each partial's m is the max score inside its own block: shifting one block's keys so all
+    its scores rise leaves every other edge's partial unchanged."""
+    sw = _sw(53, all_blocks=True)
+    o, m, l = oracle.sparse_forward(sw)
+    sw2 = dict(sw)
+    sw2["k_pages"] = sw["k_pages"].copy()
+    em = sw["edge_meta"]
+    b, blk, h = em[0, 3], em[0, 2], em[0, 1]
+    ppb = sw["pages_per_block"]
+    for slot in range(blk * ppb, (blk + 1) * ppb):
+        pid = sw["block_tables"][b, slot]
+        if pid >= 0:
+            sw2["k_pages"][pid, h] *= 3.0
+    o2, m2, l2 = oracle.sparse_forward(sw2)
+    touched = (em[:, 3] == b) & (em[:, 2] == blk) & (em[:, 1] == h)
+    rows = np.repeat(~touched, sw["qhead"])
+    assert np.array_equal(o[rows], o2[rows]) and np.array_equal(m[rows], m2[rows])
+    assert np.array_equal(l[rows], l2[rows])
