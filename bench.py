@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark: paged GQA decode step on one MI355X.
+
+A step is one pass of the hot path over the batch-64 GQA serving-decode workload (B=64, H=32,
+G=8, D=128, bs=16, past ~ U[512, 8192], seed 2): pa_kv_append of the 64 new K/V rows, then
+pa_paged_attention (device planner, split-KV decode kernel, log-sum-exp combine). Inputs are
+resident in HBM before timing starts.
+
+Printed: ONE JSON line. `value` is the step's KV-cache read rate (sum_b L_b * G * D * 2 * 2
+bytes per step / step time) in GB/s; `query_tokens_per_s` sits beside it. `roofline` is the
+decode attention kernel alone: algorithmic KV bytes per launch / its mean launch time from HIP
+events recorded by the library on the launch stream, against 8 TB/s. `cpu_baseline` times the
+CPU oracle on the same workload's attention rows. `extra` carries the mixed prefill+decode and
+block-sparse workloads.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFS = 2500.0
+FP32_MFMA_PEAK_TFS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip mixed and sparse workloads")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (for counter calibration runs)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_gqa_paged_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on the current kernels."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def timed(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / steps, wall
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_gqa_paged_amd as pa
+    from block_sparse_gqa_paged_amd import device as dev
+    from block_sparse_gqa_paged_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    print("# generating the batch-64 GQA decode workload", file=sys.stderr, flush=True)
+    w = W.gqa_decode()
+    kv = W.kv_bytes(w)
+    c = dev.PagedCase(w)
+
+    def step():
+        c.append()
+        c.attention(pa.PA_SPLITS_AUTO)
+
+    pa.pa_timing_reset()
+    pa.pa_timing_enable(True)
+    ms, wall = timed(step, args.steps, args.warmup, torch)
+    pa.pa_timing_enable(False)
+    n_launch = args.steps + args.warmup
+    kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "attn_prefill",
+                                           "combine")}
+    pa.pa_timing_reset()
+    # the same steps without the library's event records, for the step time itself
+    ms_plain, _ = timed(step, args.steps, args.warmup, torch)
+    print(f"# step {ms_plain:.4f} ms (with event hooks {ms:.4f} ms)", file=sys.stderr, flush=True)
+
+    dec_ms = kt["attn_decode"][0] / max(1, kt["attn_decode"][1])
+    achieved = kv / (dec_ms * 1e-3) / 1e9
+    value = kv / (ms_plain * 1e-3) / 1e9
+    per_kernel = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        print("# timing the CPU oracle on the same attention rows", file=sys.stderr, flush=True)
+        kc = c.key_cache.cpu().numpy()
+        vc = c.value_cache.cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.paged_attention(w, kc, vc)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"all {w['T']} decode rows x {w['H']} heads of the workload, "
+                         f"attention only, {dt:.1f} s single-threaded"}
+
+    extra = {}
+    if not args.no_extra:
+        extra = run_extra(args, torch, np, pa, dev, W)
+
+    line = {
+        "metric": "paged-attn decode KV GB/s (% of HBM peak) and query tokens/s, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "query_tokens_per_s": round(w["T"] / (ms_plain * 1e-3), 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_plain, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "batch": w["B"], "num_heads": w["H"],
+                   "kv_num_heads": w["G"], "head_size": w["D"], "block_size": w["bs"],
+                   "past_seqlens": "uniform [512, 8192], seed 2", "kv_bytes_per_step": kv,
+                   "num_splits": "auto", "parallelism": "none (1 GPU)"},
+        "kernel_us": per_kernel,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles("attn_decode"),
+                     "kernel": "attn_decode", "kernel_us": round(dec_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_extra(args, torch, np, pa, dev, W):
+    out = {}
+    steps = max(3, args.steps // 5)
+    print("# generating the mixed prefill+decode workload", file=sys.stderr, flush=True)
+    w = W.mixed_prefill_decode()
+    c = dev.PagedCase(w)
+    kv = W.kv_bytes(w)
+    pa.pa_timing_reset()
+    pa.pa_timing_enable(True)
+    ms, _ = timed(lambda: (c.append(), c.attention(pa.PA_SPLITS_AUTO)), steps, 2, torch)
+    pa.pa_timing_enable(False)
+    kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "attn_prefill",
+                                           "combine")}
+    pa.pa_timing_reset()
+    us = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
+    # prefill flops: causal QK^T and PV over the prefill rows, 4*D per (row, head, key)
+    L = w["past"].astype(np.int64)
+    n = np.diff(w["cu"]).astype(np.int64)
+    flops = 0
+    for b in range(w["B"]):
+        if n[b] > 1:
+            keys = L[b] + np.arange(1, n[b] + 1)
+            flops += int(keys.sum()) * w["H"] * w["D"] * 4
+    app_bytes = w["T"] * w["G"] * w["D"] * 2 * 4 + w["T"] * (w["rotary_dim"] // 2) * 2 * 2
+    out["mixed_prefill_decode"] = {
+        "workload": w["name"], "ms_per_step": round(ms, 4), "kernel_us": us,
+        "kv_bytes": kv, "step_kv_GBps": round(kv / (ms * 1e-3) / 1e9, 1),
+        "prefill_TFLOPs": round(flops / (us.get("attn_prefill", 1e9) * 1e-6) / 1e12, 2),
+        "prefill_mfma_frac": round(flops / (us.get("attn_prefill", 1e9) * 1e-6) / 1e12
+                                   / MFMA_F16_PEAK_TFS, 4),
+        "append_GBps": round(app_bytes / (us.get("kv_append", 1e9) * 1e-6) / 1e9, 1),
+        "append_bytes": app_bytes,
+    }
+    del c
+    torch.cuda.empty_cache()
+
+    print("# generating the block-sparse workload", file=sys.stderr, flush=True)
+    sw = W.block_sparse_forward()
+    s = dev.SparseCase(sw)
+    pa.pa_timing_reset()
+    pa.pa_timing_enable(True)
+    ms, _ = timed(lambda: (s.forward(), s.combine()), steps, 1, torch)
+    pa.pa_timing_enable(False)
+    kt = {k: pa.pa_timing_get(k) for k in ("sparse_forward", "combine")}
+    pa.pa_timing_reset()
+    us = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
+    E, q, D = sw["E"], sw["qhead"], sw["D"]
+    part_bytes = E * q * (D + 2) * 4
+    rows = sw["Tq"] * sw["hq"]
+    comb_bytes = part_bytes + rows * D * 4 + (len(sw["group_ptr"])) * 4
+    # flops over mapped keys: 4*D per (edge lane, key)
+    em = sw["edge_meta"]
+    ppb = sw["pages_per_block"]
+    mapped = (sw["block_tables"] >= 0)
+    mk = 0
+    blen = em[:, 4].astype(np.int64)
+    for t in range(sw["block_size"]):
+        ok = (blen > t) & mapped[em[:, 3], em[:, 2] * ppb + t // sw["page_size"]]
+        mk += int(ok.sum())
+    flops = mk * q * D * 4
+    out["block_sparse"] = {
+        "workload": sw["name"], "edges": E, "ms_per_step": round(ms, 4), "kernel_us": us,
+        "combine_GBps": round(comb_bytes / (us.get("combine", 1e9) * 1e-6) / 1e9, 1),
+        "combine_bytes": comb_bytes,
+        "combine_pct_hbm": round(100 * comb_bytes / (us.get("combine", 1e9) * 1e-6) / 1e9
+                                 / HBM_PEAK_GBS, 2),
+        "forward_TFLOPs": round(flops / (us.get("sparse_forward", 1e9) * 1e-6) / 1e12, 2),
+        "forward_frac_fp32_mfma": round(flops / (us.get("sparse_forward", 1e9) * 1e-6) / 1e12
+                                        / FP32_MFMA_PEAK_TFS, 4),
+        "forward_flops": flops,
+    }
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = 2 * a.numel() * 4
+    return out
+
+
+if __name__ == "__main__":
+    main()

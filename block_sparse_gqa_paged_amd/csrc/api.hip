@@ -1,0 +1,472 @@
+// C entry points of libpa: argument checks, workspace layout, split policy and launches.
+// Every check runs before anything is enqueued; device-resident index contents are the
+// caller's contract (see include/pa.h).
+#include <math.h>
+
+#include <algorithm>
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------------------------------------
+// Timing hooks
+// ---------------------------------------------------------------------------------------------
+namespace {
+struct TimingRec {
+    std::string name;
+    hipEvent_t start, stop;
+};
+std::atomic<int> g_timing{0};
+std::mutex g_timing_mu;
+std::vector<TimingRec> g_pending;
+std::map<std::string, std::pair<double, int64_t>> g_done;
+}  // namespace
+
+LaunchScope::LaunchScope(const char *name, hipStream_t stream)
+    : name_(name), stream_(stream), start_(nullptr) {
+    if (!g_timing.load(std::memory_order_relaxed)) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    (void)hipEventRecord(e, stream);
+    start_ = e;
+}
+
+LaunchScope::~LaunchScope() {
+    if (!start_) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipEventDestroy((hipEvent_t)start_);
+        return;
+    }
+    (void)hipEventRecord(e, stream_);
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_pending.push_back(TimingRec{name_, (hipEvent_t)start_, e});
+}
+
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+        v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Paged attention planning (host side of the split policy and workspace layout)
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kSplitMinKeys = 128;      // manifest tunable SPLIT_MIN_KEYS
+constexpr int kMaxSplits = 16;          // manifest tunable MAX_SPLITS
+constexpr int kSplitTargetWg = 1024;    // manifest tunable SPLIT_TARGET_WORKGROUPS
+constexpr int kWavesPerCu = 8;          // resident decode waves per CU (2 per SIMD)
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct PagedPlan {
+    int Q, ncb_dec, ncb_pre, tpi_dec, tpi_pre;
+    int mode, splits, target_units;
+    int cap_dec, cap_pre, cap_comb, unit_cap;
+    size_t off_dec, off_pre, off_comb, off_o, off_m, off_l, total;
+};
+
+pa_status check_shape(const pa_paged_shape *s) {
+    if (!s) return PA_ERR_NULL;
+    if (s->batch < 1 || s->num_tokens < 0 || s->num_heads <= 0 || s->kv_num_heads <= 0 ||
+        s->num_heads % s->kv_num_heads != 0 || s->head_size <= 0 || s->num_blocks < 1 ||
+        s->block_size < 1 || s->max_blocks < 1 || (s->packed_qkv != 0 && s->packed_qkv != 1))
+        return PA_ERR_SHAPE;
+    if (s->head_size != 64 && s->head_size != 128) return PA_ERR_UNSUPPORTED;
+    if (s->num_heads / s->kv_num_heads > 64) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+int page_rule_splits(const pa_paged_shape *s) {
+    const long long ceiling = (long long)s->max_blocks * s->block_size;
+    const long long cap = std::max(1LL, std::min((long long)kMaxSplits, ceiling / kSplitMinKeys));
+    const long long base = std::max(1LL, (long long)s->num_tokens * s->kv_num_heads);
+    const long long want = (kSplitTargetWg + base - 1) / base;
+    return (int)std::max(1LL, std::min(cap, want));
+}
+
+bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
+    if (check_shape(s) != PA_OK || num_splits < PA_SPLITS_PAGE_RULE) return false;
+    const int T = s->num_tokens, B = s->batch, G = s->kv_num_heads, H = s->num_heads;
+    const int D = s->head_size;
+    p.Q = H / G;
+    p.ncb_dec = p.Q <= 16 ? 1 : (p.Q <= 32 ? 2 : 4);
+    p.tpi_dec = 16 * p.ncb_dec / p.Q;
+    p.ncb_pre = std::max(2, p.ncb_dec);
+    p.tpi_pre = 16 * p.ncb_pre / p.Q;
+    if (num_splits == PA_SPLITS_AUTO) {
+        p.mode = 0;
+        p.splits = 0;
+        p.target_units = device_cu_count() * kWavesPerCu * 2;
+        p.cap_dec = std::max(1, p.target_units / G) + B;
+        p.unit_cap = p.tpi_dec * p.cap_dec;
+    } else {
+        p.mode = 1;
+        p.splits = num_splits == PA_SPLITS_PAGE_RULE ? page_rule_splits(s) : num_splits;
+        p.target_units = 0;
+        const long long cd = (long long)p.splits * B;
+        if (cd > (1LL << 30)) return false;
+        p.cap_dec = (int)cd;
+        const long long uc = p.splits >= 2 ? (long long)p.splits * T : 0;
+        if (uc > (1LL << 30)) return false;
+        p.unit_cap = (int)uc;
+    }
+    p.cap_pre = T / p.tpi_pre + T / (p.tpi_dec + 1) + 1;
+    p.cap_comb = std::max(1, T);
+    size_t off = align_up(sizeof(PlanHeader));
+    p.off_dec = off;
+    off = align_up(off + sizeof(AttnItem) * (size_t)p.cap_dec);
+    p.off_pre = off;
+    off = align_up(off + sizeof(AttnItem) * (size_t)p.cap_pre);
+    p.off_comb = off;
+    off = align_up(off + sizeof(CombItem) * (size_t)p.cap_comb);
+    p.off_o = off;
+    off = align_up(off + sizeof(float) * (size_t)p.unit_cap * H * D);
+    p.off_m = off;
+    off = align_up(off + sizeof(float) * (size_t)p.unit_cap * H);
+    p.off_l = off;
+    off = align_up(off + sizeof(float) * (size_t)p.unit_cap * H);
+    p.total = off;
+    return true;
+}
+
+int log2_pow2_ge8(int bs) {
+    if (bs < 8 || (bs & (bs - 1))) return -1;
+    int l = 0;
+    while ((1 << l) < bs) ++l;
+    return l;
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char *pa_status_string(pa_status status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL: return "a required pointer is NULL";
+        case PA_ERR_SHAPE: return "sizes or attributes violate the op contract";
+        case PA_ERR_UNSUPPORTED: return "configuration not implemented by this build";
+        case PA_ERR_WORKSPACE: return "workspace too small";
+        case PA_ERR_HIP: return "HIP runtime error while enqueueing";
+        default: return "unknown status";
+    }
+}
+
+void pa_timing_enable(int32_t on) { g_timing.store(on ? 1 : 0); }
+
+void pa_timing_reset(void) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    for (auto &r : g_pending) {
+        (void)hipEventSynchronize(r.stop);
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    g_pending.clear();
+    g_done.clear();
+}
+
+pa_status pa_timing_get(const char *kernel, double *total_ms, int64_t *launches) {
+    if (!total_ms || !launches) return PA_ERR_NULL;
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    pa_status st = PA_OK;
+    for (auto &r : g_pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.stop) != hipSuccess ||
+            hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+            st = PA_ERR_HIP;
+        auto &d = g_done[r.name];
+        d.first += ms;
+        d.second += 1;
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    g_pending.clear();
+    double t = 0.0;
+    int64_t n = 0;
+    for (auto &kv : g_done) {
+        if (kernel && kv.first != kernel) continue;
+        t += kv.second.first;
+        n += kv.second.second;
+    }
+    *total_ms = t;
+    *launches = n;
+    return st;
+}
+
+pa_status pa_kv_append(const pa_paged_shape *shape, const void *query, const void *key,
+                       const void *value, void *key_cache, void *value_cache,
+                       const int32_t *cumulative_sequence_length, const int32_t *past_seqlens,
+                       const int32_t *block_table, const int32_t *slot_mapping,
+                       const void *cos_cache, const void *sin_cache, int32_t rotary_dim,
+                       int32_t rotary_mode, int32_t rotary_positions, void *stream) {
+    pa_status st = check_shape(shape);
+    if (st != PA_OK) return st;
+    const pa_paged_shape &s = *shape;
+    if (s.packed_qkv) {
+        if (key || value) return PA_ERR_SHAPE;
+        if (!query) return PA_ERR_NULL;
+    } else {
+        if ((key == nullptr) != (value == nullptr)) return PA_ERR_SHAPE;
+        if (!key) return PA_ERR_NULL;
+    }
+    if (!key_cache || !value_cache || !cumulative_sequence_length || !past_seqlens)
+        return PA_ERR_NULL;
+    if (!slot_mapping && !block_table) return PA_ERR_NULL;
+    if (rotary_mode != PA_ROTARY_NONE && rotary_mode != PA_ROTARY_NEOX &&
+        rotary_mode != PA_ROTARY_INTERLEAVED)
+        return PA_ERR_SHAPE;
+    if (rotary_mode != PA_ROTARY_NONE) {
+        if (rotary_dim <= 0 || rotary_dim % 2 != 0 || rotary_dim > s.head_size ||
+            rotary_positions < 1)
+            return PA_ERR_SHAPE;
+        if (!cos_cache || !sin_cache) return PA_ERR_NULL;
+    }
+    if (s.num_tokens == 0) return PA_OK;
+    AppendArgs a;
+    const int H = s.num_heads, G = s.kv_num_heads, D = s.head_size;
+    a.query = s.packed_qkv ? (const half_t *)query : nullptr;
+    a.key = (const half_t *)key;
+    a.value = (const half_t *)value;
+    a.kc = (half_t *)key_cache;
+    a.vc = (half_t *)value_cache;
+    a.cu = cumulative_sequence_length;
+    a.past = past_seqlens;
+    a.bt = block_table;
+    a.slot_mapping = slot_mapping;
+    a.cos = (const half_t *)cos_cache;
+    a.sin = (const half_t *)sin_cache;
+    a.src_stride = s.packed_qkv ? (int64_t)(H + 2 * G) * D : (int64_t)G * D;
+    a.k_off = s.packed_qkv ? (int64_t)H * D : 0;
+    a.v_off = s.packed_qkv ? (int64_t)(H + G) * D : 0;
+    a.T = s.num_tokens;
+    a.B = s.batch;
+    a.G = G;
+    a.D = D;
+    a.bs = s.block_size;
+    a.MB = s.max_blocks;
+    a.rotary_dim = rotary_mode == PA_ROTARY_NONE ? 0 : rotary_dim;
+    a.rotary_mode = rotary_mode;
+    return launch_kv_append(a, (hipStream_t)stream);
+}
+
+size_t pa_paged_attention_workspace_size(const pa_paged_shape *shape, int32_t num_splits) {
+    PagedPlan p;
+    if (!make_plan(shape, num_splits, p)) return 0;
+    return p.total;
+}
+
+pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
+                             const void *key_cache, const void *value_cache,
+                             const int32_t *cumulative_sequence_length,
+                             const int32_t *past_seqlens, const int32_t *block_table, float scale,
+                             int32_t causal, int32_t num_splits, void *workspace,
+                             size_t workspace_bytes, void *output, void *stream) {
+    pa_status st = check_shape(shape);
+    if (st != PA_OK) return st;
+    if (causal != 0 && causal != 1) return PA_ERR_SHAPE;
+    if (num_splits < PA_SPLITS_PAGE_RULE) return PA_ERR_SHAPE;
+    const pa_paged_shape &s = *shape;
+    if (!query || !key_cache || !value_cache || !cumulative_sequence_length || !past_seqlens ||
+        !block_table || !output)
+        return PA_ERR_NULL;
+    PagedPlan p;
+    if (!make_plan(shape, num_splits, p)) return PA_ERR_SHAPE;
+    if (s.num_tokens == 0) return PA_OK;
+    if (!workspace) return PA_ERR_NULL;
+    if (workspace_bytes < p.total || ((uintptr_t)workspace % kAlign) != 0)
+        return PA_ERR_WORKSPACE;
+    hipStream_t strm = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    const int H = s.num_heads, G = s.kv_num_heads, D = s.head_size;
+
+    PlanArgs pl;
+    pl.cu = cumulative_sequence_length;
+    pl.past = past_seqlens;
+    pl.B = s.batch;
+    pl.G = G;
+    pl.causal = causal;
+    pl.tpi_dec = p.tpi_dec;
+    pl.tpi_pre = p.tpi_pre;
+    pl.mode = p.mode;
+    pl.splits = p.splits;
+    pl.target_units = p.target_units;
+    pl.min_chunk = kSplitMinKeys;
+    pl.unit_cap = p.unit_cap;
+    pl.cap_dec = p.cap_dec;
+    pl.cap_pre = p.cap_pre;
+    pl.cap_comb = p.cap_comb;
+    pl.hdr = (PlanHeader *)ws;
+    pl.dec = (AttnItem *)(ws + p.off_dec);
+    pl.pre = (AttnItem *)(ws + p.off_pre);
+    pl.comb = (CombItem *)(ws + p.off_comb);
+    if ((st = launch_plan(pl, strm)) != PA_OK) return st;
+
+    const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)D);
+    AttnArgs a;
+    a.query = (const half_t *)query;
+    a.kc = (const half_t *)key_cache;
+    a.vc = (const half_t *)value_cache;
+    a.cu = cumulative_sequence_length;
+    a.past = past_seqlens;
+    a.bt = block_table;
+    a.out = (half_t *)output;
+    a.o_part = (float *)(ws + p.off_o);
+    a.m_part = (float *)(ws + p.off_m);
+    a.l_part = (float *)(ws + p.off_l);
+    a.q_stride = s.packed_qkv ? (int64_t)(H + 2 * G) * D : (int64_t)H * D;
+    a.H = H;
+    a.G = G;
+    a.Q = p.Q;
+    a.bs = s.block_size;
+    a.MB = s.max_blocks;
+    a.log2bs = log2_pow2_ge8(s.block_size);
+    a.causal = causal;
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    const int cus = device_cu_count();
+
+    a.items = pl.dec;
+    a.n_items = &pl.hdr->n_dec;
+    a.tpi = p.tpi_dec;
+    const long long gdec = std::min((long long)p.cap_dec * G, (long long)cus * kWavesPerCu);
+    if ((st = launch_attention(a, D, p.ncb_dec, (int)gdec, "attn_decode", strm)) != PA_OK)
+        return st;
+
+    a.items = pl.pre;
+    a.n_items = &pl.hdr->n_pre;
+    a.tpi = p.tpi_pre;
+    const long long gpre = std::min((long long)p.cap_pre * G, (long long)cus * 4);
+    if ((st = launch_attention(a, D, p.ncb_pre, (int)gpre, "attn_prefill", strm)) != PA_OK) return st;
+
+    if (p.unit_cap > 0) {
+        CombineArgs c;
+        c.o = a.o_part;
+        c.m = a.m_part;
+        c.l = a.l_part;
+        c.group_ptr = nullptr;
+        c.items = pl.comb;
+        c.n_items = &pl.hdr->n_comb;
+        c.num_groups = 0;
+        c.lanes = H;
+        c.splits = 0;
+        c.D = D;
+        c.out_f32 = 0;
+        c.out = output;
+        if ((st = launch_combine(c, p.cap_comb, strm)) != PA_OK) return st;
+    }
+    return PA_OK;
+}
+
+pa_status pa_split_combine(const float *o_partial, const float *m_partial,
+                           const float *l_partial, const int32_t *group_ptr, int32_t num_groups,
+                           int32_t lanes, int32_t num_splits, int32_t head_dim, int32_t out_dtype,
+                           void *out, void *stream) {
+    if (num_groups < 0 || lanes < 1 || head_dim <= 0 || head_dim % 4 != 0 ||
+        (out_dtype != PA_F16 && out_dtype != PA_F32))
+        return PA_ERR_SHAPE;
+    if (!group_ptr && num_splits < 1) return PA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (num_groups == 0) return PA_OK;
+    if (!o_partial || !m_partial || !l_partial || !out) return PA_ERR_NULL;
+    CombineArgs c;
+    c.o = o_partial;
+    c.m = m_partial;
+    c.l = l_partial;
+    c.group_ptr = group_ptr;
+    c.items = nullptr;
+    c.n_items = nullptr;
+    c.num_groups = num_groups;
+    c.lanes = lanes;
+    c.splits = num_splits;
+    c.D = head_dim;
+    c.out_f32 = out_dtype == PA_F32;
+    c.out = out;
+    return launch_combine(c, num_groups, (hipStream_t)stream);
+}
+
+static pa_status check_sparse(const pa_sparse_shape *s) {
+    if (!s) return PA_ERR_NULL;
+    if (s->num_edges < 0 || s->tq < 0 || s->hkv < 1 || s->qhead < 1 || s->head_dim <= 0 ||
+        s->block_size < 1 || s->page_size < 1 || s->block_size % s->page_size != 0 ||
+        s->num_pages < 0 || s->max_pages < 1 || s->batch < 1)
+        return PA_ERR_SHAPE;
+    if (s->head_dim != 64 && s->head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (s->block_size > 128 || s->qhead > 16) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+static int sparse_units(const pa_sparse_shape *s) {
+    const long long nblk = s->max_pages / (s->block_size / s->page_size) + 1;
+    return (int)std::min((long long)s->batch * s->hkv * nblk, 1LL << 30);
+}
+
+size_t pa_sparse_forward_workspace_size(const pa_sparse_shape *shape) {
+    if (check_sparse(shape) != PA_OK) return 0;
+    return sparse_workspace_bytes(shape->num_edges, sparse_units(shape));
+}
+
+pa_status pa_sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
+                            const float *k_pages, const float *v_pages,
+                            const int32_t *edge_meta, const int32_t *block_tables,
+                            float softmax_scale, int32_t causal, void *workspace,
+                            size_t workspace_bytes, float *o_partial, float *m_partial,
+                            float *l_partial, void *stream) {
+    pa_status st = check_sparse(shape);
+    if (st != PA_OK) return st;
+    if (causal != 0) return PA_ERR_UNSUPPORTED;
+    const pa_sparse_shape &s = *shape;
+    if (s.num_edges == 0) return PA_OK;
+    if (!q_buf || !k_pages || !v_pages || !edge_meta || !block_tables || !o_partial ||
+        !m_partial || !l_partial || !workspace)
+        return PA_ERR_NULL;
+    const int units = sparse_units(shape);
+    if (workspace_bytes < sparse_workspace_bytes(s.num_edges, units) ||
+        ((uintptr_t)workspace % 256) != 0)
+        return PA_ERR_WORKSPACE;
+    SparseArgs a;
+    a.q = q_buf;
+    a.kp = k_pages;
+    a.vp = v_pages;
+    a.edge_meta = edge_meta;
+    a.bt = block_tables;
+    a.o = o_partial;
+    a.m = m_partial;
+    a.l = l_partial;
+    a.ws = (int32_t *)workspace;
+    a.E = s.num_edges;
+    a.tq = s.tq;
+    a.hkv = s.hkv;
+    a.qhead = s.qhead;
+    a.D = s.head_dim;
+    a.block_size = s.block_size;
+    a.page_size = s.page_size;
+    a.ppb = s.block_size / s.page_size;
+    a.max_pages = s.max_pages;
+    a.batch = s.batch;
+    a.num_pages = s.num_pages;
+    a.units = units;
+    a.nblk = units / (s.batch * s.hkv);
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    return launch_sparse(a, (hipStream_t)stream);
+}
+
+}  // extern "C"

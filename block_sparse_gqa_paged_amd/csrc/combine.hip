@@ -1,0 +1,122 @@
+// Log-sum-exp merge of (o, m, l) partials for gfx950.
+//
+// Operation: the merge pass of the "com.microsoft.PagedAttention ... manifest.json" page
+// (PagedAttention.AttendSplitKMerge over the partialOut / partialStats intermediates), and the
+// merge of the per-edge partials of the "alice-llm ... sparse_attention_forward.wgsl" page.
+// Output row r = k*lanes + lane of group k:
+//   M = max m over units with l > 0, w = exp(m - M), out = sum w o / sum w l (0 if no l > 0).
+//
+// The pass streams the partial vectors once: HBM-bound. D/4 lanes own one output row (a float4
+// each), so a wave covers 64*4/D rows; the rows of one unit are adjacent in memory, so a wave's
+// loads for one unit are one contiguous span. Statistics (m, l) of a row are reduced first
+// (lanes stride over units), then the o vectors stream with the unit loop unrolled by 4 to keep
+// several loads in flight per lane.
+#include "common.h"
+
+namespace pa {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int mode) {
+    constexpr int LPR = D / 4;      // lanes per row
+    constexpr int RPW = 64 / LPR;   // rows per wave
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % LPR;     // float4 index inside the row
+    const int rw = lane / LPR;      // row inside the wave's row block
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int nwaves = (gridDim.x * blockDim.x) >> 6;
+    const int n_groups = (mode == 2) ? a.n_items[0] : a.num_groups;
+    const int blocks_per_group = (a.lanes + RPW - 1) / RPW;
+    const long long n_work = (long long)n_groups * blocks_per_group;
+
+    for (long long w = wave; w < n_work; w += nwaves) {
+        const int k = (int)(w / blocks_per_group);
+        const int lane_row = (int)(w - (long long)k * blocks_per_group) * RPW + rw;
+        long long e0, e1, row_group;
+        if (mode == 0) {          // uniform splits
+            e0 = (long long)k * a.splits; e1 = e0 + a.splits; row_group = k;
+        } else if (mode == 1) {   // CSR offsets
+            e0 = a.group_ptr[k]; e1 = a.group_ptr[k + 1]; row_group = k;
+        } else {                  // planner list
+            const CombItem it = a.items[k];
+            e0 = it.e0; e1 = e0 + it.count; row_group = it.row;
+        }
+        const bool active = lane_row < a.lanes;
+        const int lr = active ? lane_row : 0;
+
+        // Row statistics: lanes of the row stride over its units.
+        float M = -INFINITY;
+        for (long long e = e0 + sub; e < e1; e += LPR) {
+            const long long p = e * a.lanes + lr;
+            if (a.l[p] > 0.f) M = fmaxf(M, a.m[p]);
+        }
+        for (int o = 1; o < LPR; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        float Ls = 0.f;
+        for (long long e = e0 + sub; e < e1; e += LPR) {
+            const long long p = e * a.lanes + lr;
+            const float lv = a.l[p];
+            if (lv > 0.f) Ls += __builtin_amdgcn_exp2f((a.m[p] - M) * kLog2e) * lv;
+        }
+        for (int o = 1; o < LPR; o <<= 1) Ls += __shfl_xor(Ls, o, 64);
+
+        // Weighted sum of the o vectors.
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        long long e = e0;
+        for (; e + 4 <= e1; e += 4) {
+            float4_t v[4];
+            float wgt[4];
+            for (int u = 0; u < 4; ++u) {
+                const long long p = (e + u) * a.lanes + lr;
+                v[u] = *(const float4_t *)(a.o + p * D + 4 * sub);
+                const float lv = a.l[p];
+                wgt[u] = lv > 0.f ? __builtin_amdgcn_exp2f((a.m[p] - M) * kLog2e) : 0.f;
+            }
+            for (int u = 0; u < 4; ++u) acc += wgt[u] * v[u];
+        }
+        for (; e < e1; ++e) {
+            const long long p = e * a.lanes + lr;
+            const float4_t v = *(const float4_t *)(a.o + p * D + 4 * sub);
+            const float lv = a.l[p];
+            const float wgt = lv > 0.f ? __builtin_amdgcn_exp2f((a.m[p] - M) * kLog2e) : 0.f;
+            acc += wgt * v;
+        }
+        if (!active) continue;
+        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+        acc *= inv;
+        const long long r = row_group * a.lanes + lane_row;
+        if (a.out_f32) {
+            *(float4_t *)((float *)a.out + r * D + 4 * sub) = acc;
+        } else {
+            half4_t h;
+            for (int i = 0; i < 4; ++i) h[i] = (half_t)acc[i];
+            *(half4_t *)((half_t *)a.out + r * D + 4 * sub) = h;
+        }
+    }
+}
+
+}  // namespace
+
+// mode: group_ptr given -> CSR; items given -> planner list; else uniform splits.
+pa_status launch_combine(const CombineArgs &a, int max_groups, hipStream_t stream) {
+    LaunchScope scope("combine", stream);
+    const int mode = a.items ? 2 : (a.group_ptr ? 1 : 0);
+    if (max_groups <= 0) return PA_OK;
+    const int rpw = 64 / (a.D / 4);
+    const long long work = (long long)max_groups * ((a.lanes + rpw - 1) / rpw);
+    const long long cap = (long long)device_cu_count() * 32;  // waves: 8 per SIMD
+    const long long waves = work < cap ? work : cap;
+    const int grid = (int)((waves + 3) / 4);
+    switch (a.D) {
+        case 64:
+            hipLaunchKernelGGL(combine_kernel<64>, dim3(grid), dim3(256), 0, stream, a, mode);
+            break;
+        case 128:
+            hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, a, mode);
+            break;
+        default:
+            return PA_ERR_UNSUPPORTED;
+    }
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace pa

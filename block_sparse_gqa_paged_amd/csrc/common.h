@@ -1,0 +1,180 @@
+// Internal helpers shared by the HIP kernels and the host entry points of libpa.
+// gfx950 (CDNA4) only: wave64, MFMA f32_16x16x32_f16 / f32_16x16x4_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegLarge = -1.0e30f;  // the sentinel max of an empty partial
+
+// ---------------------------------------------------------------------------------------------
+// Host side: launch bookkeeping (timing hooks) and device properties.
+// ---------------------------------------------------------------------------------------------
+struct LaunchScope {
+    // Records a HIP event pair around the kernels enqueued while it lives, when timing is on.
+    LaunchScope(const char *name, hipStream_t stream);
+    ~LaunchScope();
+    const char *name_;
+    hipStream_t stream_;
+    void *start_;
+};
+
+int device_cu_count();  // compute units of the current device (cached per device)
+
+// ---------------------------------------------------------------------------------------------
+// Launchers (one per kernel family); each returns PA_OK or PA_ERR_HIP.
+// ---------------------------------------------------------------------------------------------
+struct AppendArgs {
+    const half_t *query;  // packed rows, or NULL
+    const half_t *key;
+    const half_t *value;
+    half_t *kc;
+    half_t *vc;
+    const int32_t *cu;
+    const int32_t *past;
+    const int32_t *bt;
+    const int32_t *slot_mapping;
+    const half_t *cos;
+    const half_t *sin;
+    int64_t src_stride;  // elements per source row (G*D or (H+2G)*D)
+    int64_t k_off;       // element offset of K inside a source row
+    int64_t v_off;       // element offset of V inside a source row
+    int T, B, G, D, bs, MB;
+    int rotary_dim, rotary_mode;
+};
+pa_status launch_kv_append(const AppendArgs &a, hipStream_t stream);
+
+// Work item of the attention kernels, written by the device planner.
+struct AttnItem {
+    int32_t b;     // sequence
+    int32_t t0;    // first new token of the item, within the sequence
+    int32_t k0;    // key range [k0, k1) this item covers
+    int32_t k1;
+    int32_t base;  // first partial unit of the sequence, or -1: write the output directly
+    int32_t nsplit;  // chunks the sequence's key range is cut into
+    int32_t split;   // this item's chunk
+    int32_t pad;
+};
+
+// Combine work entry for one output row group (a query row with >= 2 partial units).
+struct CombItem {
+    int32_t row;    // output row group
+    int32_t e0;     // first partial unit
+    int32_t count;  // units
+    int32_t pad;
+};
+
+// Header of the planner's output inside the workspace.
+struct PlanHeader {
+    int32_t n_dec;      // decode-like items
+    int32_t n_pre;      // prefill items
+    int32_t n_comb;     // combine entries
+    int32_t chunk;      // chunk keys chosen for split decode (0 when no split)
+    int32_t units;      // partial units used
+    int32_t pad[59];    // keeps the lists 256-byte aligned
+};
+
+struct PlanArgs {
+    const int32_t *cu;
+    const int32_t *past;
+    int B, G, causal;
+    int tpi_dec;        // max tokens of a decode-like item
+    int tpi_pre;        // tokens per prefill item
+    int mode;           // 0: auto chunk, 1: even split into `splits`
+    int splits;         // S for mode 1
+    int target_units;   // mode 0: wanted decode work units (items * G)
+    int min_chunk;      // mode 0: smallest chunk
+    int unit_cap;       // partial units that fit the workspace
+    int cap_dec, cap_pre, cap_comb;
+    PlanHeader *hdr;
+    AttnItem *dec;
+    AttnItem *pre;
+    CombItem *comb;
+};
+pa_status launch_plan(const PlanArgs &a, hipStream_t stream);
+
+struct AttnArgs {
+    const half_t *query;
+    const half_t *kc;
+    const half_t *vc;
+    const int32_t *cu;
+    const int32_t *past;
+    const int32_t *bt;
+    const AttnItem *items;
+    const int32_t *n_items;  // device count of items
+    half_t *out;
+    float *o_part;
+    float *m_part;
+    float *l_part;
+    int64_t q_stride;  // elements per query row
+    int H, G, Q, bs, MB, log2bs;  // log2bs < 0: block size is not a power of two >= 8
+    int causal;
+    int tpi;           // tokens per item
+    float scale_log2;  // scale * log2(e)
+};
+// ncb: 16-column blocks of (token, head) columns per item (1, 2 or 4).
+pa_status launch_attention(const AttnArgs &a, int D, int ncb, int grid, const char *name,
+                           hipStream_t stream);
+
+struct CombineArgs {
+    const float *o;
+    const float *m;
+    const float *l;
+    const int32_t *group_ptr;     // CSR mode
+    const CombItem *items;        // list mode
+    const int32_t *n_items;       // list mode: device count
+    int num_groups;               // CSR / uniform modes
+    int lanes, splits, D;
+    int out_f32;
+    void *out;
+};
+pa_status launch_combine(const CombineArgs &a, int max_groups, hipStream_t stream);
+
+struct SparseArgs {
+    const float *q;
+    const float *kp;
+    const float *vp;
+    const int32_t *edge_meta;
+    const int32_t *bt;
+    float *o;
+    float *m;
+    float *l;
+    int32_t *ws;  // workspace (int32 words)
+    int E, tq, hkv, qhead, D, block_size, page_size, ppb, max_pages, batch, num_pages;
+    int units;    // batch * hkv * nblk
+    int nblk;     // blocks per batch row (max_pages / ppb)
+    float scale_log2;
+};
+pa_status launch_sparse(const SparseArgs &a, hipStream_t stream);
+size_t sparse_workspace_bytes(int E, int units);
+
+// ---------------------------------------------------------------------------------------------
+// Device helpers.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+    return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+__device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float4_t mfma16x16x4f32(float a, float b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace pa

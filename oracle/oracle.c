@@ -84,6 +84,21 @@ uint16_t oracle_f64_to_f16(double x)
 
 uint16_t oracle_f32_to_f16(float x) { return oracle_f64_to_f16((double)x); }
 
+/* The same decode, tabulated once: every fp16 bit pattern -> its float64 value. The oracle is
+ * single-threaded, so the lazy fill needs no lock. */
+static double f16_table[65536];
+static int f16_table_ready = 0;
+
+static double f16v(uint16_t h)
+{
+    if (!f16_table_ready) {
+        for (int i = 0; i < 65536; ++i)
+            f16_table[i] = oracle_f16_to_f64((uint16_t)i);
+        f16_table_ready = 1;
+    }
+    return f16_table[h];
+}
+
 /* ---------------------------------------------------------------------------------------- */
 /* [append] past-length rule for a padded batch.                                             */
 /* ---------------------------------------------------------------------------------------- */
@@ -219,7 +234,7 @@ static void gather_rows(const uint16_t *cache, const int32_t *block_table, int M
         const long long blk = block_table[(long long)b * MB + j / bs];
         const uint16_t *src = cache + ((blk * bs + j % bs) * G + g) * (long long)D;
         for (int d = 0; d < D; ++d)
-            dst[(long long)j * D + d] = oracle_f16_to_f64(src[d]);
+            dst[(long long)j * D + d] = f16v(src[d]);
     }
 }
 
@@ -295,7 +310,7 @@ void oracle_paged_attention(int T, int B, int H, int G, int D, int bs, int MB,
                 gather_rows(key_cache, block_table, MB, bs, G, D, b, g, limit, K);
                 gather_rows(value_cache, block_table, MB, bs, G, D, b, g, limit, V);
                 for (int d = 0; d < D; ++d)
-                    q[d] = oracle_f16_to_f64(query[i * q_row_stride + (long long)h * D + d]);
+                    q[d] = f16v(query[i * q_row_stride + (long long)h * D + d]);
                 double m, l;
                 attend(q, K, V, limit, D, scale, o, &m, &l, s);
                 for (int d = 0; d < D; ++d)
@@ -354,7 +369,7 @@ void oracle_paged_attention_partials(int T, int B, int H, int G, int D, int bs, 
                 gather_rows(key_cache, block_table, MB, bs, G, D, b, g, limit, K);
                 gather_rows(value_cache, block_table, MB, bs, G, D, b, g, limit, V);
                 for (int d = 0; d < D; ++d)
-                    q[d] = oracle_f16_to_f64(query[i * q_row_stride + (long long)h * D + d]);
+                    q[d] = f16v(query[i * q_row_stride + (long long)h * D + d]);
                 for (int sp = 0; sp < num_splits; ++sp) {
                     const long long p = (i * num_splits + sp) * H + h;
                     long long lo = sp * C, hi = (sp + 1) * C;

@@ -1,0 +1,178 @@
+"""Host-only checks of the C ABI: the library loads, exports every function include/pa.h
+declares, and rejects contract violations (the PagedAttention manifest's cacheShapeOk,
+headLayoutOk, scheduleShapeOk, separateKv/packedKv and is_causal rules; the sparse page's
+Params) before it enqueues anything. No call here reaches a GPU: every argument set fails
+validation, or is empty, or only sizes a workspace."""
+import os
+import re
+
+import pytest
+
+import block_sparse_gqa_paged_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20   # a non-NULL address that validation never dereferences
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = pa.lib()
+    declared = _declared()
+    assert set(declared) == set(pa.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def _shape(**kw):
+    a = dict(batch=2, num_tokens=2, num_heads=4, kv_num_heads=2, head_size=64, num_blocks=16,
+             block_size=16, max_blocks=8, packed_qkv=False)
+    a.update(kw)
+    return pa.paged_shape(**a)
+
+
+def _append(shape, **kw):
+    a = dict(query=None, key=FAKE, value=FAKE, key_cache=FAKE, value_cache=FAKE,
+             cumulative_sequence_length=FAKE, past_seqlens=FAKE, block_table=FAKE,
+             slot_mapping=None, cos_cache=None, sin_cache=None, rotary_dim=0,
+             rotary_mode=pa.PA_ROTARY_NONE, rotary_positions=0, stream=0, check=False)
+    a.update(kw)
+    return pa.pa_kv_append(shape, **a)
+
+
+@pytest.mark.parametrize("bad,expect", [
+    (dict(batch=0), pa.PA_ERR_SHAPE),
+    (dict(num_heads=6, kv_num_heads=4), pa.PA_ERR_SHAPE),      # H % G != 0
+    (dict(kv_num_heads=0), pa.PA_ERR_SHAPE),
+    (dict(block_size=0), pa.PA_ERR_SHAPE),
+    (dict(max_blocks=0), pa.PA_ERR_SHAPE),
+    (dict(num_blocks=0), pa.PA_ERR_SHAPE),
+    (dict(num_tokens=-1), pa.PA_ERR_SHAPE),
+    (dict(head_size=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_heads=128, kv_num_heads=1), pa.PA_ERR_UNSUPPORTED),  # qPerKv > 64
+])
+def test_append_rejects_bad_shapes(bad, expect):
+    assert _append(_shape(**bad)) == expect
+
+
+def test_append_kv_presence_rules():
+    # separate layout needs both key and value; packed needs neither
+    assert _append(_shape(), value=None) == pa.PA_ERR_SHAPE
+    assert _append(_shape(), key=None, value=None) == pa.PA_ERR_NULL
+    assert _append(_shape(packed_qkv=True), query=FAKE) == pa.PA_ERR_SHAPE
+    assert _append(_shape(packed_qkv=True), query=None, key=None, value=None) == pa.PA_ERR_NULL
+    assert _append(_shape(), key_cache=None) == pa.PA_ERR_NULL
+    assert _append(_shape(), block_table=None) == pa.PA_ERR_NULL  # no slots without either
+
+
+def test_append_rotary_rules():
+    rot = dict(cos_cache=FAKE, sin_cache=FAKE, rotary_mode=pa.PA_ROTARY_NEOX,
+               rotary_positions=4)
+    assert _append(_shape(), rotary_dim=63, **rot) == pa.PA_ERR_SHAPE
+    assert _append(_shape(), rotary_dim=128, **rot) == pa.PA_ERR_SHAPE
+    assert _append(_shape(), rotary_dim=0, **rot) == pa.PA_ERR_SHAPE
+    assert _append(_shape(), rotary_dim=64, rotary_mode=3, rotary_positions=4) == pa.PA_ERR_SHAPE
+    rot["cos_cache"] = None
+    assert _append(_shape(), rotary_dim=64, **rot) == pa.PA_ERR_NULL
+
+
+def test_empty_append_is_a_no_op():
+    assert _append(_shape(num_tokens=0)) == pa.PA_OK
+
+
+def _attn(shape, **kw):
+    a = dict(query=FAKE, key_cache=FAKE, value_cache=FAKE, cumulative_sequence_length=FAKE,
+             past_seqlens=FAKE, block_table=FAKE, scale=0.0, causal=1,
+             num_splits=pa.PA_SPLITS_AUTO, workspace=FAKE, workspace_bytes=0, output=FAKE,
+             stream=0, check=False)
+    a.update(kw)
+    return pa.pa_paged_attention(shape, **a)
+
+
+def test_attention_rejects_bad_arguments():
+    assert _attn(_shape(), causal=2) == pa.PA_ERR_SHAPE          # is_causal values [1] (+0)
+    assert _attn(_shape(), num_splits=-2) == pa.PA_ERR_SHAPE
+    assert _attn(_shape(), block_table=None) == pa.PA_ERR_NULL
+    assert _attn(_shape(), output=None) == pa.PA_ERR_NULL
+    assert _attn(_shape(head_size=256)) == pa.PA_ERR_UNSUPPORTED
+    assert _attn(_shape(), workspace_bytes=16) == pa.PA_ERR_WORKSPACE
+    n = pa.pa_paged_attention_workspace_size(_shape())
+    assert _attn(_shape(), workspace=FAKE + 4, workspace_bytes=n) == pa.PA_ERR_WORKSPACE
+    assert _attn(_shape(num_tokens=0), workspace=None) == pa.PA_OK
+
+
+def test_workspace_size_is_zero_for_invalid_shapes():
+    assert pa.pa_paged_attention_workspace_size(_shape(batch=0)) == 0
+    assert pa.pa_paged_attention_workspace_size(_shape(), -3) == 0
+    assert pa.pa_paged_attention_workspace_size(_shape()) > 0
+
+
+@pytest.mark.parametrize("shape,expect_s", [
+    # the manifest's numSplits: min(cap, ceil(1024 / (T*G))), cap = min(16, MB*bs/128)
+    (dict(batch=2, num_tokens=2, num_heads=4, kv_num_heads=2, head_size=64, block_size=16,
+          max_blocks=8), 1),                                        # tiny decode: cap 1
+    (dict(batch=4, num_tokens=4, num_heads=8, kv_num_heads=8, head_size=128, block_size=32,
+          max_blocks=128), 16),                                     # rotary decode
+    (dict(batch=64, num_tokens=64, num_heads=32, kv_num_heads=8, head_size=128, block_size=16,
+          max_blocks=513), 2),                                      # GQA serving decode
+    (dict(batch=64, num_tokens=4152, num_heads=32, kv_num_heads=8, head_size=128,
+          block_size=32, max_blocks=513), 1),                       # mixed prefill + decode
+])
+def test_page_rule_split_count(shape, expect_s):
+    s = _shape(**shape)
+    assert (pa.pa_paged_attention_workspace_size(s, pa.PA_SPLITS_PAGE_RULE) ==
+            pa.pa_paged_attention_workspace_size(s, expect_s))
+    if expect_s > 1:
+        assert (pa.pa_paged_attention_workspace_size(s, expect_s) >
+                pa.pa_paged_attention_workspace_size(s, 1))
+
+
+def test_combine_rejects_bad_arguments():
+    def comb(**kw):
+        a = dict(o_partial=FAKE, m_partial=FAKE, l_partial=FAKE, group_ptr=None, num_groups=4,
+                 lanes=4, num_splits=2, head_dim=128, out_dtype=pa.PA_F32, out=FAKE, stream=0,
+                 check=False)
+        a.update(kw)
+        return pa.pa_split_combine(**a)
+    assert comb(lanes=0) == pa.PA_ERR_SHAPE
+    assert comb(num_groups=-1) == pa.PA_ERR_SHAPE
+    assert comb(num_splits=0) == pa.PA_ERR_SHAPE
+    assert comb(out_dtype=7) == pa.PA_ERR_SHAPE
+    assert comb(head_dim=30) == pa.PA_ERR_SHAPE
+    assert comb(head_dim=96) == pa.PA_ERR_UNSUPPORTED
+    assert comb(out=None) == pa.PA_ERR_NULL
+    assert comb(num_groups=0, out=None) == pa.PA_OK
+
+
+def test_sparse_rejects_bad_arguments():
+    def sh(**kw):
+        a = dict(num_edges=10, tq=8, hkv=2, qhead=4, head_dim=128, block_size=64, page_size=16,
+                 num_pages=64, max_pages=32, batch=2)
+        a.update(kw)
+        return pa.sparse_shape(**a)
+
+    def fwd(shape, **kw):
+        a = dict(q_buf=FAKE, k_pages=FAKE, v_pages=FAKE, edge_meta=FAKE, block_tables=FAKE,
+                 softmax_scale=0.1, causal=0, workspace=FAKE, workspace_bytes=0, o_partial=FAKE,
+                 m_partial=FAKE, l_partial=FAKE, stream=0, check=False)
+        a.update(kw)
+        return pa.pa_sparse_forward(shape, **a)
+    assert fwd(sh(), causal=1) == pa.PA_ERR_UNSUPPORTED     # right-aligned causal unimplemented
+    assert fwd(sh(block_size=60)) == pa.PA_ERR_SHAPE          # not a multiple of page_size
+    assert fwd(sh(block_size=256)) == pa.PA_ERR_UNSUPPORTED
+    assert fwd(sh(qhead=32)) == pa.PA_ERR_UNSUPPORTED
+    assert fwd(sh(head_dim=80)) == pa.PA_ERR_UNSUPPORTED
+    assert fwd(sh(), edge_meta=None) == pa.PA_ERR_NULL
+    assert fwd(sh(), workspace_bytes=8) == pa.PA_ERR_WORKSPACE
+    assert fwd(sh(num_edges=0), q_buf=None) == pa.PA_OK
+    assert pa.pa_sparse_forward_workspace_size(sh()) > 0
+    assert pa.pa_sparse_forward_workspace_size(sh(hkv=0)) == 0
+
+
+def test_status_strings():
+    for s in range(6):
+        assert pa.status_string(s)
+    assert "unknown" in pa.status_string(99)

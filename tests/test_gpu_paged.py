@@ -1,0 +1,203 @@
+"""GPU parity of the paged path (pa_kv_append, pa_paged_attention, pa_split_combine) against
+the CPU oracle, on seeded workloads: a tiny family that spans several 32-key tiles with ragged
+tails, the four paged workload shapes at full size (mixed prefill checked on sampled rows), NaN
+in stale cache rows, page permutation, and every split policy.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import block_sparse_gqa_paged_amd as pa  # noqa: E402
+import oracle  # noqa: E402
+from block_sparse_gqa_paged_amd import device as dev  # noqa: E402
+from block_sparse_gqa_paged_amd import workloads as W  # noqa: E402
+from parity import (assert_attention_close, assert_bits_equal, rows_as_decode,  # noqa: E402
+                    ROT_ABS)
+
+pytestmark = pytest.mark.gpu
+
+SPLITS = [pa.PA_SPLITS_AUTO, pa.PA_SPLITS_PAGE_RULE, 1, 2, 3, 16]
+
+
+def _run(w, num_splits=pa.PA_SPLITS_AUTO, use_slot_mapping=True):
+    c = dev.PagedCase(w)
+    c.append(use_slot_mapping=use_slot_mapping)
+    out = c.attention(num_splits)
+    torch.cuda.synchronize()
+    return c, out
+
+
+def _oracle(w):
+    kc, vc = oracle.kv_append(w)
+    return kc, vc, oracle.paged_attention(w, kc, vc)
+
+
+TINY = [
+    dict(seed=100, past=[37, 100], n_new=[1, 1], num_heads=4, kv_num_heads=2, head_size=64,
+         block_size=16),
+    dict(seed=101, past=[0, 5, 290, 64], n_new=[9, 1, 1, 40], num_heads=8, kv_num_heads=2,
+         head_size=128, block_size=16),
+    dict(seed=102, past=[31, 33], n_new=[2, 3], num_heads=4, kv_num_heads=4, head_size=128,
+         block_size=32),                                              # Q = 1, 2-3 token decode
+    dict(seed=103, past=[17, 3], n_new=[5, 70], num_heads=6, kv_num_heads=2, head_size=64,
+         block_size=5),                                               # bs not a power of two
+    dict(seed=104, past=[200, 0, 7], n_new=[1, 0, 2], num_heads=16, kv_num_heads=1,
+         head_size=64, block_size=8),                                 # MQA, empty sequence
+    dict(seed=105, past=[100, 12], n_new=[3, 19], num_heads=8, kv_num_heads=8, head_size=128,
+         block_size=64, packed=True, rotary_mode=W.ROTARY_NEOX, rotary_dim=128,
+         rotary_positions=256),
+    dict(seed=106, past=[45], n_new=[2], num_heads=32, kv_num_heads=1, head_size=64,
+         block_size=16, rotary_mode=W.ROTARY_INTERLEAVED, rotary_dim=32, rotary_positions=64),
+    dict(seed=107, past=[130, 257], n_new=[1, 1], num_heads=64, kv_num_heads=2, head_size=128,
+         block_size=16),                                              # qPerKv 32: two blocks
+]
+
+
+@pytest.mark.parametrize("case", TINY, ids=lambda c: str(c["seed"]))
+@pytest.mark.parametrize("num_splits", SPLITS, ids=lambda s: f"S{s}")
+def test_tiny_family(case, num_splits):
+    case = dict(case)
+    w = W.paged_workload(case.pop("seed"), table="pool", slack=0.3, name="tiny", **case)
+    kc, vc, ref = _oracle(w)
+    c, out = _run(w, num_splits)
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_bits_equal(c.value_cache, vc, "value_cache")
+    assert_attention_close(out, ref, f"attention S={num_splits}")
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_non_causal_and_prefill(causal):
+    w = W.paged_workload(110, past=[3, 60, 0], n_new=[33, 1, 17], num_heads=8, kv_num_heads=2,
+                         head_size=128, block_size=16, table="pool", causal=causal,
+                         name="causal")
+    kc, vc, ref = _oracle(w)
+    _, out = _run(w)
+    assert_attention_close(out, ref, f"causal={causal}")
+
+
+def test_tiny_decode_workload():
+    w = W.tiny_decode()
+    kc, vc, ref = _oracle(w)
+    c, out = _run(w, pa.PA_SPLITS_PAGE_RULE)
+    assert_bits_equal(c.key_cache, kc)
+    assert_bits_equal(c.value_cache, vc)
+    assert_attention_close(out, ref)
+
+
+@pytest.mark.parametrize("mode", [W.ROTARY_NEOX, W.ROTARY_INTERLEAVED])
+@pytest.mark.parametrize("use_slot_mapping", [True, False])
+def test_rotary_append_decode(mode, use_slot_mapping):
+    w = W.rotary_append_decode(rotary_mode=mode)
+    kc, vc, ref = _oracle(w)
+    c, out = _run(w, pa.PA_SPLITS_PAGE_RULE, use_slot_mapping=use_slot_mapping)
+    g = c.key_cache.cpu().numpy()
+    assert np.abs(g.astype(np.float32) - kc.astype(np.float32)).max() <= ROT_ABS
+    assert_bits_equal(g, kc, "rotated key_cache")       # matched float32 arithmetic
+    assert_bits_equal(c.value_cache, vc, "value_cache")
+    assert_attention_close(out, ref)
+
+
+def test_nan_in_stale_rows_never_reaches_output():
+    w = W.paged_workload(111, past=[70, 5, 129], n_new=[1, 12, 1], num_heads=8, kv_num_heads=2,
+                         head_size=128, block_size=16, table="pool", slack=0.5, poison=True,
+                         name="poison")
+    kc, vc, ref = _oracle(w)
+    for s in (pa.PA_SPLITS_AUTO, 4):
+        _, out = _run(w, s)
+        assert_attention_close(out, ref, f"poisoned S={s}")
+
+
+def test_page_permutation_is_bit_identical():
+    w = W.paged_workload(112, past=[300, 41], n_new=[1, 20], num_heads=8, kv_num_heads=2,
+                         head_size=128, block_size=16, table="pool", name="perm")
+    _, a = _run(w)
+    a = a.cpu().numpy()
+    perm = np.random.default_rng(3).permutation(w["NB"])
+    inv = np.argsort(perm)
+    w2 = dict(w)
+    w2["key_cache"], w2["value_cache"] = w["key_cache"][perm], w["value_cache"][perm]
+    bt = w["block_table"].copy()
+    bt[bt >= 0] = inv[bt[bt >= 0]]
+    w2["block_table"] = bt
+    _, b = _run(w2)
+    assert_bits_equal(b, a, "permuted pages")
+
+
+@pytest.fixture(scope="module")
+def gqa():
+    w = W.gqa_decode()
+    kc, vc, ref = _oracle(w)
+    return w, kc, vc, ref
+
+
+@pytest.mark.parametrize("num_splits", SPLITS + [7], ids=lambda s: f"S{s}")
+def test_gqa_serving_decode_full_size(gqa, num_splits):
+    w, kc, vc, ref = gqa
+    c, out = _run(w, num_splits)
+    if num_splits == pa.PA_SPLITS_AUTO:
+        assert_bits_equal(c.key_cache, kc, "key_cache")
+        assert_bits_equal(c.value_cache, vc, "value_cache")
+    assert_attention_close(out, ref, f"S={num_splits}")
+
+
+@pytest.fixture(scope="module")
+def mixed():
+    return W.mixed_prefill_decode()
+
+
+def test_mixed_prefill_decode_full_size(mixed):
+    w = mixed
+    c = dev.PagedCase(w)
+    c.append()
+    out = c.attention(pa.PA_SPLITS_AUTO).cpu().numpy()
+    torch.cuda.synchronize()
+    # the append over the whole cache, bit for bit
+    kc, vc = oracle.kv_append(w)
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_bits_equal(c.value_cache, vc, "value_cache")
+    # attention on sampled rows: every decode row, and rows of each prefill sequence
+    rng = np.random.default_rng(0)
+    pre = np.concatenate([w["cu"][b] + np.unique(np.r_[0, 1, 511, rng.integers(0, 512, 5)])
+                          for b in range(8)])
+    rows = np.concatenate([pre, np.arange(w["cu"][8], w["T"])])
+    sub = rows_as_decode(w, rows)
+    ref = oracle.paged_attention(sub, kc, vc)
+    assert_attention_close(out[rows], ref, "mixed sampled rows")
+
+
+# ------------------------------------------------------------------ combine of oracle partials
+@pytest.mark.parametrize("S", [2, 5])
+@pytest.mark.parametrize("out_dtype", [pa.PA_F16, pa.PA_F32])
+def test_combine_uniform_splits(S, out_dtype):
+    w = W.paged_workload(120, past=[333, 70, 1000], n_new=[1, 1, 1], num_heads=8,
+                         kv_num_heads=2, head_size=128, block_size=16, name="comb")
+    o, m, l = oracle.paged_attention_partials(w, S)
+    ref = oracle.split_combine(o, m, l, lanes=w["H"], head_dim=128, num_splits=S,
+                               out_dtype=np.float16 if out_dtype == pa.PA_F16 else np.float32)
+    got = dev.combine(o, m, l, lanes=w["H"], head_dim=128, num_splits=S, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    if out_dtype == pa.PA_F16:
+        assert_attention_close(got, ref)
+    else:
+        g = got.cpu().numpy()
+        assert np.allclose(g, ref, rtol=1e-5, atol=1e-6)
+
+
+def test_combine_csr_with_empty_and_sentinel_groups():
+    w = W.paged_workload(121, past=[90, 20], n_new=[1, 1], num_heads=4, kv_num_heads=4,
+                         head_size=64, block_size=16, name="comb")
+    o, m, l = oracle.paged_attention_partials(w, 4, chunk_keys=32)   # 91 keys: 3 + 1 empty
+    # groups: token 0's 4 units, an empty group, token 1's 4 units in reverse order
+    order = np.r_[0, 1, 2, 3, 7, 6, 5, 4]
+    H, D = w["H"], w["D"]
+    o2 = o.reshape(8, H, D)[order].reshape(-1, D)
+    m2 = m.reshape(8, H)[order].reshape(-1)
+    l2 = l.reshape(8, H)[order].reshape(-1)
+    gp = np.array([0, 4, 4, 8], dtype=np.int32)
+    ref = oracle.split_combine(o2, m2, l2, lanes=H, head_dim=D, group_ptr=gp,
+                               out_dtype=np.float32)
+    got = dev.combine(o2, m2, l2, lanes=H, head_dim=D, group_ptr=gp, out_dtype=pa.PA_F32)
+    g = got.cpu().numpy()
+    assert np.all(g[H:2 * H] == 0)
+    assert np.allclose(g, ref, rtol=1e-5, atol=1e-6)
