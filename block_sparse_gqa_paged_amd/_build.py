@@ -4,6 +4,7 @@ Each .hip source compiles to an object in parallel, then one shared-library link
   --offload-arch=gfx950  CDNA4 code objects only
   -O3 -fPIC -std=c++17
   -Xclang -target-feature -Xclang -packed-fp32-ops   no packed fp32 instructions in device code
+  -mllvm -amdgpu-mfma-vgpr-form                      MFMA operands and results in VGPRs
 The host pass warns that it does not know that feature; the warning is harmless.
 """
 import concurrent.futures as cf
@@ -18,7 +19,9 @@ LIB = os.path.join(HERE, "libpa.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around the softmax rescale
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src, verbose):

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <map>
+#include <numeric>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -77,9 +78,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct PagedPlan {
     int Q, ncb_dec, ncb_pre, tpi_dec, tpi_pre;
-    int mode, splits, target_units;
+    int mode, splits, gw, slots;
     int cap_dec, cap_pre, cap_comb, unit_cap;
-    size_t off_dec, off_pre, off_comb, off_o, off_m, off_l, total;
+    size_t off_dec, off_pre, off_comb, off_slot, off_o, off_m, off_l, total;
 };
 
 pa_status check_shape(const pa_paged_shape *s) {
@@ -90,6 +91,7 @@ pa_status check_shape(const pa_paged_shape *s) {
         return PA_ERR_SHAPE;
     if (s->head_size != 64 && s->head_size != 128) return PA_ERR_UNSUPPORTED;
     if (s->num_heads / s->kv_num_heads > 64) return PA_ERR_UNSUPPORTED;
+    if ((long long)s->kv_num_heads * s->head_size >= (1LL << 24)) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
 
@@ -106,20 +108,23 @@ bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
     const int T = s->num_tokens, B = s->batch, G = s->kv_num_heads, H = s->num_heads;
     const int D = s->head_size;
     p.Q = H / G;
+    p.gw = 0;  // set below from the decode kernel's column blocks
     p.ncb_dec = p.Q <= 16 ? 1 : (p.Q <= 32 ? 2 : 4);
     p.tpi_dec = 16 * p.ncb_dec / p.Q;
     p.ncb_pre = std::max(2, p.ncb_dec);
+    p.gw = p.ncb_dec == 1 ? std::gcd(G, 8) : 1;
     p.tpi_pre = 16 * p.ncb_pre / p.Q;
     if (num_splits == PA_SPLITS_AUTO) {
         p.mode = 0;
         p.splits = 0;
-        p.target_units = device_cu_count() * kWavesPerCu * 2;
-        p.cap_dec = std::max(1, p.target_units / G) + B;
+        // one share per resident decode workgroup: gw waves each, kWavesPerCu waves per CU
+        p.slots = std::max(1, device_cu_count() * kWavesPerCu / p.gw);
+        p.cap_dec = p.slots + B;   // each share boundary adds at most one piece
         p.unit_cap = p.tpi_dec * p.cap_dec;
     } else {
         p.mode = 1;
         p.splits = num_splits == PA_SPLITS_PAGE_RULE ? page_rule_splits(s) : num_splits;
-        p.target_units = 0;
+        p.slots = 0;
         const long long cd = (long long)p.splits * B;
         if (cd > (1LL << 30)) return false;
         p.cap_dec = (int)cd;
@@ -136,6 +141,8 @@ bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
     off = align_up(off + sizeof(AttnItem) * (size_t)p.cap_pre);
     p.off_comb = off;
     off = align_up(off + sizeof(CombItem) * (size_t)p.cap_comb);
+    p.off_slot = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)(p.slots + 1));
     p.off_o = off;
     off = align_up(off + sizeof(float) * (size_t)p.unit_cap * H * D);
     p.off_m = off;
@@ -309,7 +316,8 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     pl.tpi_pre = p.tpi_pre;
     pl.mode = p.mode;
     pl.splits = p.splits;
-    pl.target_units = p.target_units;
+    pl.slots = p.slots;
+    pl.slot_ptr = (int32_t *)(ws + p.off_slot);
     pl.min_chunk = kSplitMinKeys;
     pl.unit_cap = p.unit_cap;
     pl.cap_dec = p.cap_dec;
@@ -334,6 +342,8 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     a.m_part = (float *)(ws + p.off_m);
     a.l_part = (float *)(ws + p.off_l);
     a.q_stride = s.packed_qkv ? (int64_t)(H + 2 * G) * D : (int64_t)H * D;
+    a.block_elems = (int64_t)s.block_size * G * D;
+    a.key_elems = (uint32_t)(G * D);
     a.H = H;
     a.G = G;
     a.Q = p.Q;
@@ -341,21 +351,36 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     a.MB = s.max_blocks;
     a.log2bs = log2_pow2_ge8(s.block_size);
     a.causal = causal;
+    a.gw = p.gw;
     a.scale_log2 = (float)(sc * 1.4426950408889634);
     const int cus = device_cu_count();
 
     a.items = pl.dec;
     a.n_items = &pl.hdr->n_dec;
+    a.counter = &pl.hdr->next_dec;
     a.tpi = p.tpi_dec;
-    const long long gdec = std::min((long long)p.cap_dec * G, (long long)cus * kWavesPerCu);
-    if ((st = launch_attention(a, D, p.ncb_dec, (int)gdec, "attn_decode", strm)) != PA_OK)
+    int blocks;
+    if (p.mode == 0) {
+        a.slot_ptr = pl.slot_ptr;
+        blocks = p.slots;
+    } else {
+        a.slot_ptr = nullptr;
+        const long long units = (long long)p.cap_dec * (G / p.gw);
+        blocks = (int)std::min(units, (long long)cus * kWavesPerCu / p.gw);
+    }
+    if ((st = launch_attention(a, D, p.ncb_dec, blocks, true, "attn_decode", strm)) != PA_OK)
         return st;
 
     a.items = pl.pre;
     a.n_items = &pl.hdr->n_pre;
+    a.counter = &pl.hdr->next_pre;
+    a.slot_ptr = nullptr;
     a.tpi = p.tpi_pre;
-    const long long gpre = std::min((long long)p.cap_pre * G, (long long)cus * 4);
-    if ((st = launch_attention(a, D, p.ncb_pre, (int)gpre, "attn_prefill", strm)) != PA_OK) return st;
+    a.gw = 1;
+    const long long pre_units = (long long)p.cap_pre * G;
+    const int pblocks = (int)std::min(pre_units, (long long)cus * 4);
+    if ((st = launch_attention(a, D, p.ncb_pre, pblocks, false, "attn_prefill", strm)) != PA_OK)
+        return st;
 
     if (p.unit_cap > 0) {
         CombineArgs c;

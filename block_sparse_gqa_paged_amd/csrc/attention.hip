@@ -31,7 +31,7 @@ namespace pa {
 // ============================================================================================
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kTileKeys = 32;
 
 __device__ __forceinline__ long long block_sum_ll(long long v, long long *sh) {
@@ -56,28 +56,30 @@ __device__ __forceinline__ int block_max_i(int v, long long *sh) {
     return t;
 }
 
-// Exclusive scan of four counters across the workgroup; returns totals in tot[].
-__device__ __forceinline__ void block_scan4(int v[4], int excl[4], int tot[4], int *sh) {
+// Exclusive scan of NV counters across the workgroup; returns totals in tot[].
+template <int NV>
+__device__ __forceinline__ void block_scan(const int (&v)[NV], int (&excl)[NV], int (&tot)[NV],
+                                           int *sh) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int inc[4];
-    for (int k = 0; k < 4; ++k) {
+    int inc[NV];
+    for (int k = 0; k < NV; ++k) {
         int x = v[k];
         for (int o = 1; o < 64; o <<= 1) {
-            int y = __shfl_up(x, o, 64);
+            const int y = __shfl_up(x, o, 64);
             if (lane >= o) x += y;
         }
         inc[k] = x;
     }
     __syncthreads();
     if (lane == 63)
-        for (int k = 0; k < 4; ++k) sh[wid * 4 + k] = inc[k];
+        for (int k = 0; k < NV; ++k) sh[wid * NV + k] = inc[k];
     __syncthreads();
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NV; ++k) {
         int before = 0, all = 0;
         for (int i = 0; i < kPlanThreads / 64; ++i) {
-            const int s = sh[i * 4 + k];
-            if (i < wid) before += s;
-            all += s;
+            const int x = sh[i * NV + k];
+            if (i < wid) before += x;
+            all += x;
         }
         excl[k] = before + inc[k] - v[k];
         tot[k] = all;
@@ -85,66 +87,84 @@ __device__ __forceinline__ void block_scan4(int v[4], int excl[4], int tot[4], i
 }
 
 __device__ __forceinline__ int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b); }
-
-__device__ __forceinline__ int chunk_of(int mode, int C, int S, int L) {
-    if (mode == 0) return C;
-    const int per = ceil_div_i(L, S);
-    return ((per + kTileKeys - 1) / kTileKeys) * kTileKeys;
+__device__ __forceinline__ int round_tile(long long x) {
+    return (int)((x + kTileKeys - 1) / kTileKeys * kTileKeys);
 }
 
 }  // namespace
 
+// One workgroup turns the sequence lengths into work lists.
+//  * Decode-like sequences (1 <= n_b <= tpi_dec) are cut into pieces of their key range [0, L_b).
+//    Auto mode balances them stream-K style: the 32-key tiles of all decode-like sequences are
+//    laid end to end and cut into `slots` equal shares of q tiles; the decode kernel's
+//    workgroup j processes share j, i.e. the pieces of the sequences that overlap
+//    [j*q, (j+1)*q). Even mode cuts sequence b into ceil(L_b / C_b) pieces with
+//    C_b = ceil(L_b / splits) rounded up to the tile, listed whole pieces first and taken from a
+//    dynamic counter.
+//  * Every query row of a sequence cut into >= 2 pieces gets nsplit partial units and one entry
+//    of the combine list; a sequence left whole writes its output directly.
+//  * Longer sequences get tiles of tpi_pre rows, the last (longest causal) tile of each first.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __shared__ long long sh_ll[kPlanThreads / 64];
     __shared__ int sh_i[kPlanThreads / 64 * 4];
     const int tid = threadIdx.x;
+    const bool streamk = a.mode == 0;
 
-    // Pass 1: decode-like sequences (1 <= n_b <= tpi_dec): count and longest key range.
-    int ndec = 0, maxL = 0;
+    auto decode_like = [&](int n) { return n >= 1 && n <= a.tpi_dec; };
+    auto piece_keys = [&](int L) { return round_tile(ceil_div_i(L, a.splits)); };
+
+    // Pass 1: tiles of decode-like sequences; in even mode, the count of whole pieces.
+    long long ntiles = 0, nfull = 0;
     for (int b = tid; b < a.B; b += kPlanThreads) {
         const int n = a.cu[b + 1] - a.cu[b];
-        if (n >= 1 && n <= a.tpi_dec) {
-            ++ndec;
-            maxL = max(maxL, a.past[b] + n);
+        if (!decode_like(n)) continue;
+        const int L = a.past[b] + n;
+        ntiles += ceil_div_i(L, kTileKeys);
+        if (!streamk) {
+            const int Cb = piece_keys(L);
+            const int c = ceil_div_i(L, Cb);
+            nfull += (L % Cb == 0) ? c : c - 1;
         }
     }
-    ndec = (int)block_sum_ll(ndec, sh_ll);
-    maxL = block_max_i(maxL, sh_ll);
-
-    // Auto mode: smallest chunk (multiple of 32, >= min_chunk) whose item count fits the target.
-    int C = max(kTileKeys, ((maxL + kTileKeys - 1) / kTileKeys) * kTileKeys);
-    if (a.mode == 0 && ndec > 0) {
-        const long long want = max((long long)ndec, (long long)max(1, a.target_units / a.G));
-        int lo = max(1, (a.min_chunk + kTileKeys - 1) / kTileKeys), hi = C / kTileKeys;
-        if (lo > hi) lo = hi;
-        while (lo < hi) {  // smallest k in [lo, hi] with items(32k) <= want
-            const int mid = (lo + hi) / 2;
-            const int Cm = mid * kTileKeys;
-            long long items = 0;
-            for (int b = tid; b < a.B; b += kPlanThreads) {
-                const int n = a.cu[b + 1] - a.cu[b];
-                if (n >= 1 && n <= a.tpi_dec) items += ceil_div_i(a.past[b] + n, Cm);
-            }
-            items = block_sum_ll(items, sh_ll);
-            if (items <= want) hi = mid; else lo = mid + 1;
-        }
-        C = lo * kTileKeys;
+    ntiles = block_sum_ll(ntiles, sh_ll);
+    const int full_total = (int)block_sum_ll(nfull, sh_ll);
+    long long q = 1;
+    int used = 0;
+    if (streamk && ntiles > 0) {
+        const long long min_tiles = max(1, (a.min_chunk + kTileKeys - 1) / kTileKeys);
+        q = max(min_tiles, (ntiles + a.slots - 1) / a.slots);
+        used = (int)((ntiles + q - 1) / q);
     }
 
-    // Pass 2: per-sequence counts, exclusive scans, item lists.
-    int carry[4] = {0, 0, 0, 0};  // dec items, partial units, combine rows, prefill items
+    // Pass 2: per-sequence counts, scans, lists.
+    // carry: decode items, partial units, combine rows, prefill tiles, tiles before the chunk
+    int carry[4] = {0, 0, 0, 0};
+    long long carry_tiles = 0;
+    int carry_tail = 0;
     for (int base = 0; base < a.B; base += kPlanThreads) {
         const int b = base + tid;
-        int cnt[4] = {0, 0, 0, 0};
-        int n = 0, L = 0, Cb = 0, c = 0, past = 0, cu0 = 0;
+        int n = 0, L = 0, past = 0, cu0 = 0, T = 0;
         if (b < a.B) {
             cu0 = a.cu[b];
             n = a.cu[b + 1] - cu0;
             past = a.past[b];
             L = past + n;
-            if (n >= 1 && n <= a.tpi_dec) {
-                Cb = chunk_of(a.mode, C, a.splits, L);
-                c = ceil_div_i(L, Cb);
+            if (decode_like(n)) T = ceil_div_i(L, kTileKeys);
+        }
+        int tv[1] = {T}, tex[1], ttot[1];
+        block_scan<1>(tv, tex, ttot, sh_i);
+        const long long TB = carry_tiles + tex[0];   // first global tile of sequence b
+        int c = 0, Cb = 1, tail = 0;
+        int cnt[4] = {0, 0, 0, 0};
+        if (b < a.B) {
+            if (decode_like(n)) {
+                if (streamk) {
+                    c = (int)((TB + T - 1) / q - TB / q + 1);
+                } else {
+                    Cb = piece_keys(L);
+                    c = ceil_div_i(L, Cb);
+                    tail = (L % Cb == 0) ? 0 : 1;
+                }
                 cnt[0] = c;
                 if (c >= 2) {
                     cnt[1] = n * c;
@@ -155,20 +175,36 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             }
         }
         int ex[4], tot[4];
-        block_scan4(cnt, ex, tot, sh_i);
+        block_scan<4>(cnt, ex, tot, sh_i);
+        int tl_[1] = {tail}, tlex[1], tltot[1];
+        block_scan<1>(tl_, tlex, tltot, sh_i);
         if (b < a.B) {
             const int ubase = carry[1] + ex[1];
-            for (int s = 0; s < cnt[0]; ++s) {
-                const int idx = carry[0] + ex[0] + s;
-                if (idx < a.cap_dec) {
-                    AttnItem it;
-                    it.b = b; it.t0 = 0; it.k0 = s * Cb; it.k1 = min(L, (s + 1) * Cb);
-                    it.base = c >= 2 ? ubase : -1; it.nsplit = c; it.split = s; it.pad = 0;
-                    a.dec[idx] = it;
+            const int cbase = carry[2] + ex[2];
+            for (int sp = 0; sp < c; ++sp) {
+                AttnItem it;
+                it.b = b; it.t0 = 0;
+                it.base = c >= 2 ? ubase : -1; it.nsplit = c; it.split = sp;
+                it.comb = c >= 2 ? cbase : -1;
+                int idx;
+                if (streamk) {
+                    idx = carry[0] + ex[0] + sp;
+                    const long long j = TB / q + sp;
+                    const long long t0 = max(TB, j * q), t1 = min(TB + T, (j + 1) * q);
+                    it.k0 = (int)(t0 - TB) * kTileKeys;
+                    it.k1 = min(L, (int)(t1 - TB) * kTileKeys);
+                    if (t0 == j * q && j < a.slots) a.slot_ptr[j] = idx;
+                } else {
+                    const bool is_tail = sp >= c - tail;
+                    idx = is_tail ? full_total + carry_tail + tlex[0] : carry[0] - carry_tail +
+                                                                            (ex[0] - tlex[0]) + sp;
+                    it.k0 = sp * Cb;
+                    it.k1 = min(L, (sp + 1) * Cb);
                 }
+                if (idx < a.cap_dec) a.dec[idx] = it;
             }
             for (int t = 0; t < cnt[2]; ++t) {
-                const int idx = carry[2] + ex[2] + t;
+                const int idx = cbase + t;
                 if (idx < a.cap_comb) {
                     CombItem ci;
                     ci.row = cu0 + t; ci.e0 = ubase + t * c; ci.count = c; ci.pad = 0;
@@ -178,23 +214,31 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             for (int j = 0; j < cnt[3]; ++j) {
                 const int idx = carry[3] + ex[3] + j;
                 if (idx < a.cap_pre) {
-                    const int tlast = min(n, (j + 1) * a.tpi_pre) - 1;
+                    const int tile = cnt[3] - 1 - j;   // longest (last) tile first
+                    const int tlast = min(n, (tile + 1) * a.tpi_pre) - 1;
                     AttnItem it;
-                    it.b = b; it.t0 = j * a.tpi_pre; it.k0 = 0;
+                    it.b = b; it.t0 = tile * a.tpi_pre; it.k0 = 0;
                     it.k1 = a.causal ? past + tlast + 1 : L;
-                    it.base = -1; it.nsplit = 1; it.split = 0; it.pad = 0;
+                    it.base = -1; it.nsplit = 1; it.split = 0; it.comb = -1;
                     a.pre[idx] = it;
                 }
             }
         }
         for (int k = 0; k < 4; ++k) carry[k] += tot[k];
+        carry_tiles += ttot[0];
+        carry_tail += tltot[0];
     }
+    const int ndec_items = min(carry[0], a.cap_dec);
+    if (streamk)
+        for (int j = used + tid; j <= a.slots; j += kPlanThreads) a.slot_ptr[j] = ndec_items;
     if (tid == 0) {
-        a.hdr->n_dec = min(carry[0], a.cap_dec);
+        a.hdr->n_dec = ndec_items;
         a.hdr->units = carry[1];
         a.hdr->n_comb = min(carry[2], a.cap_comb);
         a.hdr->n_pre = min(carry[3], a.cap_pre);
-        a.hdr->chunk = C;
+        a.hdr->chunk = (int)(q * kTileKeys);
+        a.hdr->next_dec = 0;
+        a.hdr->next_pre = 0;
     }
 }
 
@@ -222,52 +266,76 @@ struct Tile {
     uint32_t v[8][W / 2];              // keys 8*g16 + s, dims W*n16 .. W*n16 + W - 1
 };
 
-template <int D, bool POW2>
-__device__ __forceinline__ void load_tile(Tile<D> &t, const AttnArgs &a, int b, int g, int kt,
-                                          int k1, int g16, int n16) {
+// Physical blocks a lane needs for the tile at kt (power-of-two block sizes >= 8): bk for its
+// K row group (keys kt + 8*(n16/4) ..) and bv for its V row group (keys kt + 8*g16 ..). Groups
+// past the last valid key are clamped to it, so no table entry beyond the range is read.
+struct TileIds {
+    int bk, bv;
+};
+
+__device__ __forceinline__ TileIds tile_ids(const AttnArgs &a, const int32_t *bt, int kt, int k1,
+                                            int g16, int n16) {
+    const int lastg = (k1 - 1) & ~7;
+    TileIds r;
+    r.bk = bt[min(kt + 8 * (n16 >> 2), lastg) >> a.log2bs];
+    r.bv = bt[min(kt + 8 * g16, lastg) >> a.log2bs];
+    return r;
+}
+
+// Issue the 16 loads of the tile at kt. kcg / vcg point at kv head g of cache row 0. A row of
+// key j inside block B sits at B*block_elems + (j mod bs)*key_elems, so each lane forms one
+// 64-bit block base per row group and adds 32-bit in-block offsets. Keys past k1 - 1 load key
+// k1 - 1 instead (their scores are masked), so nothing outside the sequence is read.
+template <int D, bool POW2, bool NT>
+__device__ __forceinline__ void load_tile(Tile<D> &t, const AttnArgs &a, const int32_t *bt,
+                                          TileIds ids, const half_t *kcg, const half_t *vcg,
+                                          int kt, int k1, int g16, int n16) {
     constexpr int KB = Tile<D>::KB, W = Tile<D>::W;
-    const int32_t *bt = a.bt + (long long)b * a.MB;
     const int kl = k1 - 1;
-    size_t rowK[2], rowV[8];
+    const uint32_t ke = a.key_elems;
+    const half_t *pk[2];
+    const half_t *pv[8];
     if (POW2) {
         // bs is a power of two >= 8, so each aligned 8-key group lies inside one block.
         const int lastg = kl & ~7;
         const int gk = min(kt + 8 * (n16 >> 2), lastg);
         const int gv = min(kt + 8 * g16, lastg);
-        const int bk = bt[gk >> a.log2bs];
-        const int bv = bt[gv >> a.log2bs];
         const int mask = a.bs - 1;
-        for (int u = 0; u < 2; ++u) {
-            const int key = min(kt + kappa(u, n16), kl);
-            rowK[u] = ((size_t)bk * a.bs + (gk & mask) + (key - gk)) * a.G + g;
-        }
-        for (int s = 0; s < 8; ++s) {
-            const int key = min(kt + 8 * g16 + s, kl);
-            rowV[s] = ((size_t)bv * a.bs + (gv & mask) + (key - gv)) * a.G + g;
+        // In-block offsets use 24-bit multiplies: key_elems < 2^24 is checked on the host.
+        const half_t *bK = kcg + (size_t)ids.bk * a.block_elems + __umul24(gk & mask, ke);
+        const half_t *bV = vcg + (size_t)ids.bv * a.block_elems + __umul24(gv & mask, ke);
+        if (kt + kTileKeys <= k1) {
+            const uint32_t r0 = __umul24(n16 & 3, ke);
+            pk[0] = bK + r0;
+            pk[1] = bK + r0 + 4 * ke;
+            for (int s = 0; s < 8; ++s) pv[s] = bV + (uint32_t)s * ke;
+        } else {
+            for (int u = 0; u < 2; ++u) pk[u] = bK + __umul24(min(kt + kappa(u, n16), kl) - gk, ke);
+            for (int s = 0; s < 8; ++s) pv[s] = bV + __umul24(min(kt + 8 * g16 + s, kl) - gv, ke);
         }
     } else {
         for (int u = 0; u < 2; ++u) {
             const int key = min(kt + kappa(u, n16), kl);
             const int j = key / a.bs;
-            rowK[u] = ((size_t)bt[j] * a.bs + (key - j * a.bs)) * a.G + g;
+            pk[u] = kcg + (size_t)bt[j] * a.block_elems + (uint32_t)(key - j * a.bs) * ke;
         }
         for (int s = 0; s < 8; ++s) {
             const int key = min(kt + 8 * g16 + s, kl);
             const int j = key / a.bs;
-            rowV[s] = ((size_t)bt[j] * a.bs + (key - j * a.bs)) * a.G + g;
+            pv[s] = vcg + (size_t)bt[j] * a.block_elems + (uint32_t)(key - j * a.bs) * ke;
         }
     }
-    for (int u = 0; u < 2; ++u) {
-        const half_t *p = a.kc + rowK[u] * D + 8 * g16;
-        for (int kb = 0; kb < KB; ++kb) t.k[u][kb] = *(const half8_t *)(p + 32 * kb);
-    }
+    for (int u = 0; u < 2; ++u)
+        for (int kb = 0; kb < KB; ++kb)
+            t.k[u][kb] = NT ? gload_nt<half8_t>(pk[u] + 8 * g16 + 32 * kb)
+                            : gload<half8_t>(pk[u] + 8 * g16 + 32 * kb);
     for (int s = 0; s < 8; ++s) {
-        const half_t *p = a.vc + rowV[s] * D + W * n16;
+        const half_t *p = pv[s] + W * n16;
         if constexpr (W == 8) {
-            const u32x4_t x = *(const u32x4_t *)p;
+            const u32x4_t x = NT ? gload_nt<u32x4_t>(p) : gload<u32x4_t>(p);
             t.v[s][0] = x[0]; t.v[s][1] = x[1]; t.v[s][2] = x[2]; t.v[s][3] = x[3];
         } else {
-            const u32x2_t x = *(const u32x2_t *)p;
+            const u32x2_t x = NT ? gload_nt<u32x2_t>(p) : gload<u32x2_t>(p);
             t.v[s][0] = x[0]; t.v[s][1] = x[1];
         }
     }
@@ -358,128 +426,180 @@ __device__ __forceinline__ void tile_softmax_pv(State<D, NCB> &st, const float4_
     }
 }
 
-template <int D, int NCB, bool POW2>
-__global__ __launch_bounds__(64) void attn_kernel(AttnArgs a) {
+// Work of one (item, kv head) unit: one wave.
+template <int D, int NCB, bool POW2, bool NT>
+__device__ __forceinline__ void process_unit(const AttnArgs &a, const AttnItem &it, int g,
+                                             int lane) {
     constexpr int KB = D / 32, W = D / 16;
-    const int lane = threadIdx.x;
     const int g16 = lane >> 4, n16 = lane & 15;
-    const int n_work = a.n_items[0] * a.G;
-    for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
-        const AttnItem it = a.items[w / a.G];
-        const int g = w - (w / a.G) * a.G;
-        const int cu_b = a.cu[it.b];
-        const int n_b = a.cu[it.b + 1] - cu_b;
-        const int past_b = a.past[it.b];
-        const int ntok = min(a.tpi, n_b - it.t0);
-        const int ncols = ntok * a.Q;
+    const int cu_b = a.cu[it.b];
+    const int n_b = a.cu[it.b + 1] - cu_b;
+    const int past_b = a.past[it.b];
+    const int ntok = min(a.tpi, n_b - it.t0);
+    const int ncols = ntok * a.Q;
 
-        State<D, NCB> st;
-        for (int cb = 0; cb < NCB; ++cb) {
-            const int col = cb * 16 + n16;
-            st.m[cb] = -INFINITY;
-            st.l[cb] = 0.f;
-            for (int i = 0; i < W; ++i) st.o[cb][i] = float4_t{0.f, 0.f, 0.f, 0.f};
-            if (col < ncols) {
-                const int t = col / a.Q, qh = col - t * a.Q;
-                const half_t *qp = a.query + (long long)(cu_b + it.t0 + t) * a.q_stride +
-                                   (long long)(g * a.Q + qh) * D + 8 * g16;
-                for (int kb = 0; kb < KB; ++kb) st.q[cb][kb] = *(const half8_t *)(qp + 32 * kb);
-                const int lim = a.causal ? past_b + it.t0 + t + 1 : past_b + n_b;
-                st.kend[cb] = min(lim, it.k1);
-            } else {
-                for (int kb = 0; kb < KB; ++kb) st.q[cb][kb] = half8_t{};
-                st.kend[cb] = 0;
-            }
+    State<D, NCB> st;
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int col = cb * 16 + n16;
+        st.m[cb] = -INFINITY;
+        st.l[cb] = 0.f;
+        for (int i = 0; i < W; ++i) st.o[cb][i] = float4_t{0.f, 0.f, 0.f, 0.f};
+        if (col < ncols) {
+            const int t = col / a.Q, qh = col - t * a.Q;
+            const half_t *qp = a.query + (long long)(cu_b + it.t0 + t) * a.q_stride +
+                               (long long)(g * a.Q + qh) * D + 8 * g16;
+            for (int kb = 0; kb < KB; ++kb) st.q[cb][kb] = *(const half8_t *)(qp + 32 * kb);
+            const int lim = a.causal ? past_b + it.t0 + t + 1 : past_b + n_b;
+            st.kend[cb] = min(lim, it.k1);
+        } else {
+            for (int kb = 0; kb < KB; ++kb) st.q[cb][kb] = half8_t{};
+            st.kend[cb] = 0;
         }
+    }
 
-        // One tile buffer: the tile's scores and V^T operands are formed first, then the next
-        // tile's loads reuse its registers while the softmax and PV of this tile run.
+    // One tile buffer. In each step the tile's scores and V^T operands are formed first,
+    // then the next tile's loads are issued while softmax and PV run. The last tile is
+    // peeled off so the in-loop load is unconditional. The block ids of tile t+2 are
+    // requested before the data loads of tile t+1, so by the time a tile's loads issue its
+    // ids have arrived (loads complete in order).
+    const int32_t *bt = a.bt + (long long)it.b * a.MB;
+    const half_t *kcg = a.kc + (size_t)g * D;
+    const half_t *vcg = a.vc + (size_t)g * D;
+    if (it.k0 < it.k1) {
         Tile<D> tl;
         int kt = it.k0;
-        if (kt < it.k1) load_tile<D, POW2>(tl, a, it.b, g, kt, it.k1, g16, n16);
-        while (kt < it.k1) {
+        TileIds ids2 = {0, 0};
+        if (POW2) ids2 = tile_ids(a, bt, kt, it.k1, g16, n16);
+        load_tile<D, POW2, NT>(tl, a, bt, ids2, kcg, vcg, kt, it.k1, g16, n16);
+        if (POW2 && kt + kTileKeys < it.k1)
+            ids2 = tile_ids(a, bt, kt + kTileKeys, it.k1, g16, n16);
+        for (; kt + kTileKeys < it.k1; kt += kTileKeys) {
             float4_t s[NCB][2];
             tile_scores<D, NCB>(st, tl, s);
             half8_t vb[W];
             tile_vt<D>(tl, vb);
             const int kn = kt + kTileKeys;
-            if (kn < it.k1) load_tile<D, POW2>(tl, a, it.b, g, kn, it.k1, g16, n16);
+            TileIds ids3 = ids2;
+            if (POW2 && kn + kTileKeys < it.k1)
+                ids3 = tile_ids(a, bt, kn + kTileKeys, it.k1, g16, n16);
+            load_tile<D, POW2, NT>(tl, a, bt, ids2, kcg, vcg, kn, it.k1, g16, n16);
             tile_softmax_pv<D, NCB>(st, s, vb, kt, a.scale_log2, g16);
-            kt = kn;
+            ids2 = ids3;
         }
+        float4_t s[NCB][2];
+        tile_scores<D, NCB>(st, tl, s);
+        half8_t vb[W];
+        tile_vt<D>(tl, vb);
+        tile_softmax_pv<D, NCB>(st, s, vb, kt, a.scale_log2, g16);
+    }
 
-        // Column totals, then each lane writes rows 4*g16 + j of every column block.
-        for (int cb = 0; cb < NCB; ++cb) {
-            float lt = st.l[cb] + __shfl_xor(st.l[cb], 16, 64);
-            lt += __shfl_xor(lt, 32, 64);
-            float lr[4], mr[4];
-            for (int j = 0; j < 4; ++j) {
-                lr[j] = __shfl(lt, 4 * g16 + j, 64);
-                mr[j] = __shfl(st.m[cb], 4 * g16 + j, 64);
-            }
-            for (int j = 0; j < 4; ++j) {
-                const int col = cb * 16 + 4 * g16 + j;
-                if (col >= ncols) continue;
-                const int t = col / a.Q, qh = col - t * a.Q;
-                const int h = g * a.Q + qh;
-                const long long row = cu_b + it.t0 + t;
-                if (it.base < 0) {
-                    const float inv = 1.f / lr[j];
-                    half_t *op = a.out + row * (long long)a.H * D + (long long)h * D + W * n16;
-                    if constexpr (W == 8) {
-                        half8_t r;
-                        for (int i = 0; i < W; ++i) r[i] = (half_t)(st.o[cb][i][j] * inv);
-                        *(half8_t *)op = r;
-                    } else {
-                        half4_t r;
-                        for (int i = 0; i < W; ++i) r[i] = (half_t)(st.o[cb][i][j] * inv);
-                        *(half4_t *)op = r;
-                    }
+    // Column totals, then each lane writes rows 4*g16 + j of every column block.
+    for (int cb = 0; cb < NCB; ++cb) {
+        float lt = st.l[cb] + __shfl_xor(st.l[cb], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        float lr[4], mr[4];
+        for (int j = 0; j < 4; ++j) {
+            lr[j] = __shfl(lt, 4 * g16 + j, 64);
+            mr[j] = __shfl(st.m[cb], 4 * g16 + j, 64);
+        }
+        for (int j = 0; j < 4; ++j) {
+            const int col = cb * 16 + 4 * g16 + j;
+            if (col >= ncols) continue;
+            const int t = col / a.Q, qh = col - t * a.Q;
+            const int h = g * a.Q + qh;
+            const long long row = cu_b + it.t0 + t;
+            if (it.base < 0) {
+                const float inv = 1.f / lr[j];
+                half_t *op = a.out + row * (long long)a.H * D + (long long)h * D + W * n16;
+                if constexpr (W == 8) {
+                    half8_t r;
+                    for (int i = 0; i < W; ++i) r[i] = (half_t)(st.o[cb][i][j] * inv);
+                    *(half8_t *)op = r;
                 } else {
-                    const long long p =
-                        (long long)(it.base + t * it.nsplit + it.split) * a.H + h;
-                    float *op = a.o_part + p * D + W * n16;
-                    for (int i = 0; i < W; i += 4)
-                        *(float4_t *)(op + i) = float4_t{st.o[cb][i][j], st.o[cb][i + 1][j],
-                                                         st.o[cb][i + 2][j], st.o[cb][i + 3][j]};
-                    if (n16 == 0) {
-                        a.m_part[p] = (lr[j] > 0.f) ? mr[j] * kLn2 : kNegLarge;
-                        a.l_part[p] = lr[j];
-                    }
+                    half4_t r;
+                    for (int i = 0; i < W; ++i) r[i] = (half_t)(st.o[cb][i][j] * inv);
+                    *(half4_t *)op = r;
+                }
+            } else {
+                const long long p =
+                    (long long)(it.base + t * it.nsplit + it.split) * a.H + h;
+                float *op = a.o_part + p * D + W * n16;
+                for (int i = 0; i < W; i += 4)
+                    *(float4_t *)(op + i) = float4_t{st.o[cb][i][j], st.o[cb][i + 1][j],
+                                                     st.o[cb][i + 2][j], st.o[cb][i + 3][j]};
+                if (n16 == 0) {
+                    a.m_part[p] = (lr[j] > 0.f) ? mr[j] * kLn2 : kNegLarge;
+                    a.l_part[p] = lr[j];
                 }
             }
         }
     }
 }
 
-template <int D, int NCB>
-pa_status launch_d_ncb(const AttnArgs &a, int grid, hipStream_t stream) {
+// Persistent kernel. A workgroup holds a.gw waves (gw divides G; gw = 1 unless NCB == 1), so
+// the kv heads of one work item run side by side on one CU and read neighbouring rows of the
+// same cache blocks. With a
+// slot table (stream-K balanced decode) workgroup j processes the items of share j; otherwise
+// workgroups take (item, head group) units from the planner's counter, longest items first.
+template <int D, int NCB, bool POW2, bool NT>
+__global__ __launch_bounds__(NCB == 1 ? 512 : 64) void attn_kernel(AttnArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int gblocks = a.G / a.gw;
+    if (a.slot_ptr) {
+        const int u0 = a.slot_ptr[blockIdx.x] * gblocks, u1 = a.slot_ptr[blockIdx.x + 1] * gblocks;
+        for (int unit = u0; unit < u1; ++unit) {
+            const AttnItem it = a.items[unit / gblocks];
+            const int g = (unit - (unit / gblocks) * gblocks) * a.gw + wave;
+            process_unit<D, NCB, POW2, NT>(a, it, g, lane);
+        }
+        return;
+    }
+    __shared__ int s_unit;
+    const int n_work = a.n_items[0] * gblocks;
+    for (;;) {
+        if (threadIdx.x == 0) s_unit = atomicAdd(a.counter, 1);
+        __syncthreads();
+        const int unit = s_unit;
+        __syncthreads();
+        if (unit >= n_work) break;
+        const AttnItem it = a.items[unit / gblocks];
+        const int g = (unit - (unit / gblocks) * gblocks) * a.gw + wave;
+        process_unit<D, NCB, POW2, NT>(a, it, g, lane);
+    }
+}
+
+template <int D, int NCB, bool NT>
+pa_status launch_d_ncb(const AttnArgs &a, int blocks, hipStream_t stream) {
+    const dim3 g(blocks), blk(64 * a.gw);
     if (a.log2bs >= 0)
-        hipLaunchKernelGGL((attn_kernel<D, NCB, true>), dim3(grid), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((attn_kernel<D, NCB, true, NT>), g, blk, 0, stream, a);
     else
-        hipLaunchKernelGGL((attn_kernel<D, NCB, false>), dim3(grid), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((attn_kernel<D, NCB, false, NT>), g, blk, 0, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-template <int D>
-pa_status launch_d(const AttnArgs &a, int ncb, int grid, hipStream_t stream) {
+template <int D, bool NT>
+pa_status launch_d(const AttnArgs &a, int ncb, int blocks, hipStream_t stream) {
     switch (ncb) {
-        case 1: return launch_d_ncb<D, 1>(a, grid, stream);
-        case 2: return launch_d_ncb<D, 2>(a, grid, stream);
-        case 4: return launch_d_ncb<D, 4>(a, grid, stream);
+        case 1: return launch_d_ncb<D, 1, NT>(a, blocks, stream);
+        case 2: return launch_d_ncb<D, 2, NT>(a, blocks, stream);
+        case 4: return launch_d_ncb<D, 4, NT>(a, blocks, stream);
         default: return PA_ERR_UNSUPPORTED;
     }
 }
 
 }  // namespace
 
-pa_status launch_attention(const AttnArgs &a, int D, int ncb, int grid, const char *name,
-                           hipStream_t stream) {
+pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, bool streaming,
+                           const char *name, hipStream_t stream) {
     LaunchScope scope(name, stream);
-    if (grid <= 0) return PA_OK;
-    switch (D) {
-        case 64: return launch_d<64>(a, ncb, grid, stream);
-        case 128: return launch_d<128>(a, ncb, grid, stream);
+    if (blocks <= 0) return PA_OK;
+    switch (D * 2 + (streaming ? 1 : 0)) {
+        case 128: return launch_d<64, false>(a, ncb, blocks, stream);
+        case 129: return launch_d<64, true>(a, ncb, blocks, stream);
+        case 256: return launch_d<128, false>(a, ncb, blocks, stream);
+        case 257: return launch_d<128, true>(a, ncb, blocks, stream);
         default: return PA_ERR_UNSUPPORTED;
     }
 }

@@ -8,9 +8,8 @@
 //
 // The pass streams the partial vectors once: HBM-bound. D/4 lanes own one output row (a float4
 // each), so a wave covers 64*4/D rows; the rows of one unit are adjacent in memory, so a wave's
-// loads for one unit are one contiguous span. Statistics (m, l) of a row are reduced first
-// (lanes stride over units), then the o vectors stream with the unit loop unrolled by 4 to keep
-// several loads in flight per lane.
+// loads for one unit are one contiguous span. Units are merged online, eight per memory round
+// trip (running max, rescaled sums), so a row costs ceil(units / 8) dependent loads.
 #include "common.h"
 
 namespace pa {
@@ -20,6 +19,7 @@ template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int mode) {
     constexpr int LPR = D / 4;      // lanes per row
     constexpr int RPW = 64 / LPR;   // rows per wave
+    constexpr int NB = 8;           // units loaded per round trip
     const int lane = threadIdx.x & 63;
     const int sub = lane % LPR;     // float4 index inside the row
     const int rw = lane / LPR;      // row inside the wave's row block
@@ -44,41 +44,34 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int mode) {
         const bool active = lane_row < a.lanes;
         const int lr = active ? lane_row : 0;
 
-        // Row statistics: lanes of the row stride over its units.
-        float M = -INFINITY;
-        for (long long e = e0 + sub; e < e1; e += LPR) {
-            const long long p = e * a.lanes + lr;
-            if (a.l[p] > 0.f) M = fmaxf(M, a.m[p]);
-        }
-        for (int o = 1; o < LPR; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        float Ls = 0.f;
-        for (long long e = e0 + sub; e < e1; e += LPR) {
-            const long long p = e * a.lanes + lr;
-            const float lv = a.l[p];
-            if (lv > 0.f) Ls += __builtin_amdgcn_exp2f((a.m[p] - M) * kLog2e) * lv;
-        }
-        for (int o = 1; o < LPR; o <<= 1) Ls += __shfl_xor(Ls, o, 64);
-
-        // Weighted sum of the o vectors.
+        // Online merge, NB units per round trip: every lane of the row loads the units' m and l
+        // (one broadcast line) and its own float4 of o, all before any of them is used.
+        float M = -INFINITY, Ls = 0.f;
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
-        long long e = e0;
-        for (; e + 4 <= e1; e += 4) {
-            float4_t v[4];
-            float wgt[4];
-            for (int u = 0; u < 4; ++u) {
-                const long long p = (e + u) * a.lanes + lr;
-                v[u] = *(const float4_t *)(a.o + p * D + 4 * sub);
-                const float lv = a.l[p];
-                wgt[u] = lv > 0.f ? __builtin_amdgcn_exp2f((a.m[p] - M) * kLog2e) : 0.f;
+        for (long long e = e0; e < e1; e += NB) {
+            float mv[NB], lv[NB];
+            float4_t ov[NB];
+            for (int u = 0; u < NB; ++u) {
+                const long long eu = e + u < e1 ? e + u : e1 - 1;
+                const long long p = eu * a.lanes + lr;
+                mv[u] = a.m[p];
+                lv[u] = e + u < e1 ? a.l[p] : 0.f;
+                ov[u] = gload_nt<float4_t>(a.o + p * D + 4 * sub);
             }
-            for (int u = 0; u < 4; ++u) acc += wgt[u] * v[u];
-        }
-        for (; e < e1; ++e) {
-            const long long p = e * a.lanes + lr;
-            const float4_t v = *(const float4_t *)(a.o + p * D + 4 * sub);
-            const float lv = a.l[p];
-            const float wgt = lv > 0.f ? __builtin_amdgcn_exp2f((a.m[p] - M) * kLog2e) : 0.f;
-            acc += wgt * v;
+            float bm = -INFINITY;
+            for (int u = 0; u < NB; ++u)
+                if (lv[u] > 0.f) bm = fmaxf(bm, mv[u]);
+            if (bm == -INFINITY) continue;             // no unit of this batch counts
+            const float Mn = fmaxf(M, bm);
+            const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
+            acc *= sc;
+            Ls *= sc;
+            for (int u = 0; u < NB; ++u) {
+                const float wu = lv[u] > 0.f ? __builtin_amdgcn_exp2f((mv[u] - Mn) * kLog2e) : 0.f;
+                acc += wu * ov[u];
+                Ls += wu * lv[u];
+            }
+            M = Mn;
         }
         if (!active) continue;
         const float inv = Ls > 0.f ? 1.f / Ls : 0.f;

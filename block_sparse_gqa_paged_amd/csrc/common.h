@@ -67,7 +67,7 @@ struct AttnItem {
     int32_t base;  // first partial unit of the sequence, or -1: write the output directly
     int32_t nsplit;  // chunks the sequence's key range is cut into
     int32_t split;   // this item's chunk
-    int32_t pad;
+    int32_t comb;    // combine-list entry of the item's first row, or -1
 };
 
 // Combine work entry for one output row group (a query row with >= 2 partial units).
@@ -85,7 +85,9 @@ struct PlanHeader {
     int32_t n_comb;     // combine entries
     int32_t chunk;      // chunk keys chosen for split decode (0 when no split)
     int32_t units;      // partial units used
-    int32_t pad[59];    // keeps the lists 256-byte aligned
+    int32_t next_dec;   // dynamic scheduling counters, zeroed by the planner
+    int32_t next_pre;
+    int32_t pad[57];    // keeps the lists 256-byte aligned
 };
 
 struct PlanArgs {
@@ -94,12 +96,13 @@ struct PlanArgs {
     int B, G, causal;
     int tpi_dec;        // max tokens of a decode-like item
     int tpi_pre;        // tokens per prefill item
-    int mode;           // 0: auto chunk, 1: even split into `splits`
+    int mode;           // 0: stream-K shares over `slots`, 1: even split into `splits`
     int splits;         // S for mode 1
-    int target_units;   // mode 0: wanted decode work units (items * G)
     int min_chunk;      // mode 0: smallest chunk
     int unit_cap;       // partial units that fit the workspace
     int cap_dec, cap_pre, cap_comb;
+    int slots;          // mode 0: decode workgroups, one key-range share each
+    int32_t *slot_ptr;  // mode 0: [slots + 1] first item of each share
     PlanHeader *hdr;
     AttnItem *dec;
     AttnItem *pre;
@@ -116,19 +119,25 @@ struct AttnArgs {
     const int32_t *bt;
     const AttnItem *items;
     const int32_t *n_items;  // device count of items
+    int32_t *counter;        // dynamic scheduling counter (zeroed by the planner)
+    const int32_t *slot_ptr; // stream-K share table [gridDim.x + 1], or NULL for dynamic
     half_t *out;
     float *o_part;
     float *m_part;
     float *l_part;
-    int64_t q_stride;  // elements per query row
+    int64_t q_stride;     // elements per query row
+    int64_t block_elems;  // elements per cache block: bs * G * D
+    uint32_t key_elems;   // elements between consecutive keys of a block: G * D
     int H, G, Q, bs, MB, log2bs;  // log2bs < 0: block size is not a power of two >= 8
     int causal;
+    int gw;            // waves per workgroup, a divisor of G
     int tpi;           // tokens per item
     float scale_log2;  // scale * log2(e)
 };
-// ncb: 16-column blocks of (token, head) columns per item (1, 2 or 4).
-pa_status launch_attention(const AttnArgs &a, int D, int ncb, int grid, const char *name,
-                           hipStream_t stream);
+// ncb: 16-column blocks of (token, head) columns per item (1, 2 or 4); blocks: workgroups of
+// a.gw waves; streaming: non-temporal K/V loads (data read once).
+pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, bool streaming,
+                           const char *name, hipStream_t stream);
 
 struct CombineArgs {
     const float *o;
@@ -165,6 +174,19 @@ size_t sparse_workspace_bytes(int E, int units);
 // ---------------------------------------------------------------------------------------------
 // Device helpers.
 // ---------------------------------------------------------------------------------------------
+// Load through a global (address space 1) pointer, so the access is a global_load rather than
+// a flat load that must also check the LDS and scratch apertures.
+template <class T>
+__device__ __forceinline__ T gload(const void *p) {
+    return *(const __attribute__((address_space(1))) T *)p;
+}
+
+// Streaming (non-temporal) global load, for data read once: K/V cache rows.
+template <class T>
+__device__ __forceinline__ T gload_nt(const void *p) {
+    return __builtin_nontemporal_load((const __attribute__((address_space(1))) T *)p);
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
     return fmaxf(v, __shfl_xor(v, mask, 64));
 }
