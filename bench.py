@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip mixed and sparse workloads")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a 1 GiB device copy (for counter calibration runs)")
+                    help="also run three 1 GiB device copies (for counter calibration runs)")
     return ap.parse_args()
 
 
@@ -134,6 +134,14 @@ def main():
     extra = {}
     if not args.no_extra:
         extra = run_extra(args, torch, np, pa, dev, W)
+    if args.copy_calibration:
+        # a plain device copy of known size, for scaling HBM counter readings
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes_each_way"] = src.numel() * 4
 
     line = {
         "metric": "paged-attn decode KV GB/s (% of HBM peak) and query tokens/s, 1 MI355X",
@@ -236,13 +244,6 @@ def run_extra(args, torch, np, pa, dev, W):
                                         / FP32_MFMA_PEAK_TFS, 4),
         "forward_flops": flops,
     }
-    if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = 2 * a.numel() * 4
     return out
 
 
