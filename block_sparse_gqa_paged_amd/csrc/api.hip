@@ -26,28 +26,43 @@ struct TimingRec {
 std::atomic<int> g_timing{0};
 std::mutex g_timing_mu;
 std::vector<TimingRec> g_pending;
+std::vector<hipEvent_t> g_free;  // recycled events
 std::map<std::string, std::pair<double, int64_t>> g_done;
+
+hipEvent_t take_event() {  // caller holds g_timing_mu
+    if (!g_free.empty()) {
+        hipEvent_t e = g_free.back();
+        g_free.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
 }  // namespace
 
-LaunchScope::LaunchScope(const char *name, hipStream_t stream)
-    : name_(name), stream_(stream), start_(nullptr) {
+LaunchScope::LaunchScope(const char *name, hipStream_t stream, int launches)
+    : name_(name), stream_(stream), start_(nullptr), stop_(nullptr), n_(launches), idx_(0) {
     if (!g_timing.load(std::memory_order_relaxed)) return;
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return;
-    (void)hipEventRecord(e, stream);
-    start_ = e;
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    start_ = take_event();
+    stop_ = take_event();
+    if (!start_ || !stop_) {
+        if (start_) g_free.push_back(start_);
+        if (stop_) g_free.push_back(stop_);
+        start_ = stop_ = nullptr;
+    }
 }
 
 LaunchScope::~LaunchScope() {
     if (!start_) return;
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) {
-        (void)hipEventDestroy((hipEvent_t)start_);
-        return;
-    }
-    (void)hipEventRecord(e, stream_);
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    g_pending.push_back(TimingRec{name_, (hipEvent_t)start_, e});
+    if (idx_ == n_) {
+        g_pending.push_back(TimingRec{name_, start_, stop_});
+    } else {  // not every planned kernel was launched (error or early exit): drop the record
+        g_free.push_back(start_);
+        g_free.push_back(stop_);
+    }
 }
 
 int device_cu_count() {
@@ -185,8 +200,8 @@ void pa_timing_reset(void) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     for (auto &r : g_pending) {
         (void)hipEventSynchronize(r.stop);
-        (void)hipEventDestroy(r.start);
-        (void)hipEventDestroy(r.stop);
+        g_free.push_back(r.start);
+        g_free.push_back(r.stop);
     }
     g_pending.clear();
     g_done.clear();
@@ -204,8 +219,8 @@ pa_status pa_timing_get(const char *kernel, double *total_ms, int64_t *launches)
         auto &d = g_done[r.name];
         d.first += ms;
         d.second += 1;
-        (void)hipEventDestroy(r.start);
-        (void)hipEventDestroy(r.stop);
+        g_free.push_back(r.start);
+        g_free.push_back(r.stop);
     }
     g_pending.clear();
     double t = 0.0;

@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
 pa_status launch_plan(const PlanArgs &a, hipStream_t stream) {
     LaunchScope scope("plan", stream);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
+    scope.launch(plan_kernel, dim3(1), dim3(kPlanThreads), 0, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -570,21 +570,21 @@ __global__ __launch_bounds__(NCB == 1 ? 512 : 64) void attn_kernel(AttnArgs a) {
 }
 
 template <int D, int NCB, bool NT>
-pa_status launch_d_ncb(const AttnArgs &a, int blocks, hipStream_t stream) {
+pa_status launch_d_ncb(const AttnArgs &a, int blocks, LaunchScope &scope) {
     const dim3 g(blocks), blk(64 * a.gw);
     if (a.log2bs >= 0)
-        hipLaunchKernelGGL((attn_kernel<D, NCB, true, NT>), g, blk, 0, stream, a);
+        scope.launch(attn_kernel<D, NCB, true, NT>, g, blk, 0, a);
     else
-        hipLaunchKernelGGL((attn_kernel<D, NCB, false, NT>), g, blk, 0, stream, a);
+        scope.launch(attn_kernel<D, NCB, false, NT>, g, blk, 0, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 template <int D, bool NT>
-pa_status launch_d(const AttnArgs &a, int ncb, int blocks, hipStream_t stream) {
+pa_status launch_d(const AttnArgs &a, int ncb, int blocks, LaunchScope &scope) {
     switch (ncb) {
-        case 1: return launch_d_ncb<D, 1, NT>(a, blocks, stream);
-        case 2: return launch_d_ncb<D, 2, NT>(a, blocks, stream);
-        case 4: return launch_d_ncb<D, 4, NT>(a, blocks, stream);
+        case 1: return launch_d_ncb<D, 1, NT>(a, blocks, scope);
+        case 2: return launch_d_ncb<D, 2, NT>(a, blocks, scope);
+        case 4: return launch_d_ncb<D, 4, NT>(a, blocks, scope);
         default: return PA_ERR_UNSUPPORTED;
     }
 }
@@ -596,10 +596,10 @@ pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, bool s
     LaunchScope scope(name, stream);
     if (blocks <= 0) return PA_OK;
     switch (D * 2 + (streaming ? 1 : 0)) {
-        case 128: return launch_d<64, false>(a, ncb, blocks, stream);
-        case 129: return launch_d<64, true>(a, ncb, blocks, stream);
-        case 256: return launch_d<128, false>(a, ncb, blocks, stream);
-        case 257: return launch_d<128, true>(a, ncb, blocks, stream);
+        case 128: return launch_d<64, false>(a, ncb, blocks, scope);
+        case 129: return launch_d<64, true>(a, ncb, blocks, scope);
+        case 256: return launch_d<128, false>(a, ncb, blocks, scope);
+        case 257: return launch_d<128, true>(a, ncb, blocks, scope);
         default: return PA_ERR_UNSUPPORTED;
     }
 }

@@ -101,10 +101,10 @@ pa_status launch_combine(const CombineArgs &a, int max_groups, hipStream_t strea
     const int grid = (int)((waves + 3) / 4);
     switch (a.D) {
         case 64:
-            hipLaunchKernelGGL(combine_kernel<64>, dim3(grid), dim3(256), 0, stream, a, mode);
+            scope.launch(combine_kernel<64>, dim3(grid), dim3(256), 0, a, mode);
             break;
         case 128:
-            hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, a, mode);
+            scope.launch(combine_kernel<128>, dim3(grid), dim3(256), 0, a, mode);
             break;
         default:
             return PA_ERR_UNSUPPORTED;

@@ -2,6 +2,7 @@
 // gfx950 (CDNA4) only: wave64, MFMA f32_16x16x32_f16 / f32_16x16x4_f32.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,13 +25,23 @@ constexpr float kNegLarge = -1.0e30f;  // the sentinel max of an empty partial
 // ---------------------------------------------------------------------------------------------
 // Host side: launch bookkeeping (timing hooks) and device properties.
 // ---------------------------------------------------------------------------------------------
+// Launch helper. When timing is enabled (pa_timing_enable), the first kernel launched through a
+// scope carries the start event and the last one the stop event, recorded by the dispatch
+// itself (hipExtLaunchKernelGGL), so the interval covers exactly the scope's kernels.
 struct LaunchScope {
-    // Records a HIP event pair around the kernels enqueued while it lives, when timing is on.
-    LaunchScope(const char *name, hipStream_t stream);
+    LaunchScope(const char *name, hipStream_t stream, int launches = 1);
     ~LaunchScope();
+    template <class F, class... Args>
+    void launch(F kernel, dim3 grid, dim3 block, uint32_t shmem, Args... args) {
+        hipEvent_t s = (idx_ == 0) ? start_ : nullptr;
+        hipEvent_t e = (idx_ == n_ - 1) ? stop_ : nullptr;
+        ++idx_;
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream_, s, e, 0, args...);
+    }
     const char *name_;
     hipStream_t stream_;
-    void *start_;
+    hipEvent_t start_, stop_;
+    int n_, idx_;
 };
 
 int device_cu_count();  // compute units of the current device (cached per device)

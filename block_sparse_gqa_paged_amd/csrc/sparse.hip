@@ -6,13 +6,21 @@
 // table row; unmapped pages contribute nothing), and writes the block-local, unnormalised
 // (o, m, l) at p = e*qhead + qh. block_len <= 0, or no mapped key, gives o = 0, m = -1e30, l = 0.
 //
-// MI355X design: edges are grouped by their (batch, h, blk) key block with a counting sort on
-// the device (histogram, scan, scatter into a workspace permutation), so one workgroup stages a
-// key block (K row-major, V transposed, both fp32) in LDS once and reuses it for up to kChunk
-// edges. Four waves each take 16 query rows (16 / qhead edges) at a time; S^T = K . Q^T and
-// O = P . V run on v_mfma_f32_16x16x4_f32. The S^T accumulator gives each lane 4 keys of one
-// query row, which are exactly its A-operand k-slots for the PV product, so P never leaves
-// registers. Results per edge do not depend on the grouping or the order.
+// MI355X design:
+//  * Edges are grouped by their (batch, h, blk) key block with a counting sort on the device:
+//    a histogram whose atomic returns each edge's rank, a scan, and a plain scatter into a
+//    workspace permutation. One workgroup then stages a key block in LDS once and reuses it for
+//    up to kChunk edges; results per edge do not depend on the grouping or the order.
+//  * fp32 products run as three fp16 MFMAs (v_mfma_f32_16x16x32_f16) on split operands:
+//    x = hi + lo with hi = fp16(x), lo = fp16(x - hi), and a.b ~ hi.hi + hi.lo + lo.hi with fp32
+//    accumulation; the dropped lo.lo term is ~2^-22 of the product. Before the split, K and V
+//    of the block and each query row are scaled by a power of two that brings their largest
+//    magnitude into [0.5, 1), which is exact and keeps every value inside fp16 range; the scale
+//    is folded back into the scores and the output.
+//  * S^T = K . Q^T has 16 keys as rows and 16 query rows as columns; its accumulator gives each
+//    lane 8 keys of one row across two key tiles, exactly the k-slots of the P operand of
+//    O = P . V, so P never leaves registers. K (row-major) and V (transposed) live in LDS as
+//    fp16 hi/lo planes with XOR-swizzled chunks.
 //
 // Edges whose batch, head, block or query index lie outside the shapes write the sentinel.
 #include "common.h"
@@ -24,7 +32,7 @@ constexpr int kChunk = 64;     // edges per work item
 constexpr int kThreads = 256;  // 4 waves
 
 struct SparseWs {
-    int32_t *counts, *cursor, *offs, *ioffs, *nitems, *item_unit, *perm;
+    int32_t *counts, *rank, *offs, *ioffs, *nitems, *item_unit, *perm;
     int max_items;
 };
 
@@ -35,7 +43,7 @@ SparseWs carve(int32_t *ws, int E, int units) {
     w.max_items = (E + kChunk - 1) / kChunk + units;
     size_t off = 0;
     w.counts = ws + off; off = al(off + units);
-    w.cursor = ws + off; off = al(off + units);
+    w.rank = ws + off; off = al(off + E);
     w.offs = ws + off; off = al(off + units + 1);
     w.ioffs = ws + off; off = al(off + units + 1);
     w.nitems = ws + off; off = al(off + 1);
@@ -61,13 +69,14 @@ __global__ void sp_zero(int32_t *p, int n) {
     if (i < n) p[i] = 0;
 }
 
-// Histogram of valid edges per key block; invalid and empty edges get their sentinel here.
+// Histogram of valid edges per key block (the returned count is the edge's rank in its block);
+// invalid and empty edges get their sentinel here.
 __global__ void sp_hist(SparseArgs a, SparseWs w) {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= a.E) return;
     int q, h, blk, b, len, unit;
     if (decode_edge(a, e, q, h, blk, b, len, unit)) {
-        atomicAdd(&w.counts[unit], 1);
+        w.rank[e] = atomicAdd(&w.counts[unit], 1);
         return;
     }
     for (int qh = 0; qh < a.qhead; ++qh) {
@@ -123,24 +132,41 @@ __global__ void sp_scatter(SparseArgs a, SparseWs w) {
     if (e >= a.E) return;
     int q, h, blk, b, len, unit;
     if (!decode_edge(a, e, q, h, blk, b, len, unit)) return;
-    const int pos = w.offs[unit] + atomicAdd(&w.cursor[unit], 1);
-    w.perm[pos] = e;
+    w.perm[w.offs[unit] + w.rank[e]] = e;
 }
 
-// LDS float4 chunk swizzle: chunk q of row r lives at q ^ (r & (nq - 1)) (nq = chunks per row,
-// a power of two), so the 16 rows a 16-lane group reads at one column hit distinct banks.
-__device__ __forceinline__ int swz(int row, int q, int nq) { return q ^ (row & (min(nq, 16) - 1)); }
+// Split a float (already scaled into [-1, 1]) into fp16 hi and lo parts: x ~ hi + lo.
+struct HiLo {
+    half_t hi, lo;
+};
+__device__ __forceinline__ HiLo split16(float x) {
+    const half_t hi = (half_t)x;
+    return HiLo{hi, (half_t)(x - (float)hi)};
+}
+
+// Power-of-two factor that brings max |x| = mx into [0.5, 1) (1 for mx == 0).
+__device__ __forceinline__ int pow2_exp(float mx) {
+    int e = 0;
+    (void)frexpf(mx, &e);
+    return mx > 0.f ? e : 0;
+}
+
+// XOR swizzle of chunk q in row r (nq chunks per row, a power of two): the 16 rows a 16-lane
+// group reads at one logical chunk land in distinct banks.
+__device__ __forceinline__ int swz(int r, int q, int nq) { return q ^ (r & (min(nq, 16) - 1)); }
 
 template <int D, int NT>
-__global__ __launch_bounds__(kThreads) void sp_main(SparseArgs a, SparseWs w) {
-    constexpr int BSP = 16 * NT;     // padded keys per block
-    constexpr int KD = D / 4;        // dims per lane group in the QK^T contraction
-    constexpr int NDT = D / 16;      // 16-dim output tiles
-    constexpr int KQ = D / 4;        // float4 chunks per K row
-    constexpr int VQ = BSP / 4;      // float4 chunks per V^T row
-    extern __shared__ float lds[];
-    float *Ks = lds;                 // [BSP][D], swizzled chunks
-    float *Vt = lds + BSP * D;       // [D][BSP], swizzled chunks
+__global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 2 : 1) void sp_main(SparseArgs a, SparseWs w) {
+    constexpr int BSP = 16 * NT;             // padded keys per block (NT even)
+    constexpr int KB = D / 32;               // 32-dim k-blocks of QK^T
+    constexpr int NDT = D / 16;              // 16-dim output tiles
+    constexpr int KK = NT / 2;               // 32-key k-blocks of PV
+    constexpr int KQ = D / 8;                // 16-byte chunks per K row (8 halfs)
+    constexpr int VC = BSP / 4;              // 8-byte chunks per V^T row (4 halfs)
+    extern __shared__ half_t lds[];
+    half_t *Khi = lds, *Klo = lds + BSP * D;
+    half_t *Vhi = lds + 2 * BSP * D, *Vlo = lds + 3 * BSP * D;
+    __shared__ float s_max[2][kThreads / 64];
 
     const int item = blockIdx.x;
     if (item >= w.nitems[0]) return;
@@ -153,47 +179,109 @@ __global__ __launch_bounds__(kThreads) void sp_main(SparseArgs a, SparseWs w) {
     const int h = bh % a.hkv;
     const int b = bh / a.hkv;
     const int32_t *btrow = a.bt + (long long)b * a.max_pages;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-    // Stage the key block: K row-major, V transposed; zeros for unmapped or missing keys.
-    for (int idx = threadIdx.x; idx < BSP * KQ; idx += kThreads) {
-        const int t = idx / KQ, q = idx - t * KQ;
+    auto page_of = [&](int t) {
         const int slot = blk * a.ppb + t / a.page_size;
         int pid = -1;
         if (t < a.block_size && slot < a.max_pages) pid = btrow[slot];
-        float4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-        if (pid >= 0 && pid < a.num_pages) {
-            const long long row =
-                (((long long)pid * a.hkv + h) * a.page_size + t % a.page_size) * D + 4 * q;
-            kv = *(const float4_t *)(a.kp + row);
-            vv = *(const float4_t *)(a.vp + row);
+        return (pid >= 0 && pid < a.num_pages) ? pid : -1;
+    };
+    auto row_ptr = [&](const float *base, int pid, int t) {
+        return base + (((long long)pid * a.hkv + h) * a.page_size + t % a.page_size) * D;
+    };
+
+    // ---- stage the key block. A task is 4 consecutive keys x 8 dims of K and of V (32 + 32
+    // floats). Pass 1 loads and takes the block-wide max |K| and |V|; pass 2 scales by the
+    // powers of two, splits into fp16 hi/lo and stores K row-major and V transposed. With one
+    // task per thread the pass-1 registers are reused; otherwise pass 2 reloads (from L2).
+    constexpr int TASKS = BSP / 4 * KQ;                       // (key quad, 8-dim chunk) pairs
+    constexpr int TPT = (TASKS + kThreads - 1) / kThreads;    // tasks per thread
+    float kr[4][8], vr[4][8];
+    auto load_task = [&](int task) {
+        const int t4 = task / KQ, q = task - t4 * KQ;
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * t4 + r;
+            const int pid = page_of(t);
+            for (int x = 0; x < 8; ++x) { kr[r][x] = 0.f; vr[r][x] = 0.f; }
+            if (pid >= 0) {
+                const float *pk = row_ptr(a.kp, pid, t) + 8 * q;
+                const float *pv = row_ptr(a.vp, pid, t) + 8 * q;
+                const float4_t k0 = gload<float4_t>(pk), k1 = gload<float4_t>(pk + 4);
+                const float4_t v0 = gload<float4_t>(pv), v1 = gload<float4_t>(pv + 4);
+                for (int x = 0; x < 4; ++x) {
+                    kr[r][x] = k0[x]; kr[r][4 + x] = k1[x];
+                    vr[r][x] = v0[x]; vr[r][4 + x] = v1[x];
+                }
+            }
         }
-        *(float4_t *)(Ks + t * D + 4 * swz(t, q, KQ)) = kv;
-        for (int k = 0; k < 4; ++k) {
-            const int r = 4 * q + k;
-            Vt[r * BSP + 4 * swz(r, t >> 2, VQ) + (t & 3)] = vv[k];
+    };
+    float mk = 0.f, mv = 0.f;
+    for (int k = 0; k < TPT; ++k) {
+        const int task = threadIdx.x + k * kThreads;
+        if (task >= TASKS) break;
+        load_task(task);
+        for (int r = 0; r < 4; ++r)
+            for (int x = 0; x < 8; ++x) {
+                mk = fmaxf(mk, fabsf(kr[r][x]));
+                mv = fmaxf(mv, fabsf(vr[r][x]));
+            }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        mk = fmaxf(mk, __shfl_xor(mk, o, 64));
+        mv = fmaxf(mv, __shfl_xor(mv, o, 64));
+    }
+    if (lane == 0) { s_max[0][wave] = mk; s_max[1][wave] = mv; }
+    __syncthreads();
+    for (int i = 0; i < kThreads / 64; ++i) {
+        mk = fmaxf(mk, s_max[0][i]);
+        mv = fmaxf(mv, s_max[1][i]);
+    }
+    const int eK = pow2_exp(mk), eV = pow2_exp(mv);
+    for (int k = 0; k < TPT; ++k) {
+        const int task = threadIdx.x + k * kThreads;
+        if (task >= TASKS) break;
+        if (TPT > 1) load_task(task);
+        const int t4 = task / KQ, q = task - t4 * KQ;
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * t4 + r;
+            half8_t hi, lo;
+            for (int x = 0; x < 8; ++x) {
+                const HiLo v = split16(ldexpf(kr[r][x], -eK));
+                hi[x] = v.hi;
+                lo[x] = v.lo;
+            }
+            const int off = t * D + 8 * swz(t, q, KQ);
+            *(half8_t *)(Khi + off) = hi;
+            *(half8_t *)(Klo + off) = lo;
+        }
+        for (int x = 0; x < 8; ++x) {
+            const int d = 8 * q + x;
+            half4_t hi, lo;
+            for (int r = 0; r < 4; ++r) {
+                const HiLo v = split16(ldexpf(vr[r][x], -eV));
+                hi[r] = v.hi;
+                lo[r] = v.lo;
+            }
+            const int off = d * BSP + 4 * swz(d, t4, VC);
+            *(half4_t *)(Vhi + off) = hi;
+            *(half4_t *)(Vlo + off) = lo;
         }
     }
-    __syncthreads();
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g16 = lane >> 4, n16 = lane & 15;
-    // Mapped-key masks (wave-uniform): bit t set when key t sits on a mapped page.
+    // mapped-key masks (wave-uniform): bit t set when key t sits on a mapped page
     uint64_t mmask[(BSP + 63) / 64];
     for (int hw = 0; hw < (BSP + 63) / 64; ++hw) {
         const int t = 64 * hw + lane;
-        const int slot = blk * a.ppb + t / a.page_size;
-        bool ok = false;
-        if (t < a.block_size && t < BSP && slot < a.max_pages) {
-            const int pid = btrow[slot];
-            ok = pid >= 0 && pid < a.num_pages;
-        }
-        mmask[hw] = __ballot(ok);
+        mmask[hw] = __ballot(t < BSP && page_of(t) >= 0);
     }
-    const int epg = 16 / a.qhead;          // edges per 16-row group
+    __syncthreads();
+
+    // ---- edge groups: 16 query rows (16 / qhead edges) per wave at a time.
+    const int g16 = lane >> 4, n16 = lane & 15;
+    const int epg = 16 / a.qhead;
     const int rows = epg * a.qhead;
     const int hq = a.hkv * a.qhead;
     for (int grp = wave; grp * epg < nE; grp += kThreads / 64) {
-        // Row n16 of this group: edge el = n16 / qhead, lane qh = n16 % qhead.
         const int el = n16 / a.qhead, qh = n16 - el * a.qhead;
         const int idx = grp * epg + el;
         const bool vrow = n16 < rows && idx < nE;
@@ -203,61 +291,93 @@ __global__ __launch_bounds__(kThreads) void sp_main(SparseArgs a, SparseWs w) {
             qi = a.edge_meta[5LL * e];
             len = min(a.edge_meta[5LL * e + 4], a.block_size);
         }
-        float qf[KD];
+        // query row n16, dims 32kb + 8g16 .. +7: scale by the row's power of two, split
+        float qf[KB][8];
+        float mq = 0.f;
+        for (int kb = 0; kb < KB; ++kb)
+            for (int x = 0; x < 8; ++x) qf[kb][x] = 0.f;
         if (vrow) {
-            const float *qp = a.q + ((long long)qi * hq + h * a.qhead + qh) * D + KD * g16;
-            for (int k = 0; k < KD; k += 4) {
-                const float4_t x = *(const float4_t *)(qp + k);
-                qf[k] = x[0]; qf[k + 1] = x[1]; qf[k + 2] = x[2]; qf[k + 3] = x[3];
+            const float *qp = a.q + ((long long)qi * hq + h * a.qhead + qh) * D + 8 * g16;
+            for (int kb = 0; kb < KB; ++kb) {
+                const float4_t x0 = gload<float4_t>(qp + 32 * kb);
+                const float4_t x1 = gload<float4_t>(qp + 32 * kb + 4);
+                for (int x = 0; x < 4; ++x) { qf[kb][x] = x0[x]; qf[kb][4 + x] = x1[x]; }
             }
-        } else {
-            for (int k = 0; k < KD; ++k) qf[k] = 0.f;
         }
-        // S^T tiles: lane holds keys 16j + 4g16 + i of row n16.
+        for (int kb = 0; kb < KB; ++kb)
+            for (int x = 0; x < 8; ++x) mq = fmaxf(mq, fabsf(qf[kb][x]));
+        mq = wave_max_xor(mq, 16);
+        mq = wave_max_xor(mq, 32);
+        const int eQ = pow2_exp(mq);
+        half8_t qhi[KB], qlo[KB];
+        for (int kb = 0; kb < KB; ++kb)
+            for (int x = 0; x < 8; ++x) {
+                const HiLo v = split16(ldexpf(qf[kb][x], -eQ));
+                qhi[kb][x] = v.hi;
+                qlo[kb][x] = v.lo;
+            }
+        const float mult = ldexpf(a.scale_log2, eK + eQ);
+
+        // S^T tiles: lane holds keys 16j + 4g16 + i of row n16 (log2 units).
         float s[NT][4];
         float mx = -INFINITY;
         for (int j = 0; j < NT; ++j) {
             float4_t acc = {0.f, 0.f, 0.f, 0.f};
             const int t = 16 * j + n16;
-            for (int k = 0; k < KD; k += 4) {
-                const float4_t kk = *(const float4_t *)(Ks + t * D + 4 * swz(t, (KD * g16 + k) >> 2, KQ));
-                acc = mfma16x16x4f32(kk[0], qf[k], acc);
-                acc = mfma16x16x4f32(kk[1], qf[k + 1], acc);
-                acc = mfma16x16x4f32(kk[2], qf[k + 2], acc);
-                acc = mfma16x16x4f32(kk[3], qf[k + 3], acc);
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = t * D + 8 * swz(t, 4 * kb + g16, KQ);
+                const half8_t khi = *(const half8_t *)(Khi + off);
+                const half8_t klo = *(const half8_t *)(Klo + off);
+                acc = mfma16x16x32(khi, qlo[kb], acc);
+                acc = mfma16x16x32(klo, qhi[kb], acc);
+                acc = mfma16x16x32(khi, qhi[kb], acc);
             }
             for (int i = 0; i < 4; ++i) {
                 const int key = 16 * j + 4 * g16 + i;
                 const bool ok = key < len && ((mmask[key >> 6] >> (key & 63)) & 1);
-                s[j][i] = ok ? acc[i] * a.scale_log2 : -INFINITY;
+                s[j][i] = ok ? acc[i] * mult : -INFINITY;
                 mx = fmaxf(mx, s[j][i]);
             }
+            // keep the next tile's LDS operand reads from being hoisted over this tile (each
+            // hoisted read holds 4 registers)
+            __builtin_amdgcn_sched_barrier(0);
         }
         mx = wave_max_xor(mx, 16);
         mx = wave_max_xor(mx, 32);
         const float mu = (mx == -INFINITY) ? 0.f : mx;
         float ls = 0.f;
+        half8_t phi[KK], plo[KK];
         for (int j = 0; j < NT; ++j)
             for (int i = 0; i < 4; ++i) {
-                s[j][i] = __builtin_amdgcn_exp2f(s[j][i] - mu);
-                ls += s[j][i];
+                // a NaN score counts as excluded, as the page's "score > NEG_LARGE/2" test does
+                const float pv = (s[j][i] > -INFINITY) ? __builtin_amdgcn_exp2f(s[j][i] - mu) : 0.f;
+                ls += pv;
+                const HiLo v = split16(pv);
+                phi[j >> 1][4 * (j & 1) + i] = v.hi;
+                plo[j >> 1][4 * (j & 1) + i] = v.lo;
             }
         ls += __shfl_xor(ls, 16, 64);
         ls += __shfl_xor(ls, 32, 64);
-        // O = P . V: rows 4g16 + i, dims 16dt + n16.
+
+        // O = P . V: rows 4g16 + i, dims 16dt + n16; k-slot (g16, 4u + i) is key 32kk + 16u + 4g16 + i.
         float4_t o[NDT];
         for (int dt = 0; dt < NDT; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < NT; ++j) {
+        for (int kk = 0; kk < KK; ++kk) {
             for (int dt = 0; dt < NDT; ++dt) {
                 const int r = 16 * dt + n16;
-                const float4_t vv = *(const float4_t *)(Vt + r * BSP + 4 * swz(r, 4 * j + g16, VQ));
-                o[dt] = mfma16x16x4f32(s[j][0], vv[0], o[dt]);
-                o[dt] = mfma16x16x4f32(s[j][1], vv[1], o[dt]);
-                o[dt] = mfma16x16x4f32(s[j][2], vv[2], o[dt]);
-                o[dt] = mfma16x16x4f32(s[j][3], vv[3], o[dt]);
+                const int o0 = r * BSP + 4 * swz(r, 8 * kk + g16, VC);
+                const int o1 = r * BSP + 4 * swz(r, 8 * kk + 4 + g16, VC);
+                const half4_t h0 = *(const half4_t *)(Vhi + o0), h1 = *(const half4_t *)(Vhi + o1);
+                const half4_t l0 = *(const half4_t *)(Vlo + o0), l1 = *(const half4_t *)(Vlo + o1);
+                const half8_t vhi = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+                const half8_t vlo = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+                o[dt] = mfma16x16x32(phi[kk], vlo, o[dt]);
+                o[dt] = mfma16x16x32(plo[kk], vhi, o[dt]);
+                o[dt] = mfma16x16x32(phi[kk], vhi, o[dt]);
+                if (dt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // Stores.
+        // Stores: o scaled back by 2^eV; m and l of row n16 from lanes g16 == 0.
         if (vrow && g16 == 0) {
             const long long p = (long long)e * a.qhead + qh;
             a.m[p] = (mx == -INFINITY) ? kNegLarge : mx * kLn2;
@@ -268,7 +388,8 @@ __global__ __launch_bounds__(kThreads) void sp_main(SparseArgs a, SparseWs w) {
             const int er = __shfl(e, r, 64);
             if (r >= rows || er < 0) continue;
             const long long p = (long long)er * a.qhead + (r - (r / a.qhead) * a.qhead);
-            for (int dt = 0; dt < NDT; ++dt) a.o[p * D + 16 * dt + n16] = o[dt][i];
+            for (int dt = 0; dt < NDT; ++dt)
+                a.o[p * D + 16 * dt + n16] = ldexpf(o[dt][i], eV);
         }
     }
 }
@@ -286,37 +407,32 @@ size_t sparse_lds_limit() {
 
 size_t sparse_workspace_bytes(int E, int units) {
     const size_t max_items = (size_t)(E + kChunk - 1) / kChunk + units;
-    size_t words = al(units) * 2 + al(units + 1) * 2 + al(1) + al(max_items) + al(E);
+    size_t words = al(units) + al(E) + al(units + 1) * 2 + al(1) + al(max_items) + al(E);
     return words * 4;
 }
 
 pa_status launch_sparse(const SparseArgs &a, hipStream_t stream) {
-    LaunchScope scope("sparse_forward", stream);
-    SparseWs w = carve(a.ws, a.E, a.units);
-    const int nz = (int)(w.offs - w.counts);  // counts and cursor are contiguous
-    hipLaunchKernelGGL(sp_zero, dim3((nz + 255) / 256), dim3(256), 0, stream, w.counts, nz);
-    const int eg = (a.E + 255) / 256;
-    hipLaunchKernelGGL(sp_hist, dim3(eg), dim3(256), 0, stream, a, w);
-    hipLaunchKernelGGL(sp_scan, dim3(1), dim3(1024), 0, stream, a, w);
-    hipLaunchKernelGGL(sp_scatter, dim3(eg), dim3(256), 0, stream, a, w);
-    int nt = 1;
+    int nt = 2;
     while (16 * nt < a.block_size) nt *= 2;
-    const size_t lds = (size_t)2 * 16 * nt * a.D * sizeof(float);
-    if (lds > sparse_lds_limit()) return PA_ERR_UNSUPPORTED;
-#define PA_SP_LAUNCH(DD, NN)                                                                 \
-    hipLaunchKernelGGL((sp_main<DD, NN>), dim3(w.max_items), dim3(kThreads), lds, stream, a, w)
+    const size_t lds = (size_t)4 * 16 * nt * a.D * sizeof(half_t);
+    if (lds > sparse_lds_limit() || (a.D != 64 && a.D != 128)) return PA_ERR_UNSUPPORTED;
+    LaunchScope scope("sparse_forward", stream, 5);
+    SparseWs w = carve(a.ws, a.E, a.units);
+    scope.launch(sp_zero, dim3((a.units + 255) / 256), dim3(256), 0, w.counts, a.units);
+    const int eg = (a.E + 255) / 256;
+    scope.launch(sp_hist, dim3(eg), dim3(256), 0, a, w);
+    scope.launch(sp_scan, dim3(1), dim3(1024), 0, a, w);
+    scope.launch(sp_scatter, dim3(eg), dim3(256), 0, a, w);
+#define PA_SP_LAUNCH(DD, NN) \
+    scope.launch(sp_main<DD, NN>, dim3(w.max_items), dim3(kThreads), (uint32_t)lds, a, w)
     if (a.D == 128) {
-        if (nt == 1) PA_SP_LAUNCH(128, 1);
-        else if (nt == 2) PA_SP_LAUNCH(128, 2);
+        if (nt == 2) PA_SP_LAUNCH(128, 2);
         else if (nt == 4) PA_SP_LAUNCH(128, 4);
         else PA_SP_LAUNCH(128, 8);
-    } else if (a.D == 64) {
-        if (nt == 1) PA_SP_LAUNCH(64, 1);
-        else if (nt == 2) PA_SP_LAUNCH(64, 2);
+    } else {
+        if (nt == 2) PA_SP_LAUNCH(64, 2);
         else if (nt == 4) PA_SP_LAUNCH(64, 4);
         else PA_SP_LAUNCH(64, 8);
-    } else {
-        return PA_ERR_UNSUPPORTED;
     }
 #undef PA_SP_LAUNCH
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
