@@ -461,7 +461,9 @@ static int sparse_units(const pa_sparse_shape *s) {
 
 size_t pa_sparse_forward_workspace_size(const pa_sparse_shape *shape) {
     if (check_sparse(shape) != PA_OK) return 0;
-    return sparse_workspace_bytes(shape->num_edges, sparse_units(shape));
+    return sparse_workspace_bytes(shape->num_edges, sparse_units(shape),
+                                  (long long)shape->tq * shape->hkv * shape->qhead,
+                                  shape->head_dim);
 }
 
 pa_status pa_sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
@@ -479,7 +481,8 @@ pa_status pa_sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
         !m_partial || !l_partial || !workspace)
         return PA_ERR_NULL;
     const int units = sparse_units(shape);
-    if (workspace_bytes < sparse_workspace_bytes(s.num_edges, units) ||
+    if (workspace_bytes < sparse_workspace_bytes(s.num_edges, units,
+                                                 (long long)s.tq * s.hkv * s.qhead, s.head_dim) ||
         ((uintptr_t)workspace % 256) != 0)
         return PA_ERR_WORKSPACE;
     SparseArgs a;

@@ -557,6 +557,7 @@ __global__ __launch_bounds__(NCB == 1 ? 512 : 64) void attn_kernel(AttnArgs a) {
     }
     __shared__ int s_unit;
     const int n_work = a.n_items[0] * gblocks;
+    if (n_work == 0) return;  // e.g. no prefill rows: leave before touching the counter
     for (;;) {
         if (threadIdx.x == 0) s_unit = atomicAdd(a.counter, 1);
         __syncthreads();

@@ -180,7 +180,7 @@ struct SparseArgs {
     float scale_log2;
 };
 pa_status launch_sparse(const SparseArgs &a, hipStream_t stream);
-size_t sparse_workspace_bytes(int E, int units);
+size_t sparse_workspace_bytes(int E, int units, long long qrows, int D);
 
 // ---------------------------------------------------------------------------------------------
 // Device helpers.

@@ -19,8 +19,12 @@
 //    is folded back into the scores and the output.
 //  * S^T = K . Q^T has 16 keys as rows and 16 query rows as columns; its accumulator gives each
 //    lane 8 keys of one row across two key tiles, exactly the k-slots of the P operand of
-//    O = P . V, so P never leaves registers. K (row-major) and V (transposed) live in LDS as
-//    fp16 hi/lo planes with XOR-swizzled chunks.
+//    O^T = V^T . P^T, so P never leaves registers, and O^T gives each lane four consecutive
+//    dims of one query row for its stores. K (row-major) and V (transposed, keys ordered so
+//    that one 16-byte read is one operand) live in LDS as fp16 hi/lo planes with XOR-swizzled
+//    chunks.
+//  * The query rows are scaled and split once, in a pass of their own, into workspace planes;
+//    an edge reads its rows ready for the MFMA, and the item's edge list sits in LDS.
 //
 // Edges whose batch, head, block or query index lie outside the shapes write the sentinel.
 #include "common.h"
@@ -28,28 +32,41 @@
 namespace pa {
 namespace {
 
-constexpr int kChunk = 64;     // edges per work item
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kChunk = 128;    // edges per work item
+constexpr int kThreads = 512;  // 8 waves
 
 struct SparseWs {
     int32_t *counts, *rank, *offs, *ioffs, *nitems, *item_unit, *perm;
+    float *qmul;        // per query row: scale_log2 * 2^eQ
+    half_t *qhi, *qlo;  // query rows times 2^-eQ, split into fp16 planes [tq * hq, D]
     int max_items;
 };
 
 size_t al(size_t x) { return (x + 63) / 64 * 64; }  // in int32 words (256 bytes)
 
-SparseWs carve(int32_t *ws, int E, int units) {
-    SparseWs w;
-    w.max_items = (E + kChunk - 1) / kChunk + units;
-    size_t off = 0;
-    w.counts = ws + off; off = al(off + units);
-    w.rank = ws + off; off = al(off + E);
-    w.offs = ws + off; off = al(off + units + 1);
-    w.ioffs = ws + off; off = al(off + units + 1);
-    w.nitems = ws + off; off = al(off + 1);
-    w.item_unit = ws + off; off = al(off + w.max_items);
-    w.perm = ws + off; off = al(off + E);
-    return w;
+// Workspace layout in int32 words; returns the total.
+size_t layout(SparseWs *w, int32_t *ws, int E, int units, long long qrows, int D) {
+    const size_t max_items = (size_t)(E + kChunk - 1) / kChunk + units;
+    size_t off = 0, o[10];
+    o[0] = off; off = al(off + units);             // counts
+    o[1] = off; off = al(off + E);                 // rank
+    o[2] = off; off = al(off + units + 1);         // offs
+    o[3] = off; off = al(off + units + 1);         // ioffs
+    o[4] = off; off = al(off + 1);                 // nitems
+    o[5] = off; off = al(off + max_items);         // item_unit
+    o[6] = off; off = al(off + E);                 // perm
+    o[7] = off; off = al(off + qrows);             // qmul
+    o[8] = off; off = al(off + qrows * D / 2);     // qhi
+    o[9] = off; off = al(off + qrows * D / 2);     // qlo
+    if (w) {
+        w->counts = ws + o[0]; w->rank = ws + o[1]; w->offs = ws + o[2]; w->ioffs = ws + o[3];
+        w->nitems = ws + o[4]; w->item_unit = ws + o[5]; w->perm = ws + o[6];
+        w->qmul = (float *)(ws + o[7]);
+        w->qhi = (half_t *)(ws + o[8]);
+        w->qlo = (half_t *)(ws + o[9]);
+        w->max_items = (int)max_items;
+    }
+    return off;
 }
 
 __device__ __forceinline__ bool decode_edge(const SparseArgs &a, int e, int &q, int &h, int &blk,
@@ -155,18 +172,49 @@ __device__ __forceinline__ int pow2_exp(float mx) {
 // group reads at one logical chunk land in distinct banks.
 __device__ __forceinline__ int swz(int r, int q, int nq) { return q ^ (r & (min(nq, 16) - 1)); }
 
+// One query row per D/8 lanes: the row times the power of two that brings its largest magnitude
+// into [0.5, 1), split into the fp16 hi/lo planes, and scale_log2 * 2^eQ for its scores.
+template <int D>
+__global__ __launch_bounds__(256) void sp_qsplit(SparseArgs a, SparseWs w, long long rows) {
+    constexpr int LPR = D / 8;  // lanes per row (divides 64, so a row stays inside one wave)
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long row = gid / LPR;
+    const int c = (int)(gid - row * LPR);
+    const long long r = row < rows ? row : rows - 1;
+    const float *src = a.q + r * D + 8 * c;
+    const float4_t x0 = gload<float4_t>(src), x1 = gload<float4_t>(src + 4);
+    float mx = 0.f;
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(fabsf(x0[i]), fabsf(x1[i])));
+    for (int o = LPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    const int e = pow2_exp(mx);
+    half8_t hi, lo;
+    for (int i = 0; i < 4; ++i) {
+        const HiLo u = split16(ldexpf(x0[i], -e)), v = split16(ldexpf(x1[i], -e));
+        hi[i] = u.hi; lo[i] = u.lo;
+        hi[4 + i] = v.hi; lo[4 + i] = v.lo;
+    }
+    if (row >= rows) return;
+    *(half8_t *)(w.qhi + r * D + 8 * c) = hi;
+    *(half8_t *)(w.qlo + r * D + 8 * c) = lo;
+    if (c == 0) w.qmul[r] = ldexpf(a.scale_log2, e);
+}
+
 template <int D, int NT>
-__global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 2 : 1) void sp_main(SparseArgs a, SparseWs w) {
+__global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(SparseArgs a, SparseWs w) {
     constexpr int BSP = 16 * NT;             // padded keys per block (NT even)
     constexpr int KB = D / 32;               // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;              // 16-dim output tiles
     constexpr int KK = NT / 2;               // 32-key k-blocks of PV
     constexpr int KQ = D / 8;                // 16-byte chunks per K row (8 halfs)
-    constexpr int VC = BSP / 4;              // 8-byte chunks per V^T row (4 halfs)
+    constexpr int VC = BSP / 8;              // 16-byte chunks per V^T row (8 halfs)
+    constexpr int NW = kThreads / 64;        // waves
+    constexpr int MW = (BSP + 63) / 64;      // 64-bit key-mask words
+    static_assert(kChunk <= kThreads, "one thread per staged edge");
     extern __shared__ half_t lds[];
     half_t *Khi = lds, *Klo = lds + BSP * D;
     half_t *Vhi = lds + 2 * BSP * D, *Vlo = lds + 3 * BSP * D;
-    __shared__ float s_max[2][kThreads / 64];
+    __shared__ float s_max[2][NW];                      // per-wave maxima of |K| and |V|
+    __shared__ int s_e[kChunk], s_q[kChunk], s_len[kChunk];  // the item's edges
 
     const int item = blockIdx.x;
     if (item >= w.nitems[0]) return;
@@ -180,6 +228,14 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 2 : 1) void sp_main(Spa
     const int b = bh / a.hkv;
     const int32_t *btrow = a.bt + (long long)b * a.max_pages;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    // the item's edges: id, query index and clamped length
+    if ((int)threadIdx.x < nE) {
+        const int e = w.perm[ebeg + threadIdx.x];
+        s_e[threadIdx.x] = e;
+        s_q[threadIdx.x] = a.edge_meta[5LL * e];
+        s_len[threadIdx.x] = min(a.edge_meta[5LL * e + 4], a.block_size);
+    }
 
     auto page_of = [&](int t) {
         const int slot = blk * a.ppb + t / a.page_size;
@@ -233,7 +289,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 2 : 1) void sp_main(Spa
     }
     if (lane == 0) { s_max[0][wave] = mk; s_max[1][wave] = mv; }
     __syncthreads();
-    for (int i = 0; i < kThreads / 64; ++i) {
+    for (int i = 0; i < NW; ++i) {
         mk = fmaxf(mk, s_max[0][i]);
         mv = fmaxf(mv, s_max[1][i]);
     }
@@ -255,6 +311,9 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 2 : 1) void sp_main(Spa
             *(half8_t *)(Khi + off) = hi;
             *(half8_t *)(Klo + off) = lo;
         }
+        // V^T row d holds, in 16-byte chunk 4c + g of a 32-key block c, the keys
+        // 32c + 4g .. +3 and 32c + 16 + 4g .. +3: the k-slots (g, 0..7) of one PV operand.
+        const int vq = 4 * (t4 >> 3) + (t4 & 3), vh = 4 * ((t4 >> 2) & 1);
         for (int x = 0; x < 8; ++x) {
             const int d = 8 * q + x;
             half4_t hi, lo;
@@ -263,60 +322,46 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 2 : 1) void sp_main(Spa
                 hi[r] = v.hi;
                 lo[r] = v.lo;
             }
-            const int off = d * BSP + 4 * swz(d, t4, VC);
+            const int off = d * BSP + 8 * swz(d, vq, VC) + vh;
             *(half4_t *)(Vhi + off) = hi;
             *(half4_t *)(Vlo + off) = lo;
         }
     }
     // mapped-key masks (wave-uniform): bit t set when key t sits on a mapped page
-    uint64_t mmask[(BSP + 63) / 64];
-    for (int hw = 0; hw < (BSP + 63) / 64; ++hw) {
+    uint64_t mmask[MW];
+    for (int hw = 0; hw < MW; ++hw) {
         const int t = 64 * hw + lane;
         mmask[hw] = __ballot(t < BSP && page_of(t) >= 0);
     }
     __syncthreads();
 
-    // ---- edge groups: 16 query rows (16 / qhead edges) per wave at a time.
+    // ---- edge groups: 16 query rows (16 / qhead edges) per wave at a time. Lane (g16, n16)
+    // serves query row n16 throughout.
     const int g16 = lane >> 4, n16 = lane & 15;
     const int epg = 16 / a.qhead;
     const int rows = epg * a.qhead;
     const int hq = a.hkv * a.qhead;
-    for (int grp = wave; grp * epg < nE; grp += kThreads / 64) {
-        const int el = n16 / a.qhead, qh = n16 - el * a.qhead;
+    const int el = n16 / a.qhead, qh = n16 - el * a.qhead;
+    for (int grp = wave; grp * epg < nE; grp += NW) {
         const int idx = grp * epg + el;
         const bool vrow = n16 < rows && idx < nE;
-        int e = -1, len = 0, qi = 0;
-        if (vrow) {
-            e = w.perm[ebeg + idx];
-            qi = a.edge_meta[5LL * e];
-            len = min(a.edge_meta[5LL * e + 4], a.block_size);
-        }
-        // query row n16, dims 32kb + 8g16 .. +7: scale by the row's power of two, split
-        float qf[KB][8];
-        float mq = 0.f;
-        for (int kb = 0; kb < KB; ++kb)
-            for (int x = 0; x < 8; ++x) qf[kb][x] = 0.f;
-        if (vrow) {
-            const float *qp = a.q + ((long long)qi * hq + h * a.qhead + qh) * D + 8 * g16;
-            for (int kb = 0; kb < KB; ++kb) {
-                const float4_t x0 = gload<float4_t>(qp + 32 * kb);
-                const float4_t x1 = gload<float4_t>(qp + 32 * kb + 4);
-                for (int x = 0; x < 4; ++x) { qf[kb][x] = x0[x]; qf[kb][4 + x] = x1[x]; }
-            }
-        }
-        for (int kb = 0; kb < KB; ++kb)
-            for (int x = 0; x < 8; ++x) mq = fmaxf(mq, fabsf(qf[kb][x]));
-        mq = wave_max_xor(mq, 16);
-        mq = wave_max_xor(mq, 32);
-        const int eQ = pow2_exp(mq);
+        const int ix = vrow ? idx : 0;  // rows without an edge read edge 0's query, then drop it
+        const int e = s_e[ix];
+        const int len = vrow ? s_len[ix] : 0;
+        const long long qrow = (long long)s_q[ix] * hq + h * a.qhead + qh;
         half8_t qhi[KB], qlo[KB];
-        for (int kb = 0; kb < KB; ++kb)
-            for (int x = 0; x < 8; ++x) {
-                const HiLo v = split16(ldexpf(qf[kb][x], -eQ));
-                qhi[kb][x] = v.hi;
-                qlo[kb][x] = v.lo;
-            }
-        const float mult = ldexpf(a.scale_log2, eK + eQ);
+        for (int kb = 0; kb < KB; ++kb) {
+            qhi[kb] = gload<half8_t>(w.qhi + qrow * D + 32 * kb + 8 * g16);
+            qlo[kb] = gload<half8_t>(w.qlo + qrow * D + 32 * kb + 8 * g16);
+        }
+        const float mult = ldexpf(gload<float>(w.qmul + qrow), eK);
+        // keys this lane scores (16j + 4g16 + i) that are mapped and below the edge's length
+        uint64_t lm[MW];
+        for (int hw = 0; hw < MW; ++hw) {
+            const int rem = len - 64 * hw;
+            const uint64_t lenm = rem >= 64 ? ~0ull : (rem <= 0 ? 0ull : (1ull << rem) - 1);
+            lm[hw] = (mmask[hw] & lenm) >> (4 * g16);
+        }
 
         // S^T tiles: lane holds keys 16j + 4g16 + i of row n16 (log2 units).
         float s[NT][4];
@@ -333,8 +378,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 2 : 1) void sp_main(Spa
                 acc = mfma16x16x32(khi, qhi[kb], acc);
             }
             for (int i = 0; i < 4; ++i) {
-                const int key = 16 * j + 4 * g16 + i;
-                const bool ok = key < len && ((mmask[key >> 6] >> (key & 63)) & 1);
+                const bool ok = (lm[j >> 2] >> (16 * (j & 3) + i)) & 1;
                 s[j][i] = ok ? acc[i] * mult : -INFINITY;
                 mx = fmaxf(mx, s[j][i]);
             }
@@ -359,37 +403,35 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 2 : 1) void sp_main(Spa
         ls += __shfl_xor(ls, 16, 64);
         ls += __shfl_xor(ls, 32, 64);
 
-        // O = P . V: rows 4g16 + i, dims 16dt + n16; k-slot (g16, 4u + i) is key 32kk + 16u + 4g16 + i.
+        // O^T = V^T . P^T: rows are dims 16dt + 4g16 + i, column n16 is the lane's query row;
+        // k-slot (g16, 4u + i) is key 32kk + 16u + 4g16 + i on both operands.
         float4_t o[NDT];
         for (int dt = 0; dt < NDT; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
         for (int kk = 0; kk < KK; ++kk) {
             for (int dt = 0; dt < NDT; ++dt) {
                 const int r = 16 * dt + n16;
-                const int o0 = r * BSP + 4 * swz(r, 8 * kk + g16, VC);
-                const int o1 = r * BSP + 4 * swz(r, 8 * kk + 4 + g16, VC);
-                const half4_t h0 = *(const half4_t *)(Vhi + o0), h1 = *(const half4_t *)(Vhi + o1);
-                const half4_t l0 = *(const half4_t *)(Vlo + o0), l1 = *(const half4_t *)(Vlo + o1);
-                const half8_t vhi = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-                const half8_t vlo = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-                o[dt] = mfma16x16x32(phi[kk], vlo, o[dt]);
-                o[dt] = mfma16x16x32(plo[kk], vhi, o[dt]);
-                o[dt] = mfma16x16x32(phi[kk], vhi, o[dt]);
+                const int off = r * BSP + 8 * swz(r, 4 * kk + g16, VC);
+                const half8_t vhi = *(const half8_t *)(Vhi + off);
+                const half8_t vlo = *(const half8_t *)(Vlo + off);
+                o[dt] = mfma16x16x32(vlo, phi[kk], o[dt]);
+                o[dt] = mfma16x16x32(vhi, plo[kk], o[dt]);
+                o[dt] = mfma16x16x32(vhi, phi[kk], o[dt]);
                 if (dt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // Stores: o scaled back by 2^eV; m and l of row n16 from lanes g16 == 0.
-        if (vrow && g16 == 0) {
+        // Stores: four consecutive dims of o per lane, scaled back by 2^eV; m and l from g16 == 0.
+        if (vrow) {
             const long long p = (long long)e * a.qhead + qh;
-            a.m[p] = (mx == -INFINITY) ? kNegLarge : mx * kLn2;
-            a.l[p] = ls;
-        }
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g16 + i;
-            const int er = __shfl(e, r, 64);
-            if (r >= rows || er < 0) continue;
-            const long long p = (long long)er * a.qhead + (r - (r / a.qhead) * a.qhead);
-            for (int dt = 0; dt < NDT; ++dt)
-                a.o[p * D + 16 * dt + n16] = ldexpf(o[dt][i], eV);
+            float *op = a.o + p * D + 4 * g16;
+            for (int dt = 0; dt < NDT; ++dt) {
+                float4_t v;
+                for (int i = 0; i < 4; ++i) v[i] = ldexpf(o[dt][i], eV);
+                *(float4_t *)(op + 16 * dt) = v;
+            }
+            if (g16 == 0) {
+                a.m[p] = (mx == -INFINITY) ? kNegLarge : mx * kLn2;
+                a.l[p] = ls;
+            }
         }
     }
 }
@@ -405,19 +447,26 @@ size_t sparse_lds_limit() {
     return (size_t)v;
 }
 
-size_t sparse_workspace_bytes(int E, int units) {
-    const size_t max_items = (size_t)(E + kChunk - 1) / kChunk + units;
-    size_t words = al(units) + al(E) + al(units + 1) * 2 + al(1) + al(max_items) + al(E);
-    return words * 4;
+size_t sparse_workspace_bytes(int E, int units, long long qrows, int D) {
+    return layout(nullptr, nullptr, E, units, qrows, D) * 4;
 }
 
 pa_status launch_sparse(const SparseArgs &a, hipStream_t stream) {
     int nt = 2;
     while (16 * nt < a.block_size) nt *= 2;
     const size_t lds = (size_t)4 * 16 * nt * a.D * sizeof(half_t);
-    if (lds > sparse_lds_limit() || (a.D != 64 && a.D != 128)) return PA_ERR_UNSUPPORTED;
-    LaunchScope scope("sparse_forward", stream, 5);
-    SparseWs w = carve(a.ws, a.E, a.units);
+    // dynamic LDS plus the kernel's static arrays (edge list, per-wave maxima)
+    if (lds + 2048 > sparse_lds_limit() || (a.D != 64 && a.D != 128)) return PA_ERR_UNSUPPORTED;
+    const long long qrows = (long long)a.tq * a.hkv * a.qhead;
+    LaunchScope scope("sparse_forward", stream, qrows > 0 ? 6 : 5);
+    SparseWs w;
+    layout(&w, a.ws, a.E, a.units, qrows, a.D);
+    if (qrows > 0) {
+        const long long thr = qrows * (a.D / 8);
+        const unsigned grid = (unsigned)((thr + 255) / 256);
+        if (a.D == 128) scope.launch(sp_qsplit<128>, dim3(grid), dim3(256), 0, a, w, qrows);
+        else scope.launch(sp_qsplit<64>, dim3(grid), dim3(256), 0, a, w, qrows);
+    }
     scope.launch(sp_zero, dim3((a.units + 255) / 256), dim3(256), 0, w.counts, a.units);
     const int eg = (a.E + 255) / 256;
     scope.launch(sp_hist, dim3(eg), dim3(256), 0, a, w);

@@ -30,6 +30,12 @@ TINY = [
     dict(seed=202, qhead=1, hkv=3, block_size=16, page_size=16, unmapped_frac=0.0),
     dict(seed=203, qhead=8, block_size=128, page_size=32, head_dim=64, key_capacity=1024),
     dict(seed=204, qhead=3, block_size=48, page_size=16, key_capacity=480, all_blocks=True),
+    # 128-key blocks at D = 128: the largest LDS footprint
+    dict(seed=205, block_size=128, page_size=16, key_capacity=1024),
+    # many edges per key block: several work items share one block
+    dict(seed=206, Tq=600, hkv=1, qhead=2, key_capacity=256, window=3, p_random=0.5),
+    # one edge per 16-row group
+    dict(seed=207, qhead=16, hkv=1, head_dim=64, block_size=32, page_size=8),
 ]
 
 
