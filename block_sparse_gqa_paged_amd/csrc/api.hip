@@ -92,7 +92,7 @@ constexpr int kWavesPerCu = 8;          // resident decode waves per CU (2 per S
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct PagedPlan {
-    int Q, ncb_dec, ncb_pre, tpi_dec, tpi_pre;
+    int Q, ncb_dec, tpi_dec, tpi_pre;
     int mode, splits, gw, slots;
     int cap_dec, cap_pre, cap_comb, unit_cap;
     size_t off_dec, off_pre, off_comb, off_slot, off_o, off_m, off_l, total;
@@ -126,9 +126,8 @@ bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
     p.gw = 0;  // set below from the decode kernel's column blocks
     p.ncb_dec = p.Q <= 16 ? 1 : (p.Q <= 32 ? 2 : 4);
     p.tpi_dec = 16 * p.ncb_dec / p.Q;
-    p.ncb_pre = std::max(2, p.ncb_dec);
     p.gw = p.ncb_dec == 1 ? std::gcd(G, 8) : 1;
-    p.tpi_pre = 16 * p.ncb_pre / p.Q;
+    p.tpi_pre = std::max(1, kPrefillCols / p.Q);  // one prefill workgroup: 128 (token, head) columns
     if (num_splits == PA_SPLITS_AUTO) {
         p.mode = 0;
         p.splits = 0;
@@ -383,7 +382,7 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
         const long long units = (long long)p.cap_dec * (G / p.gw);
         blocks = (int)std::min(units, (long long)cus * kWavesPerCu / p.gw);
     }
-    if ((st = launch_attention(a, D, p.ncb_dec, blocks, true, "attn_decode", strm)) != PA_OK)
+    if ((st = launch_attention(a, D, p.ncb_dec, blocks, "attn_decode", strm)) != PA_OK)
         return st;
 
     a.items = pl.pre;
@@ -393,9 +392,8 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     a.tpi = p.tpi_pre;
     a.gw = 1;
     const long long pre_units = (long long)p.cap_pre * G;
-    const int pblocks = (int)std::min(pre_units, (long long)cus * 4);
-    if ((st = launch_attention(a, D, p.ncb_pre, pblocks, false, "attn_prefill", strm)) != PA_OK)
-        return st;
+    const int pblocks = (int)std::min(pre_units, (long long)cus * 2);
+    if ((st = launch_prefill(a, D, pblocks, strm)) != PA_OK) return st;
 
     if (p.unit_cap > 0) {
         CombineArgs c;

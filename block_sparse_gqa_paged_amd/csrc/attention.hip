@@ -1,4 +1,5 @@
-// Paged GQA attention for gfx950: the device planner and the MFMA attention kernel.
+// Paged GQA attention for gfx950: the device planner and the MFMA decode kernel (query rows of
+// sequences with few new tokens; longer ones go to the prefill kernel).
 //
 // Operation: the PagedAttention op of the "com.microsoft.PagedAttention ... manifest.json" page
 // (passes "main", "split_attention" and "merge"): every query row attends, per kv head, to the
@@ -6,10 +7,9 @@
 // may be cut into chunks whose (o, m, l) partials a log-sum-exp merge combines.
 //
 // MI355X design (not the page's WebGPU one):
-//  * One wave64 per (work item, kv head). A work item is a sequence's query rows (all of them for
-//    a decode-like sequence, a 64-column tile for a prefill sequence) and a key chunk. The wave
-//    serves every query head of the kv group, so each K/V byte of the chunk is read from HBM
-//    once per work item.
+//  * One wave64 per (work item, kv head). A work item is all query rows of a decode-like sequence
+//    and a key chunk. The wave serves every query head of the kv group, so each K/V byte of the
+//    chunk is read from HBM once per work item.
 //  * QK^T and PV run on MFMA v_mfma_f32_16x16x32_f16. The score tile is S^T = K . Q^T with
 //    16 keys as rows and 16 (token, head) columns: K rows load straight from the cache as the A
 //    operand (16 contiguous bytes per lane), so no LDS is needed. The tile's C layout already
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(NCB == 1 ? 512 : 64) void attn_kernel(AttnArgs a) {
     }
     __shared__ int s_unit;
     const int n_work = a.n_items[0] * gblocks;
-    if (n_work == 0) return;  // e.g. no prefill rows: leave before touching the counter
+    if (n_work == 0) return;  // nothing listed: leave before touching the counter
     for (;;) {
         if (threadIdx.x == 0) s_unit = atomicAdd(a.counter, 1);
         __syncthreads();
@@ -592,15 +592,14 @@ pa_status launch_d(const AttnArgs &a, int ncb, int blocks, LaunchScope &scope) {
 
 }  // namespace
 
-pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, bool streaming,
-                           const char *name, hipStream_t stream) {
+pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, const char *name,
+                           hipStream_t stream) {
     LaunchScope scope(name, stream);
     if (blocks <= 0) return PA_OK;
-    switch (D * 2 + (streaming ? 1 : 0)) {
-        case 128: return launch_d<64, false>(a, ncb, blocks, scope);
-        case 129: return launch_d<64, true>(a, ncb, blocks, scope);
-        case 256: return launch_d<128, false>(a, ncb, blocks, scope);
-        case 257: return launch_d<128, true>(a, ncb, blocks, scope);
+    // decode reads each K/V byte once: non-temporal loads
+    switch (D) {
+        case 64: return launch_d<64, true>(a, ncb, blocks, scope);
+        case 128: return launch_d<128, true>(a, ncb, blocks, scope);
         default: return PA_ERR_UNSUPPORTED;
     }
 }

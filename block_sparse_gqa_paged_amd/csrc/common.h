@@ -145,10 +145,14 @@ struct AttnArgs {
     int tpi;           // tokens per item
     float scale_log2;  // scale * log2(e)
 };
-// ncb: 16-column blocks of (token, head) columns per item (1, 2 or 4); blocks: workgroups of
-// a.gw waves; streaming: non-temporal K/V loads (data read once).
-pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, bool streaming,
-                           const char *name, hipStream_t stream);
+// Decode items. ncb: 16-column blocks of (token, head) columns per item (1, 2 or 4); blocks:
+// workgroups of a.gw waves.
+pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, const char *name,
+                           hipStream_t stream);
+// Prefill items (a.tpi = kPrefillCols / Q tokens each) on four-wave workgroups, one per
+// (item, kv head) taken from the planner's counter.
+constexpr int kPrefillCols = 128;
+pa_status launch_prefill(const AttnArgs &a, int D, int blocks, hipStream_t stream);
 
 struct CombineArgs {
     const float *o;

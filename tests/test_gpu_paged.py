@@ -66,6 +66,35 @@ def test_tiny_family(case, num_splits):
     assert_attention_close(out, ref, f"attention S={num_splits}")
 
 
+# Prefill-kernel cases: items of 128 / Q tokens, 64-key tiles with ragged tails, block sizes
+# that are not powers of two (and not multiples of 4), D 64 and 128, causal and not.
+PREFILL = [
+    dict(seed=120, past=[0, 150], n_new=[70, 129], num_heads=32, kv_num_heads=8,
+         head_size=128, block_size=16),
+    dict(seed=121, past=[77], n_new=[200], num_heads=4, kv_num_heads=4, head_size=64,
+         block_size=12),                                              # Q = 1: 128-token items
+    dict(seed=122, past=[10, 300], n_new=[50, 9], num_heads=6, kv_num_heads=2, head_size=128,
+         block_size=5),                                               # Q = 3, bs = 5
+    dict(seed=123, past=[40, 0], n_new=[5, 3], num_heads=64, kv_num_heads=1, head_size=64,
+         block_size=16),                                              # Q = 64: 2-token items
+    dict(seed=124, past=[100], n_new=[40], num_heads=32, kv_num_heads=2, head_size=128,
+         block_size=32, causal=0),                                    # Q = 16, not causal
+    dict(seed=125, past=[1000, 3], n_new=[300, 1], num_heads=16, kv_num_heads=2,
+         head_size=128, block_size=16, packed=True, rotary_mode=W.ROTARY_NEOX,
+         rotary_dim=64, rotary_positions=1400),                       # Q = 8, packed, rotary
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: str(c["seed"]))
+def test_prefill_family(case):
+    case = dict(case)
+    w = W.paged_workload(case.pop("seed"), table="pool", slack=0.2, name="prefill", **case)
+    kc, vc, ref = _oracle(w)
+    c, out = _run(w)
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_attention_close(out, ref, "prefill")
+
+
 @pytest.mark.parametrize("causal", [0, 1])
 def test_non_causal_and_prefill(causal):
     w = W.paged_workload(110, past=[3, 60, 0], n_new=[33, 1, 17], num_heads=8, kv_num_heads=2,
