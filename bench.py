@@ -204,7 +204,29 @@ def run_extra(args, torch, np, pa, dev, W):
         "prefill_mfma_frac": round(flops / (us.get("attn_prefill", 1e9) * 1e-6) / 1e12
                                    / MFMA_F16_PEAK_TFS, 4),
         "append_GBps": round(app_bytes / (us.get("kv_append", 1e9) * 1e-6) / 1e9, 1),
+        "append_pct_hbm": round(100 * app_bytes / (us.get("kv_append", 1e9) * 1e-6) / 1e9
+                                / HBM_PEAK_GBS, 2),
         "append_bytes": app_bytes,
+    }
+    del c
+    torch.cuda.empty_cache()
+
+    # the append alone at 16x the mixed workload's prefill tokens: its bandwidth regime
+    print("# generating the append stress workload", file=sys.stderr, flush=True)
+    w = W.append_stress()
+    c = dev.PagedCase(w)
+    pa.pa_timing_reset()
+    pa.pa_timing_enable(True)
+    ms, _ = timed(c.append, steps, 2, torch)
+    pa.pa_timing_enable(False)
+    t_app = pa.pa_timing_get("kv_append")
+    pa.pa_timing_reset()
+    us_app = t_app[0] / max(1, t_app[1]) * 1e3
+    app_bytes = w["T"] * w["G"] * w["D"] * 2 * 4 + w["T"] * (w["rotary_dim"] // 2) * 2 * 2
+    out["append_stress"] = {
+        "workload": w["name"], "tokens": w["T"], "append_bytes": app_bytes,
+        "kernel_us": round(us_app, 2), "append_GBps": round(app_bytes / (us_app * 1e-6) / 1e9, 1),
+        "pct_hbm": round(100 * app_bytes / (us_app * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
     }
     del c
     torch.cuda.empty_cache()

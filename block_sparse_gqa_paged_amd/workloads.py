@@ -206,6 +206,13 @@ def mixed_prefill_decode(seed=3, prefill_tokens=512, n_prefill=8, n_decode=56):
                           name=f"mixed_prefill{n_prefill}x{prefill_tokens}_decode{n_decode}")
 
 
+def append_stress(seed=5):
+    """KV-append bandwidth run: the mixed workload's shapes (H=32, G=8, D=128, bs=32, packed
+    QKV, NeoX rotary on all 128 dims) with 16x its prefill tokens (8 sequences x 8192 new tokens
+    on past ~ U[0, 2048]) and no decode rows: T = 65536, about 554 MB moved by the append."""
+    return mixed_prefill_decode(seed, prefill_tokens=8192, n_prefill=8, n_decode=0)
+
+
 # --------------------------------------------------------------------------------------------
 # Block-sparse "edge" workloads (the fp32 KV-outer forward page).
 # --------------------------------------------------------------------------------------------

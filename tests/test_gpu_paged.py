@@ -95,6 +95,18 @@ def test_prefill_family(case):
     assert_attention_close(out, ref, "prefill")
 
 
+def test_append_stress_bit_exact():
+    """The append bandwidth workload (65536 packed rows, NeoX rotary on all dims): both caches
+    bit-identical to the oracle's, every slot."""
+    w = W.append_stress()
+    kc, vc = oracle.kv_append(w)
+    c = dev.PagedCase(w)
+    c.append()
+    torch.cuda.synchronize()
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_bits_equal(c.value_cache, vc, "value_cache")
+
+
 @pytest.mark.parametrize("causal", [0, 1])
 def test_non_causal_and_prefill(causal):
     w = W.paged_workload(110, past=[3, 60, 0], n_new=[33, 1, 17], num_heads=8, kv_num_heads=2,
