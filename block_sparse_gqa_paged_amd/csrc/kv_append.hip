@@ -90,92 +90,161 @@ __device__ __forceinline__ half8_t rotate_chunk(const AppendArgs &a, const half_
     return out;
 }
 
-// cos/sin chunk for dims d0 .. d0+7 at pos (NeoX: 8 columns; interleaved: 4 columns).
+// cos/sin chunk for dims d0 .. d0+7 at pos (NeoX: 8 columns; interleaved: 4 columns). Chunks
+// past the rotary dims load column 0 of the row instead (unused), so the loads are unconditional.
 template <int MODE>
 __device__ __forceinline__ void load_cs(const AppendArgs &a, int d0, int pos, half8_t &cs,
                                         half8_t &sn) {
     const int R = a.rotary_dim, half = R >> 1;
     cs = half8_t{};
     sn = half8_t{};
-    if (d0 >= R) return;
     if (MODE == kNeox || MODE == kNeoxFull) {  // half % 8 == 0: aligned chunk of columns
-        const long long c0 = (long long)pos * half + (d0 < half ? d0 : d0 - half);
+        const int col = d0 >= R ? 0 : (d0 < half ? d0 : d0 - half);
+        const long long c0 = (long long)pos * half + col;
         cs = gload<half8_t>(a.cos + c0);
         sn = gload<half8_t>(a.sin + c0);
     } else if (MODE == kInter) {
-        const long long c0 = (long long)pos * half + (d0 >> 1);
+        const long long c0 = (long long)pos * half + (d0 >= R ? 0 : (d0 >> 1));
         const half4_t c4 = gload<half4_t>(a.cos + c0), s4 = gload<half4_t>(a.sin + c0);
         for (int e = 0; e < 4; ++e) { cs[e] = c4[e]; sn[e] = s4[e]; }
     }
 }
 
+// One (token, kv head) row's two chunks: source data, then its place in the cache.
+struct RowIn {
+    half8_t kA, kB, vA, vB, pA, pB;
+};
+struct RowAt {
+    int pos;
+    int32_t sv;  // slot_mapping entry, or the block id of pos
+    half8_t cA, sA, cB, sB;
+};
+
 template <int MODE>
+__device__ __forceinline__ RowIn load_row(const AppendArgs &a, const half_t *ks,
+                                          const half_t *vs, int dA, int dB) {
+    RowIn r;
+    r.kA = gload<half8_t>(ks + dA);
+    r.kB = gload<half8_t>(ks + dB);
+    r.vA = gload<half8_t>(vs + dA);
+    r.vB = gload<half8_t>(vs + dB);
+    r.pA = r.kB;  // kNeoxFull: the chunks are each other's partners
+    r.pB = r.kA;
+    if (MODE == kNeox) {  // partners of chunks past the rotary dims: chunk 0 (unused)
+        const int R = a.rotary_dim, half = R >> 1;
+        r.pA = gload<half8_t>(ks + (dA >= R ? 0 : (dA < half ? dA + half : dA - half)));
+        r.pB = gload<half8_t>(ks + (dB >= R ? 0 : (dB < half ? dB + half : dB - half)));
+    }
+    return r;
+}
+
+// Sequence b of token i, its first token cu[b] and past_seqlens[b], from the cu / past
+// entries held by the wave's lanes (entry 64 c + lane in cuv[c], pav[c]).
+__device__ __forceinline__ void lane_lookup(const AppendArgs &a, const int (&cuv)[kLaneCu],
+                                            const int (&pav)[kLaneCu], int i, int &b, int &cb,
+                                            int &pb) {
+    const int i0 = __builtin_amdgcn_readfirstlane(i);
+    int cnt = 0;
+    if (__ballot(i != i0) == 0) {
+        // one token per wave: b + 1 = number of entries cu[k] <= i (cu[B] = T > i)
+        for (int c = 0; c < kLaneCu; ++c) cnt += __popcll(__ballot(cuv[c] <= i0));
+    } else {
+        // several tokens in the wave: count entry by entry
+        for (int q = 0; q < kLaneCu; ++q)
+            for (int l = 0; l < 64 && 64 * q + l <= a.B; ++l) cnt += __shfl(cuv[q], l, 64) <= i;
+    }
+    b = min(cnt, a.B) - 1;
+    const int c = b >> 6, l = b & 63;
+    cb = 0;
+    pb = 0;
+    for (int q = 0; q < kLaneCu; ++q) {
+        const int x = __shfl(cuv[q], l, 64), y = __shfl(pav[q], l, 64);
+        if (q == c) { cb = x; pb = y; }
+    }
+}
+
+// Position of the token, then one load of its slot_mapping entry or block id, and its cos/sin.
+template <int MODE>
+__device__ __forceinline__ RowAt locate(const AppendArgs &a, int i, int b, int t, int past,
+                                        int dA, int dB) {
+    RowAt w;
+    w.pos = past + t;
+    const int32_t *sp = a.slot_mapping ? a.slot_mapping + i
+                                       : a.bt + (long long)b * a.MB + w.pos / a.bs;
+    w.sv = *sp;
+    if (MODE != kCopy && MODE != kGeneric) {
+        load_cs<MODE>(a, dA, w.pos, w.cA, w.sA);
+        if (MODE == kNeoxFull) {  // dB = dA + R/2 uses the same columns
+            w.cB = w.cA;
+            w.sB = w.sA;
+        } else {
+            load_cs<MODE>(a, dB, w.pos, w.cB, w.sB);
+        }
+    }
+    return w;
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_row(const AppendArgs &a, const half_t *ks, const RowIn &r,
+                                          const RowAt &w, int g, int dA, int dB) {
+    const long long slot =
+        a.slot_mapping ? (long long)w.sv : (long long)w.sv * a.bs + (w.pos % a.bs);
+    half8_t oA = r.kA, oB = r.kB;
+    if (MODE != kCopy) {
+        oA = rotate_chunk<MODE>(a, ks, r.kA, r.pA, w.cA, w.sA, dA, w.pos);
+        oB = rotate_chunk<MODE>(a, ks, r.kB, r.pB, w.cB, w.sB, dB, w.pos);
+    }
+    if (slot < 0) return;
+    const long long dst = (slot * a.G + g) * a.D;
+    *(half8_t *)(a.kc + dst + dA) = oA;
+    *(half8_t *)(a.kc + dst + dB) = oB;
+    *(half8_t *)(a.vc + dst + dA) = r.vA;
+    *(half8_t *)(a.vc + dst + dB) = r.vB;
+}
+
+// A thread takes chunk pair j of kv head g for the two tokens 2p and 2p + 1. Token 2p + 1's rows
+// are requested after token 2p's slot and cos/sin, so token 2p's stores do not wait for them.
+// LANECU: at most kLaneCu * 64 cu entries, held in lanes; otherwise cu is searched in LDS or
+// global memory.
+template <int MODE, bool LANECU>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
-    __shared__ int32_t s_cu[kLdsCu];
-    __shared__ int32_t s_past[kLdsCu];
-    const int hc = a.D >> 4;  // chunk pairs per row
-    const long long n = (long long)a.T * a.G * hc;
-    const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
-    const bool live = gid < n;
-    const long long gidc = live ? gid : n - 1;
-    const int j = (int)(gidc % hc);
-    const long long rg = gidc / hc;
-    const int g = (int)(rg % a.G);
-    const int i = (int)(rg / a.G);
+    __shared__ int32_t s_cu[LANECU ? 1 : kLdsCu];
+    __shared__ int32_t s_past[LANECU ? 1 : kLdsCu];
+    const int lhc = a.D == 128 ? 3 : 2;  // log2 of the chunk pairs per row (D is 64 or 128)
+    const int n = ((a.T + 1) >> 1) * a.G << lhc;  // < 2^31, checked on the host
+    const int gid = blockIdx.x * kThreads + threadIdx.x;
+    const int gidc = gid < n ? gid : n - 1;
+    const int j = gidc & ((1 << lhc) - 1);
+    const int rg = gidc >> lhc;
+    const int p = (int)((unsigned)rg / (unsigned)a.G);
+    const int g = rg - p * a.G;
+    const int i0 = 2 * p, i1 = min(2 * p + 1, a.T - 1);
+    const bool live0 = gid < n, live1 = live0 && 2 * p + 1 < a.T;
     const int dA = j << 3, dB = dA + (a.D >> 1);
     const int lane = threadIdx.x & 63;
+    const half_t *src_k = a.query ? a.query : a.key;
+    const half_t *src_v = a.query ? a.query : a.value;
+    const half_t *ks0 = src_k + (long long)i0 * a.src_stride + a.k_off + (long long)g * a.D;
+    const half_t *vs0 = src_v + (long long)i0 * a.src_stride + a.v_off + (long long)g * a.D;
+    const half_t *ks1 = src_k + (long long)i1 * a.src_stride + a.k_off + (long long)g * a.D;
+    const half_t *vs1 = src_v + (long long)i1 * a.src_stride + a.v_off + (long long)g * a.D;
 
-    // Loads that do not depend on the sequence: both chunks of K and V, NeoX partners that are
-    // not the other chunk, the slot, and (small batches) this lane's cu / past entries.
-    const half_t *ks = (a.query ? a.query : a.key) + (long long)i * a.src_stride + a.k_off +
-                       (long long)g * a.D;
-    const half_t *vs = (a.query ? a.query : a.value) + (long long)i * a.src_stride + a.v_off +
-                       (long long)g * a.D;
-    const half8_t kA = gload<half8_t>(ks + dA), kB = gload<half8_t>(ks + dB);
-    const half8_t vA = gload<half8_t>(vs + dA), vB = gload<half8_t>(vs + dB);
-    half8_t pA = kB, pB = kA;  // kNeoxFull: the chunks are each other's partners
-    if (MODE == kNeox) {
-        const int half = a.rotary_dim >> 1;
-        if (dA < a.rotary_dim) pA = gload<half8_t>(ks + (dA < half ? dA + half : dA - half));
-        if (dB < a.rotary_dim) pB = gload<half8_t>(ks + (dB < half ? dB + half : dB - half));
-    }
-    long long slot = a.slot_mapping ? a.slot_mapping[i] : 0;
-
-    int b, t, past;
-    if (a.B + 1 <= kLaneCu * 64) {
-        int cuv[kLaneCu], pav[kLaneCu];
+    // cu / past entries first (clamped, unconditional), then token 2p's rows: waiting for the
+    // entries leaves the rows in flight
+    int cuv[kLaneCu], pav[kLaneCu];
+    if (LANECU)
         for (int c = 0; c < kLaneCu; ++c) {
             const int k = 64 * c + lane;
-            cuv[c] = k <= a.B ? a.cu[k] : 0x7fffffff;
-            pav[c] = k < a.B ? a.past[k] : 0;
+            cuv[c] = a.cu[min(k, a.B)];
+            pav[c] = a.past[min(k, a.B - 1)];
         }
-        const int i0 = __builtin_amdgcn_readfirstlane(i);
-        if (__ballot(i != i0) == 0) {
-            // one token per wave: b + 1 = number of entries cu[k] <= i (cu[B] = T > i)
-            int cnt = 0;
-            for (int c = 0; c < kLaneCu; ++c) cnt += __popcll(__ballot(cuv[c] <= i0));
-            b = min(cnt, a.B) - 1;
-            const int c = b >> 6, l = b & 63;
-            int cb = 0, pb = 0;
-            for (int q = 0; q < kLaneCu; ++q)
-                if (q == c) { cb = __shfl(cuv[q], l, 64); pb = __shfl(pav[q], l, 64); }
-            t = i0 - cb;
-            past = pb;
-        } else {
-            // several tokens in the wave: count entry by entry
-            int cnt = 0;
-            for (int q = 0; q < kLaneCu; ++q)
-                for (int l = 0; l < 64 && 64 * q + l <= a.B; ++l) cnt += __shfl(cuv[q], l, 64) <= i;
-            b = min(cnt, a.B) - 1;
-            const int c = b >> 6, l = b & 63;
-            int cb = 0, pb = 0;
-            for (int q = 0; q < kLaneCu; ++q) {
-                const int x = __shfl(cuv[q], l, 64), y = __shfl(pav[q], l, 64);
-                if (q == c) { cb = x; pb = y; }
-            }
-            t = i - cb;
-            past = pb;
-        }
+    const RowIn r0 = load_row<MODE>(a, ks0, vs0, dA, dB);
+    int b0, b1, cb0, cb1, pb0, pb1;
+    if (LANECU) {
+        for (int c = 0; c < kLaneCu; ++c)
+            if (64 * c + lane > a.B) cuv[c] = 0x7fffffff;  // entries past cu[B] never count
+        lane_lookup(a, cuv, pav, i0, b0, cb0, pb0);
+        lane_lookup(a, cuv, pav, i1, b1, cb1, pb1);
     } else {
         const bool lds = a.B + 1 <= kLdsCu;  // uniform over the grid
         if (lds) {
@@ -185,44 +254,27 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
             }
             __syncthreads();
         }
-        b = lds ? find_batch(s_cu, a.B, i) : find_batch(a.cu, a.B, i);
-        t = i - (lds ? s_cu[b] : a.cu[b]);
-        past = lds ? s_past[b] : a.past[b];
+        const int32_t *cu = lds ? s_cu : a.cu;
+        const int32_t *pa = lds ? s_past : a.past;
+        b0 = find_batch(cu, a.B, i0);
+        b1 = find_batch(cu, a.B, i1);
+        cb0 = cu[b0]; pb0 = pa[b0];
+        cb1 = cu[b1]; pb1 = pa[b1];
     }
-    if (!live) return;
-    const int pos = past + t;
-    if (!a.slot_mapping) {
-        const int blk = pos / a.bs;
-        slot = (long long)a.bt[(long long)b * a.MB + blk] * a.bs + (pos - blk * a.bs);
-    }
-
-    half8_t oA = kA, oB = kB;
-    if (MODE != kCopy) {
-        half8_t cA, sA, cB, sB;
-        load_cs<MODE>(a, dA, pos, cA, sA);
-        if (MODE == kNeoxFull) {  // dB = dA + R/2 uses the same columns
-            cB = cA;
-            sB = sA;
-        } else {
-            load_cs<MODE>(a, dB, pos, cB, sB);
-        }
-        oA = rotate_chunk<MODE>(a, ks, kA, pA, cA, sA, dA, pos);
-        oB = rotate_chunk<MODE>(a, ks, kB, pB, cB, sB, dB, pos);
-    }
-    if (slot < 0) return;
-    const long long dst = (slot * a.G + g) * a.D;
-    *(half8_t *)(a.kc + dst + dA) = oA;
-    *(half8_t *)(a.kc + dst + dB) = oB;
-    *(half8_t *)(a.vc + dst + dA) = vA;
-    *(half8_t *)(a.vc + dst + dB) = vB;
+    const RowAt w0 = locate<MODE>(a, i0, b0, i0 - cb0, pb0, dA, dB);
+    const RowIn r1 = load_row<MODE>(a, ks1, vs1, dA, dB);
+    const RowAt w1 = locate<MODE>(a, i1, b1, i1 - cb1, pb1, dA, dB);
+    if (live0) store_row<MODE>(a, ks0, r0, w0, g, dA, dB);
+    if (live1) store_row<MODE>(a, ks1, r1, w1, g, dA, dB);
 }
 
 }  // namespace
 
 pa_status launch_kv_append(const AppendArgs &a, hipStream_t stream) {
     LaunchScope scope("kv_append", stream);
-    const long long n = (long long)a.T * a.G * (a.D >> 4);
+    const long long n = (long long)((a.T + 1) / 2) * a.G * (a.D >> 4);
     if (n == 0) return PA_OK;
+    if (n + kThreads >= (1LL << 31)) return PA_ERR_UNSUPPORTED;  // 32-bit thread indexing
     const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
     const int R = a.rotary_dim;
     int mode = kCopy;
@@ -230,15 +282,20 @@ pa_status launch_kv_append(const AppendArgs &a, hipStream_t stream) {
         mode = R == a.D ? kNeoxFull : (R % 16 == 0 ? kNeox : kGeneric);
     else if (a.rotary_mode == PA_ROTARY_INTERLEAVED)
         mode = (R % 8 == 0) ? kInter : kGeneric;
+    const bool lanecu = a.B + 1 <= kLaneCu * 64;
+#define PA_APPEND(M)                                                                    \
+    if (lanecu)                                                                         \
+        scope.launch(append_kernel<M, true>, dim3(grid), dim3(kThreads), 0, a);         \
+    else                                                                                \
+        scope.launch(append_kernel<M, false>, dim3(grid), dim3(kThreads), 0, a);
     switch (mode) {
-        case kCopy: scope.launch(append_kernel<kCopy>, dim3(grid), dim3(kThreads), 0, a); break;
-        case kNeoxFull:
-            scope.launch(append_kernel<kNeoxFull>, dim3(grid), dim3(kThreads), 0, a);
-            break;
-        case kNeox: scope.launch(append_kernel<kNeox>, dim3(grid), dim3(kThreads), 0, a); break;
-        case kInter: scope.launch(append_kernel<kInter>, dim3(grid), dim3(kThreads), 0, a); break;
-        default: scope.launch(append_kernel<kGeneric>, dim3(grid), dim3(kThreads), 0, a); break;
+        case kCopy: PA_APPEND(kCopy); break;
+        case kNeoxFull: PA_APPEND(kNeoxFull); break;
+        case kNeox: PA_APPEND(kNeox); break;
+        case kInter: PA_APPEND(kInter); break;
+        default: PA_APPEND(kGeneric); break;
     }
+#undef PA_APPEND
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
