@@ -45,6 +45,8 @@ def _load():
     lib.oracle_past_length_padded.restype = _i
     lib.oracle_kv_append.argtypes = [_i] * 8 + [_vp] * 5 + [_vp] * 4 + [_vp, _vp, _i, _i]
     lib.oracle_kv_append.restype = None
+    lib.oracle_rotate_query.argtypes = [_i] * 5 + [_vp] * 5 + [_i, _i, _vp]
+    lib.oracle_rotate_query.restype = None
     lib.oracle_paged_attention.argtypes = ([_i] * 7 + [_vp, _ll, _vp, _vp, _vp, _vp, _vp, _d, _i,
                                                        _vp])
     lib.oracle_paged_attention.restype = None
@@ -115,6 +117,22 @@ def kv_append(w, key_cache=None, value_cache=None):
                          _p(bt), _p(sm), _p(cs), _p(sn), int(w["rotary_dim"]),
                          int(w["rotary_mode"]))
     return kc.view(np.float16), vc.view(np.float16)
+
+
+def rotate_query(w, rotary_mode=None, rotary_dim=None):
+    """New query rows of workload ``w`` rotated at their positions (the key rotation applied to
+    every query head). Returns fp16 [T, H*D]."""
+    lib = _load()
+    q = _h(w["query"])
+    cu, past = _c(w["cu"], np.int32), _c(w["past"], np.int32)
+    cs, sn = _h(w["cos"]), _h(w["sin"])
+    out = np.zeros((w["T"], w["H"] * w["D"]), dtype=np.uint16)
+    lib.oracle_rotate_query(w["B"], w["H"], w["G"], w["D"], int(w["packed"]), _p(q), _p(cu),
+                            _p(past), _p(cs), _p(sn),
+                            int(w["rotary_dim"] if rotary_dim is None else rotary_dim),
+                            int(w["rotary_mode"] if rotary_mode is None else rotary_mode),
+                            _p(out))
+    return out.view(np.float16)
 
 
 def _q_stride(w):

@@ -221,6 +221,47 @@ void oracle_kv_append(int T, int B, int H, int G, int D, int bs, int MB, int pac
     }
 }
 
+/* Query rotation at the same positions (the first "next" step past the pages, which rotate only
+ * keys in the append and hand queries to attention already positioned): new query row t of
+ * sequence b sits at pos = past[b] + t, and each of its H head rows gets the same per-pair
+ * float32 rotation the key path applies, with the same cos/sin rows; components past
+ * rotary_dim are copied. Source rows are the Q part of packed rows or a separate [T, H*D]
+ * array; q_out is [T, H*D] fp16 and every row of every sequence is written. */
+void oracle_rotate_query(int B, int H, int G, int D, int packed, const uint16_t *query,
+                         const int32_t *cu, const int32_t *past, const uint16_t *cos_cache,
+                         const uint16_t *sin_cache, int rotary_dim, int rotary_mode,
+                         uint16_t *q_out)
+{
+    const int half = rotary_dim / 2;
+    const long long stride = packed ? (long long)(H + 2 * G) * D : (long long)H * D;
+    for (int b = 0; b < B; ++b) {
+        const int n = cu[b + 1] - cu[b];
+        for (int t = 0; t < n; ++t) {
+            const long long i = (long long)cu[b] + t;
+            const long long pos = (long long)past[b] + t;
+            for (int h = 0; h < H; ++h) {
+                const uint16_t *qs = query + i * stride + (long long)h * D;
+                uint16_t *qd = q_out + (i * H + h) * (long long)D;
+                for (int d = 0; d < D; ++d) {
+                    if (rotary_mode != ORACLE_ROTARY_NONE && d < rotary_dim) {
+                        const int c = rotary_column(d, half, rotary_mode);
+                        const float cs = (float)oracle_f16_to_f64(cos_cache[pos * half + c]);
+                        const float sn = (float)oracle_f16_to_f64(sin_cache[pos * half + c]);
+                        const float own = (float)oracle_f16_to_f64(qs[d]);
+                        const float partner =
+                            (float)oracle_f16_to_f64(qs[rotary_partner(d, half, rotary_mode)]);
+                        qd[d] = oracle_f32_to_f16(
+                            rotary_component(own, partner, cs, sn,
+                                             rotary_is_first(d, half, rotary_mode)));
+                    } else {
+                        qd[d] = qs[d];
+                    }
+                }
+            }
+        }
+    }
+}
+
 /* ---------------------------------------------------------------------------------------- */
 /* Paged attention: gather to contiguous, then dense softmax attention.                      */
 /* ---------------------------------------------------------------------------------------- */

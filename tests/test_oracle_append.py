@@ -244,3 +244,75 @@ def test_rotary_preserves_pair_norm(oracle):
     assert np.all(np.abs(n_out - n_in) <= 2.0 ** -10 * n_in + 1e-6)
     # the fp16 tables themselves keep cos^2 + sin^2 within 2 fp16 ulps of 1
     assert np.all(np.abs(c * c + s * s - 1.0) < 2e-3)
+
+
+# ------------------------------------------------------------------ query rotation
+def _query_rows(w):
+    """[T, H, D] float64 view of the new query rows (Q part of packed rows, or separate Q)."""
+    T, H, G, D = w["T"], w["H"], w["G"], w["D"]
+    q = w["query"].reshape(T, -1)[:, :H * D]
+    return q.astype(np.float64).reshape(T, H, D)
+
+
+@pytest.mark.parametrize("mode", [W.ROTARY_NEOX, W.ROTARY_INTERLEAVED])
+@pytest.mark.parametrize("packed", [False, True])
+def test_query_rotary_position_zero_is_identity(oracle, mode, packed):
+    """cos(0) = 1, sin(0) = 0: position 0 copies every query head row bit for bit."""
+    w = W.paged_workload(20, past=[0], n_new=[1], num_heads=4, kv_num_heads=2, head_size=64,
+                         block_size=8, table="pool", packed=packed, rotary_mode=mode,
+                         rotary_dim=64, rotary_positions=8, name="qrot0")
+    got = oracle.rotate_query(w)
+    H, D = w["H"], w["D"]
+    src = w["query"].reshape(1, -1)[:, :H * D]
+    assert np.array_equal(got.view(np.uint16), np.ascontiguousarray(src).view(np.uint16))
+
+
+@pytest.mark.parametrize("mode", [W.ROTARY_NEOX, W.ROTARY_INTERLEAVED])
+@pytest.mark.parametrize("D,R,packed", [(64, 64, False), (128, 128, True), (64, 32, False),
+                                        (128, 48, True)])
+def test_query_rotary_matches_complex_multiplication(oracle, mode, D, R, packed):
+    """Each query head row rotated as complex multiplication in float64 (pairs as for keys), within
+    half an fp16 ulp plus the float32 rounding of the page's expression; dims past R copied."""
+    w = W.paged_workload(21, past=[0, 9, 40], n_new=[2, 3, 1], num_heads=6, kv_num_heads=2,
+                         head_size=D, block_size=8, table="pool", packed=packed,
+                         rotary_mode=mode, rotary_dim=R, rotary_positions=64, name="qrot")
+    got = oracle.rotate_query(w).astype(np.float64).reshape(w["T"], w["H"], D)
+    q = _query_rows(w)
+    half = R // 2
+    pos = _positions(w)
+    c = w["cos"].astype(np.float64)[pos][:, None, :]
+    s = w["sin"].astype(np.float64)[pos][:, None, :]
+    if mode == W.ROTARY_NEOX:
+        a, bb = q[..., :half], q[..., half:R]
+    else:
+        a, bb = q[..., 0:R:2], q[..., 1:R:2]
+    z = (a + 1j * bb) * (c + 1j * s)
+    ref = q.copy()
+    if mode == W.ROTARY_NEOX:
+        ref[..., :half], ref[..., half:R] = z.real, z.imag
+    else:
+        ref[..., 0:R:2], ref[..., 1:R:2] = z.real, z.imag
+    half_ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64) / 2
+    f32 = 4 * np.finfo(np.float32).eps * (np.abs(ref) + np.abs(q).max(axis=-1, keepdims=True))
+    assert np.all(np.abs(got - ref) <= half_ulp + f32)
+    assert np.array_equal(got[..., R:], q[..., R:])
+
+
+@pytest.mark.parametrize("mode", [W.ROTARY_NEOX, W.ROTARY_INTERLEAVED])
+def test_query_rotation_equals_key_rotation(oracle, mode):
+    """With one query head per kv head, feeding the query rows in as keys makes the key path
+    write exactly the rotated query rows into the cache."""
+    w = _rot_workload(22, mode, D=128, R=128)
+    wk = dict(w)
+    wk["key"] = w["query"].reshape(w["key"].shape).copy()
+    kc, _ = oracle.kv_append(wk)
+    rows = _new_key_rows(wk, kc).reshape(w["T"], -1)
+    assert np.array_equal(oracle.rotate_query(w).view(np.uint16), rows.view(np.uint16))
+
+
+def test_query_rotation_none_copies(oracle):
+    w = W.paged_workload(23, past=[3, 7], n_new=[2, 1], num_heads=4, kv_num_heads=1,
+                         head_size=64, block_size=8, table="pool", packed=True, name="qcopy")
+    got = oracle.rotate_query(w)
+    src = np.ascontiguousarray(w["query"].reshape(w["T"], -1)[:, :4 * 64])
+    assert np.array_equal(got.view(np.uint16), src.view(np.uint16))
