@@ -208,7 +208,20 @@ def run_extra(args, torch, np, pa, dev, W):
                                 / HBM_PEAK_GBS, 2),
         "append_bytes": app_bytes,
     }
-    del c
+    # the append with every new query row rotated into q_out in the same launch
+    q_out = torch.empty((w["T"], w["H"] * w["D"]), dtype=torch.float16, device="cuda")
+    pa.pa_timing_reset()
+    pa.pa_timing_enable(True)
+    timed(lambda: c.append_rotate_query(q_out), steps, 2, torch)
+    pa.pa_timing_enable(False)
+    t_rq = pa.pa_timing_get("kv_append")
+    pa.pa_timing_reset()
+    us_rq = t_rq[0] / max(1, t_rq[1]) * 1e3
+    rq_bytes = app_bytes + w["T"] * w["H"] * w["D"] * 2 * 2
+    out["mixed_prefill_decode"].update({
+        "append_rotate_query_us": round(us_rq, 2), "append_rotate_query_bytes": rq_bytes,
+        "append_rotate_query_GBps": round(rq_bytes / (us_rq * 1e-6) / 1e9, 1)})
+    del c, q_out
     torch.cuda.empty_cache()
 
     # the append alone at 16x the mixed workload's prefill tokens: its bandwidth regime

@@ -22,7 +22,8 @@ PA_ROTARY_NONE, PA_ROTARY_NEOX, PA_ROTARY_INTERLEAVED = 0, 1, 2
 PA_F16, PA_F32 = 0, 1
 PA_SPLITS_AUTO, PA_SPLITS_PAGE_RULE = 0, -1
 
-EXPORTED = ("pa_kv_append", "pa_paged_attention_workspace_size", "pa_paged_attention",
+EXPORTED = ("pa_kv_append", "pa_kv_append_rotate_query", "pa_paged_attention_workspace_size",
+            "pa_paged_attention",
             "pa_split_combine", "pa_sparse_forward_workspace_size", "pa_sparse_forward",
             "pa_status_string", "pa_timing_enable", "pa_timing_reset", "pa_timing_get")
 
@@ -65,6 +66,8 @@ def lib():
     ss = C.POINTER(SparseShape)
     L.pa_kv_append.argtypes = [sp] + [_vp] * 11 + [_i32, _i32, _i32, _vp]
     L.pa_kv_append.restype = _i32
+    L.pa_kv_append_rotate_query.argtypes = [sp] + [_vp] * 11 + [_i32, _i32, _i32, _vp, _vp]
+    L.pa_kv_append_rotate_query.restype = _i32
     L.pa_paged_attention_workspace_size.argtypes = [sp, _i32]
     L.pa_paged_attention_workspace_size.restype = C.c_size_t
     L.pa_paged_attention.argtypes = ([sp] + [_vp] * 6 + [C.c_float, _i32, _i32, _vp, C.c_size_t,
@@ -140,6 +143,19 @@ def pa_kv_append(shape, query, key, value, key_cache, value_cache, cumulative_se
         _p(cos_cache), _p(sin_cache), int(rotary_dim), int(rotary_mode), int(rotary_positions),
         _s(stream))
     return _check(st, "pa_kv_append", check)
+
+
+def pa_kv_append_rotate_query(shape, query, key, value, key_cache, value_cache,
+                              cumulative_sequence_length, past_seqlens, block_table, q_out,
+                              slot_mapping=None, cos_cache=None, sin_cache=None, rotary_dim=0,
+                              rotary_mode=PA_ROTARY_NONE, rotary_positions=0, stream=None,
+                              check=True):
+    st = lib().pa_kv_append_rotate_query(
+        C.byref(shape), _p(query), _p(key), _p(value), _p(key_cache), _p(value_cache),
+        _p(cumulative_sequence_length), _p(past_seqlens), _p(block_table), _p(slot_mapping),
+        _p(cos_cache), _p(sin_cache), int(rotary_dim), int(rotary_mode), int(rotary_positions),
+        _p(q_out), _s(stream))
+    return _check(st, "pa_kv_append_rotate_query", check)
 
 
 def pa_paged_attention_workspace_size(shape, num_splits=PA_SPLITS_AUTO):

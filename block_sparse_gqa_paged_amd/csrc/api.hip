@@ -234,12 +234,13 @@ pa_status pa_timing_get(const char *kernel, double *total_ms, int64_t *launches)
     return st;
 }
 
-pa_status pa_kv_append(const pa_paged_shape *shape, const void *query, const void *key,
-                       const void *value, void *key_cache, void *value_cache,
-                       const int32_t *cumulative_sequence_length, const int32_t *past_seqlens,
-                       const int32_t *block_table, const int32_t *slot_mapping,
-                       const void *cos_cache, const void *sin_cache, int32_t rotary_dim,
-                       int32_t rotary_mode, int32_t rotary_positions, void *stream) {
+static pa_status kv_append(const pa_paged_shape *shape, const void *query, const void *key,
+                           const void *value, void *key_cache, void *value_cache,
+                           const int32_t *cumulative_sequence_length,
+                           const int32_t *past_seqlens, const int32_t *block_table,
+                           const int32_t *slot_mapping, const void *cos_cache,
+                           const void *sin_cache, int32_t rotary_dim, int32_t rotary_mode,
+                           int32_t rotary_positions, void *q_out, void *stream) {
     pa_status st = check_shape(shape);
     if (st != PA_OK) return st;
     const pa_paged_shape &s = *shape;
@@ -287,7 +288,41 @@ pa_status pa_kv_append(const pa_paged_shape *shape, const void *query, const voi
     a.MB = s.max_blocks;
     a.rotary_dim = rotary_mode == PA_ROTARY_NONE ? 0 : rotary_dim;
     a.rotary_mode = rotary_mode;
+    a.q_out = (half_t *)q_out;
+    a.q_src = (const half_t *)query;  // set for either layout (a.query is the packed rows only)
+    a.q_stride = s.packed_qkv ? (int64_t)(H + 2 * G) * D : (int64_t)H * D;
+    a.H = H;
+    a.nkv = a.nkv_pad = a.nq = 0;  // set by the launcher
     return launch_kv_append(a, (hipStream_t)stream);
+}
+
+pa_status pa_kv_append(const pa_paged_shape *shape, const void *query, const void *key,
+                       const void *value, void *key_cache, void *value_cache,
+                       const int32_t *cumulative_sequence_length, const int32_t *past_seqlens,
+                       const int32_t *block_table, const int32_t *slot_mapping,
+                       const void *cos_cache, const void *sin_cache, int32_t rotary_dim,
+                       int32_t rotary_mode, int32_t rotary_positions, void *stream) {
+    return kv_append(shape, query, key, value, key_cache, value_cache,
+                     cumulative_sequence_length, past_seqlens, block_table, slot_mapping,
+                     cos_cache, sin_cache, rotary_dim, rotary_mode, rotary_positions, nullptr,
+                     stream);
+}
+
+pa_status pa_kv_append_rotate_query(const pa_paged_shape *shape, const void *query,
+                                    const void *key, const void *value, void *key_cache,
+                                    void *value_cache, const int32_t *cumulative_sequence_length,
+                                    const int32_t *past_seqlens, const int32_t *block_table,
+                                    const int32_t *slot_mapping, const void *cos_cache,
+                                    const void *sin_cache, int32_t rotary_dim,
+                                    int32_t rotary_mode, int32_t rotary_positions, void *q_out,
+                                    void *stream) {
+    if (!shape) return PA_ERR_NULL;
+    if (!query || !q_out) return PA_ERR_NULL;
+    if (q_out == query) return PA_ERR_SHAPE;  // rotated rows go to their own buffer
+    return kv_append(shape, query, key, value, key_cache, value_cache,
+                     cumulative_sequence_length, past_seqlens, block_table, slot_mapping,
+                     cos_cache, sin_cache, rotary_dim, rotary_mode, rotary_positions, q_out,
+                     stream);
 }
 
 size_t pa_paged_attention_workspace_size(const pa_paged_shape *shape, int32_t num_splits) {

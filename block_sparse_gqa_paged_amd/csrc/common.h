@@ -66,6 +66,11 @@ struct AppendArgs {
     int64_t v_off;       // element offset of V inside a source row
     int T, B, G, D, bs, MB;
     int rotary_dim, rotary_mode;
+    half_t *q_out;       // rotated query rows [T, H*D], or NULL: no query rotation
+    const half_t *q_src; // query rows to rotate (packed rows, or separate [T, H*D])
+    int64_t q_stride;    // elements per query source row (H*D or (H+2G)*D)
+    int H;
+    int nkv, nkv_pad, nq;  // threads for key/value rows, padded to whole workgroups; query rows
 };
 pa_status launch_kv_append(const AppendArgs &a, hipStream_t stream);
 

@@ -110,24 +110,26 @@ __device__ __forceinline__ void load_cs(const AppendArgs &a, int d0, int pos, ha
     }
 }
 
-// One (token, kv head) row's two chunks: source data, then its place in the cache.
+// One row's two chunks: source data, then its destination.
 struct RowIn {
     half8_t kA, kB, vA, vB, pA, pB;
 };
 struct RowAt {
     int pos;
-    int32_t sv;  // slot_mapping entry, or the block id of pos
+    int32_t sv;  // slot_mapping entry, or the block id of pos (key/value rows)
     half8_t cA, sA, cB, sB;
 };
 
-template <int MODE>
+template <int MODE, bool QROLE>
 __device__ __forceinline__ RowIn load_row(const AppendArgs &a, const half_t *ks,
                                           const half_t *vs, int dA, int dB) {
     RowIn r;
     r.kA = gload<half8_t>(ks + dA);
     r.kB = gload<half8_t>(ks + dB);
-    r.vA = gload<half8_t>(vs + dA);
-    r.vB = gload<half8_t>(vs + dB);
+    if (!QROLE) {
+        r.vA = gload<half8_t>(vs + dA);
+        r.vB = gload<half8_t>(vs + dB);
+    }
     r.pA = r.kB;  // kNeoxFull: the chunks are each other's partners
     r.pB = r.kA;
     if (MODE == kNeox) {  // partners of chunks past the rotary dims: chunk 0 (unused)
@@ -163,15 +165,19 @@ __device__ __forceinline__ void lane_lookup(const AppendArgs &a, const int (&cuv
     }
 }
 
-// Position of the token, then one load of its slot_mapping entry or block id, and its cos/sin.
-template <int MODE>
+// Position of the token; for key/value rows one load of its slot_mapping entry or block id;
+// the cos/sin chunks.
+template <int MODE, bool QROLE>
 __device__ __forceinline__ RowAt locate(const AppendArgs &a, int i, int b, int t, int past,
                                         int dA, int dB) {
     RowAt w;
     w.pos = past + t;
-    const int32_t *sp = a.slot_mapping ? a.slot_mapping + i
-                                       : a.bt + (long long)b * a.MB + w.pos / a.bs;
-    w.sv = *sp;
+    w.sv = 0;
+    if (!QROLE) {
+        const int32_t *sp = a.slot_mapping ? a.slot_mapping + i
+                                           : a.bt + (long long)b * a.MB + w.pos / a.bs;
+        w.sv = *sp;
+    }
     if (MODE != kCopy && MODE != kGeneric) {
         load_cs<MODE>(a, dA, w.pos, w.cA, w.sA);
         if (MODE == kNeoxFull) {  // dB = dA + R/2 uses the same columns
@@ -184,16 +190,23 @@ __device__ __forceinline__ RowAt locate(const AppendArgs &a, int i, int b, int t
     return w;
 }
 
-template <int MODE>
+// Rotate K (or Q) and write: key/value rows to their cache slot, query rows to q_out.
+template <int MODE, bool QROLE>
 __device__ __forceinline__ void store_row(const AppendArgs &a, const half_t *ks, const RowIn &r,
-                                          const RowAt &w, int g, int dA, int dB) {
-    const long long slot =
-        a.slot_mapping ? (long long)w.sv : (long long)w.sv * a.bs + (w.pos % a.bs);
+                                          const RowAt &w, int i, int g, int dA, int dB) {
     half8_t oA = r.kA, oB = r.kB;
     if (MODE != kCopy) {
         oA = rotate_chunk<MODE>(a, ks, r.kA, r.pA, w.cA, w.sA, dA, w.pos);
         oB = rotate_chunk<MODE>(a, ks, r.kB, r.pB, w.cB, w.sB, dB, w.pos);
     }
+    if (QROLE) {  // query rows: only launched with q_out and q_src set
+        half_t *qd = a.q_out + ((long long)i * a.H + g) * a.D;
+        *(half8_t *)(qd + dA) = oA;
+        *(half8_t *)(qd + dB) = oB;
+        return;
+    }
+    const long long slot =
+        a.slot_mapping ? (long long)w.sv : (long long)w.sv * a.bs + (w.pos % a.bs);
     if (slot < 0) return;
     const long long dst = (slot * a.G + g) * a.D;
     *(half8_t *)(a.kc + dst + dA) = oA;
@@ -202,32 +215,34 @@ __device__ __forceinline__ void store_row(const AppendArgs &a, const half_t *ks,
     *(half8_t *)(a.vc + dst + dB) = r.vB;
 }
 
-// A thread takes chunk pair j of kv head g for the two tokens 2p and 2p + 1. Token 2p + 1's rows
-// are requested after token 2p's slot and cos/sin, so token 2p's stores do not wait for them.
-// LANECU: at most kLaneCu * 64 cu entries, held in lanes; otherwise cu is searched in LDS or
-// global memory.
-template <int MODE, bool LANECU>
-__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
-    __shared__ int32_t s_cu[LANECU ? 1 : kLdsCu];
-    __shared__ int32_t s_past[LANECU ? 1 : kLdsCu];
+// Thread gid < n takes chunk pair j of head g (a kv head, or a query head when QROLE) for the
+// two tokens 2p and 2p + 1. Token 2p + 1's rows are requested after token 2p's slot and
+// cos/sin, so token 2p's stores do not wait for them. LANECU: at most kLaneCu * 64 cu entries,
+// held in lanes; otherwise cu is searched in LDS (whole workgroups take one role, so the
+// barrier is uniform) or in global memory.
+template <int MODE, bool LANECU, bool QROLE>
+__device__ __forceinline__ void append_pairs(const AppendArgs &a, int gid, int n,
+                                             int32_t *s_cu, int32_t *s_past) {
     const int lhc = a.D == 128 ? 3 : 2;  // log2 of the chunk pairs per row (D is 64 or 128)
-    const int n = ((a.T + 1) >> 1) * a.G << lhc;  // < 2^31, checked on the host
-    const int gid = blockIdx.x * kThreads + threadIdx.x;
+    const int rows = QROLE ? a.H : a.G;  // head rows per token
     const int gidc = gid < n ? gid : n - 1;
     const int j = gidc & ((1 << lhc) - 1);
     const int rg = gidc >> lhc;
-    const int p = (int)((unsigned)rg / (unsigned)a.G);
-    const int g = rg - p * a.G;
+    const int p = (int)((unsigned)rg / (unsigned)rows);
+    const int g = rg - p * rows;
     const int i0 = 2 * p, i1 = min(2 * p + 1, a.T - 1);
     const bool live0 = gid < n, live1 = live0 && 2 * p + 1 < a.T;
     const int dA = j << 3, dB = dA + (a.D >> 1);
     const int lane = threadIdx.x & 63;
-    const half_t *src_k = a.query ? a.query : a.key;
+    const half_t *src_k = QROLE ? a.q_src : (a.query ? a.query : a.key);
     const half_t *src_v = a.query ? a.query : a.value;
-    const half_t *ks0 = src_k + (long long)i0 * a.src_stride + a.k_off + (long long)g * a.D;
-    const half_t *vs0 = src_v + (long long)i0 * a.src_stride + a.v_off + (long long)g * a.D;
-    const half_t *ks1 = src_k + (long long)i1 * a.src_stride + a.k_off + (long long)g * a.D;
-    const half_t *vs1 = src_v + (long long)i1 * a.src_stride + a.v_off + (long long)g * a.D;
+    const long long stride = QROLE ? a.q_stride : a.src_stride;
+    const long long off_k = (QROLE ? 0 : a.k_off) + (long long)g * a.D;
+    const long long off_v = a.v_off + (long long)g * a.D;
+    const half_t *ks0 = src_k + (long long)i0 * stride + off_k;
+    const half_t *ks1 = src_k + (long long)i1 * stride + off_k;
+    const half_t *vs0 = QROLE ? nullptr : src_v + (long long)i0 * stride + off_v;
+    const half_t *vs1 = QROLE ? nullptr : src_v + (long long)i1 * stride + off_v;
 
     // cu / past entries first (clamped, unconditional), then token 2p's rows: waiting for the
     // entries leaves the rows in flight
@@ -238,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
             cuv[c] = a.cu[min(k, a.B)];
             pav[c] = a.past[min(k, a.B - 1)];
         }
-    const RowIn r0 = load_row<MODE>(a, ks0, vs0, dA, dB);
+    const RowIn r0 = load_row<MODE, QROLE>(a, ks0, vs0, dA, dB);
     int b0, b1, cb0, cb1, pb0, pb1;
     if (LANECU) {
         for (int c = 0; c < kLaneCu; ++c)
@@ -261,21 +276,43 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         cb0 = cu[b0]; pb0 = pa[b0];
         cb1 = cu[b1]; pb1 = pa[b1];
     }
-    const RowAt w0 = locate<MODE>(a, i0, b0, i0 - cb0, pb0, dA, dB);
-    const RowIn r1 = load_row<MODE>(a, ks1, vs1, dA, dB);
-    const RowAt w1 = locate<MODE>(a, i1, b1, i1 - cb1, pb1, dA, dB);
-    if (live0) store_row<MODE>(a, ks0, r0, w0, g, dA, dB);
-    if (live1) store_row<MODE>(a, ks1, r1, w1, g, dA, dB);
+    const RowAt w0 = locate<MODE, QROLE>(a, i0, b0, i0 - cb0, pb0, dA, dB);
+    const RowIn r1 = load_row<MODE, QROLE>(a, ks1, vs1, dA, dB);
+    const RowAt w1 = locate<MODE, QROLE>(a, i1, b1, i1 - cb1, pb1, dA, dB);
+    if (live0) store_row<MODE, QROLE>(a, ks0, r0, w0, i0, g, dA, dB);
+    if (live1) store_row<MODE, QROLE>(a, ks1, r1, w1, i1, g, dA, dB);
+}
+
+// Workgroups [0, nkv_pad / kThreads) append key/value rows; the rest (when q_out is given)
+// rotate query rows.
+template <int MODE, bool LANECU>
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+    __shared__ int32_t s_cu[LANECU ? 1 : kLdsCu];
+    __shared__ int32_t s_past[LANECU ? 1 : kLdsCu];
+    const int gid = blockIdx.x * kThreads + threadIdx.x;
+    if (gid < a.nkv_pad)
+        append_pairs<MODE, LANECU, false>(a, gid, a.nkv, s_cu, s_past);
+    else
+        append_pairs<MODE, LANECU, true>(a, gid - a.nkv_pad, a.nq, s_cu, s_past);
 }
 
 }  // namespace
 
-pa_status launch_kv_append(const AppendArgs &a, hipStream_t stream) {
+pa_status launch_kv_append(const AppendArgs &a_in, hipStream_t stream) {
     LaunchScope scope("kv_append", stream);
-    const long long n = (long long)((a.T + 1) / 2) * a.G * (a.D >> 4);
-    if (n == 0) return PA_OK;
-    if (n + kThreads >= (1LL << 31)) return PA_ERR_UNSUPPORTED;  // 32-bit thread indexing
-    const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
+    AppendArgs a = a_in;
+    const long long pairs = (long long)((a.T + 1) / 2) * (a.D >> 4);  // per head row
+    const long long nkv = pairs * a.G;
+    const long long nkv_pad = (nkv + kThreads - 1) / kThreads * kThreads;
+    const long long nq = a.q_out ? pairs * a.H : 0;
+    const long long total = nkv_pad + nq;
+    if (nkv == 0) return PA_OK;
+    if (a.q_out && !a.q_src) return PA_ERR_NULL;
+    if (total + kThreads >= (1LL << 31)) return PA_ERR_UNSUPPORTED;  // 32-bit thread indexing
+    a.nkv = (int)nkv;
+    a.nkv_pad = (int)nkv_pad;
+    a.nq = (int)nq;
+    const unsigned grid = (unsigned)((total + kThreads - 1) / kThreads);
     const int R = a.rotary_dim;
     int mode = kCopy;
     if (a.rotary_mode == PA_ROTARY_NEOX)

@@ -7,7 +7,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, pa_kv_append, pa_paged_attention,
+from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, pa_kv_append, pa_kv_append_rotate_query,
+               pa_paged_attention,
                pa_paged_attention_workspace_size, pa_sparse_forward,
                pa_sparse_forward_workspace_size, pa_split_combine, paged_shape, sparse_shape)
 
@@ -52,6 +53,22 @@ class PagedCase:
                      self.slot_mapping if use_slot_mapping else None, self.cos, self.sin,
                      w["rotary_dim"], w["rotary_mode"],
                      0 if self.cos is None else self.cos.shape[0], stream=stream)
+
+    def append_rotate_query(self, q_out=None, use_slot_mapping=True, stream=None):
+        """The append plus every new query row rotated at its position into q_out
+        (fp16 [T, H*D]; allocated when not given). Returns q_out."""
+        w = self.w
+        if q_out is None:
+            q_out = torch.empty((w["T"], w["H"] * w["D"]), dtype=torch.float16,
+                                device=self.device)
+        pa_kv_append_rotate_query(
+            self.shape, self.query, None if w["packed"] else self.key,
+            None if w["packed"] else self.value, self.key_cache, self.value_cache, self.cu,
+            self.past, self.block_table, q_out,
+            self.slot_mapping if use_slot_mapping else None, self.cos, self.sin,
+            w["rotary_dim"], w["rotary_mode"], 0 if self.cos is None else self.cos.shape[0],
+            stream=stream)
+        return q_out
 
     def workspace_for(self, num_splits):
         n = pa_paged_attention_workspace_size(self.shape, num_splits)

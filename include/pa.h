@@ -1,11 +1,12 @@
 /*
  * pa.h - paged grouped-query attention over a block-table fp16 KV cache, for AMD MI355X (gfx950).
  *
- * A C ABI over device pointers. Four operations make up the path:
+ * A C ABI over device pointers. These operations make up the path:
  *   pa_kv_append        fused rotary + scatter of new K/V rows into cache slots
  *   pa_paged_attention  paged attention (decode and chunked prefill), split-KV when useful
  *   pa_split_combine    log-sum-exp merge of (o, m, l) partials
  *   pa_sparse_forward   fp32 block-sparse "edge" forward emitting (o, m, l) partials
+ *   pa_kv_append_rotate_query  the append plus the same rotation of the new query rows
  *
  * Sources. Argument names and layouts follow three web pages:
  *   [manifest] "com.microsoft.PagedAttention ... manifest.json": the op's inputs, outputs,
@@ -112,6 +113,30 @@ pa_status pa_kv_append(const pa_paged_shape *shape, const void *query, const voi
                        const int32_t *block_table, const int32_t *slot_mapping,
                        const void *cos_cache, const void *sin_cache, int32_t rotary_dim,
                        int32_t rotary_mode, int32_t rotary_positions, void *stream);
+
+/*
+ * pa_kv_append_rotate_query - pa_kv_append, plus every new query row rotated at its position.
+ *
+ * The pages rotate only keys in the append and hand queries to attention already positioned
+ * ([append] rotary macros and main; [manifest] attention binds no cos/sin). This entry applies
+ * the same per-pair rotation, with the same cos/sin rows, to each of the H query head rows of
+ * new token t of sequence b at pos = past_seqlens[b] + t, in the same launch as the key/value
+ * append. Components d >= rotary_dim are copied; with PA_ROTARY_NONE the rows are copied.
+ *   query   required: packed rows (packed_qkv = 1; the Q part is rotated) or fp16 [T, H*D]
+ *   q_out   fp16 [T, H*D], caller-owned, every row written; must not be the query buffer
+ *           (attention then reads q_out with packed_qkv = 0)
+ *   other arguments as pa_kv_append
+ * Errors: as pa_kv_append; PA_ERR_NULL when query or q_out is NULL; PA_ERR_SHAPE when
+ * q_out == query.
+ */
+pa_status pa_kv_append_rotate_query(const pa_paged_shape *shape, const void *query,
+                                    const void *key, const void *value, void *key_cache,
+                                    void *value_cache, const int32_t *cumulative_sequence_length,
+                                    const int32_t *past_seqlens, const int32_t *block_table,
+                                    const int32_t *slot_mapping, const void *cos_cache,
+                                    const void *sin_cache, int32_t rotary_dim,
+                                    int32_t rotary_mode, int32_t rotary_positions, void *q_out,
+                                    void *stream);
 
 /*
  * Bytes of device workspace pa_paged_attention needs for this shape and split policy (an upper

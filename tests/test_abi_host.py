@@ -79,6 +79,21 @@ def test_append_rotary_rules():
     assert _append(_shape(), rotary_dim=64, **rot) == pa.PA_ERR_NULL
 
 
+def test_rotate_query_rules():
+    def rq(shape, **kw):
+        a = dict(query=FAKE, key=FAKE, value=FAKE, key_cache=FAKE, value_cache=FAKE,
+                 cumulative_sequence_length=FAKE, past_seqlens=FAKE, block_table=FAKE,
+                 q_out=FAKE + 4096, stream=0, check=False)
+        a.update(kw)
+        return pa.pa_kv_append_rotate_query(shape, **a)
+    assert rq(_shape(), q_out=None) == pa.PA_ERR_NULL
+    assert rq(_shape(), query=None) == pa.PA_ERR_NULL
+    assert rq(_shape(), q_out=FAKE) == pa.PA_ERR_SHAPE             # rotated rows need own buffer
+    assert rq(_shape(batch=0)) == pa.PA_ERR_SHAPE
+    assert rq(_shape(), value=None) == pa.PA_ERR_SHAPE            # the append's own rules hold
+    assert rq(_shape(num_tokens=0)) == pa.PA_OK
+
+
 def test_empty_append_is_a_no_op():
     assert _append(_shape(num_tokens=0)) == pa.PA_OK
 

@@ -95,6 +95,76 @@ def test_prefill_family(case):
     assert_attention_close(out, ref, "prefill")
 
 
+# Fused query rotation: the key/value append plus q_out, each bit-identical to the oracle.
+QROT = [
+    dict(seed=130, past=[3, 4000, 77, 1], n_new=[1, 1, 1, 1], num_heads=8, kv_num_heads=8,
+         head_size=128, block_size=32, rotary_mode=W.ROTARY_NEOX, rotary_dim=128,
+         rotary_positions=4096, use_slot_mapping=True),                # NeoX on all dims
+    dict(seed=131, past=[3, 900, 77], n_new=[1, 4, 9], num_heads=16, kv_num_heads=8,
+         head_size=128, block_size=32, rotary_mode=W.ROTARY_INTERLEAVED, rotary_dim=128,
+         rotary_positions=1024),                                      # interleaved pairs
+    dict(seed=132, past=[0, 60], n_new=[33, 5], num_heads=32, kv_num_heads=8, head_size=128,
+         block_size=16, packed=True, rotary_mode=W.ROTARY_NEOX, rotary_dim=64,
+         rotary_positions=128),                                       # NeoX on part of the row
+    dict(seed=133, past=[5, 17], n_new=[6, 2], num_heads=6, kv_num_heads=2, head_size=128,
+         block_size=16, rotary_mode=W.ROTARY_NEOX, rotary_dim=48, rotary_positions=64),
+    dict(seed=134, past=[5, 17], n_new=[6, 2], num_heads=4, kv_num_heads=2, head_size=64,
+         block_size=8, packed=True, rotary_mode=W.ROTARY_NEOX, rotary_dim=40,
+         rotary_positions=64),                                        # element-wise path
+    dict(seed=135, past=[9, 2, 30], n_new=[2, 7, 1], num_heads=8, kv_num_heads=1,
+         head_size=64, block_size=16, rotary_mode=W.ROTARY_INTERLEAVED, rotary_dim=36,
+         rotary_positions=64),                                        # element-wise, interleaved
+    dict(seed=136, past=[12, 0], n_new=[3, 5], num_heads=8, kv_num_heads=2, head_size=128,
+         block_size=16, packed=True),                                 # no rotary: copies
+]
+
+
+@pytest.mark.parametrize("case", QROT, ids=lambda c: str(c["seed"]))
+def test_append_rotate_query(case):
+    case = dict(case)
+    sm = case.pop("use_slot_mapping", False)
+    w = W.paged_workload(case.pop("seed"), table="pool", slack=0.2, name="qrot",
+                         use_slot_mapping=sm, **case)
+    kc, vc = oracle.kv_append(w)
+    qref = oracle.rotate_query(w)
+    c = dev.PagedCase(w)
+    q_out = c.append_rotate_query(use_slot_mapping=sm)
+    torch.cuda.synchronize()
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_bits_equal(c.value_cache, vc, "value_cache")
+    assert_bits_equal(q_out, qref, "q_out")
+
+
+def test_append_rotate_query_many_sequences():
+    """300 one-token sequences: cu is searched in LDS instead of in lanes, several tokens per
+    wave."""
+    n = 300
+    w = W.paged_workload(137, past=list(range(5, 5 + n)), n_new=[1] * n, num_heads=4,
+                         kv_num_heads=2, head_size=64, block_size=16, table="pool", slack=0.1,
+                         rotary_mode=W.ROTARY_NEOX, rotary_dim=64, rotary_positions=512,
+                         name="qrot_many")
+    kc, vc = oracle.kv_append(w)
+    qref = oracle.rotate_query(w)
+    c = dev.PagedCase(w)
+    q_out = c.append_rotate_query()
+    torch.cuda.synchronize()
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_bits_equal(q_out, qref, "q_out")
+
+
+def test_append_rotate_query_mixed_full_size(mixed):
+    """The mixed workload (packed rows, NeoX on all dims, derived slots): caches and every rotated
+    query row bit-identical; attention over q_out matches the oracle on the rotated rows."""
+    w = mixed
+    kc, vc = oracle.kv_append(w)
+    qref = oracle.rotate_query(w)
+    c = dev.PagedCase(w)
+    q_out = c.append_rotate_query()
+    torch.cuda.synchronize()
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_bits_equal(q_out, qref, "q_out")
+
+
 def test_append_stress_bit_exact():
     """The append bandwidth workload (65536 packed rows, NeoX rotary on all dims): both caches
     bit-identical to the oracle's, every slot."""
