@@ -232,7 +232,8 @@ def sparse_workload(seed, *, Tq, hkv, qhead, head_dim, block_size, page_size, ba
     ceil(used_b / block_size) with probability p_random (all blocks if all_blocks).
     Edges (q_idx, h, blk, batch, block_len) are sorted by (q_idx, h, blk), with
     block_len = clamp(used_b - blk * block_size, 0, block_size) as the page's host does.
-    group_ptr[q * hkv + h] is the CSR offset of that (q, h) group's first edge.
+    group_ptr[q * hkv + h] is the CSR offset of that (q, h) group's first edge. q_pos[q] is that
+    right-aligned key position (the causal limit when the mask is applied).
     """
     rng = np.random.default_rng(seed)
     ppb = block_size // page_size
@@ -266,6 +267,7 @@ def sparse_workload(seed, *, Tq, hkv, qhead, head_dim, block_size, page_size, ba
             k[:, :nused[b]] = rnd[q, :, :nused[b]]
             k[:, max(0, qb - window + 1):qb + 1] = True
             k[:, 0] = True
+    q_pos = (used[np.arange(Tq) // qpb] - qpb + np.arange(Tq) % qpb).astype(np.int32)
     qi, hi, bi = np.nonzero(keep)          # row-major: already sorted by (q, h, blk)
     bb = qi // qpb
     blen = np.clip(used[bb] - bi * block_size, 0, block_size)
@@ -278,7 +280,7 @@ def sparse_workload(seed, *, Tq, hkv, qhead, head_dim, block_size, page_size, ba
         block_size=block_size, page_size=page_size, pages_per_block=ppb, batch=batch,
         num_pages=num_pages, max_pages=max_pages, used_kv_lens=used.astype(np.int32),
         q_buf=q_buf, k_pages=k_pages, v_pages=v_pages, block_tables=block_tables,
-        edge_meta=edge_meta, group_ptr=group_ptr, E=int(edge_meta.shape[0]),
+        edge_meta=edge_meta, group_ptr=group_ptr, E=int(edge_meta.shape[0]), q_pos=q_pos,
         softmax_scale=float(softmax_scale) if softmax_scale is not None
         else 1.0 / math.sqrt(head_dim),
         causal=0,

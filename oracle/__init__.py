@@ -55,7 +55,7 @@ def _load():
     lib.oracle_paged_attention_partials.restype = None
     lib.oracle_split_combine.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
     lib.oracle_split_combine.restype = None
-    lib.oracle_sparse_forward.argtypes = ([_i] * 7 + [_vp] * 5 + [_d, _vp, _vp, _vp])
+    lib.oracle_sparse_forward.argtypes = ([_i] * 7 + [_vp] * 5 + [_d, _vp, _vp, _vp, _vp])
     lib.oracle_sparse_forward.restype = None
     _lib = lib
     return lib
@@ -190,8 +190,9 @@ def split_combine(o, m, l, *, lanes, head_dim, group_ptr=None, num_groups=None, 
     return out.view(np.float16) if is16 else out
 
 
-def sparse_forward(sw, edge_meta=None, block_tables=None):
-    """Block-sparse edge forward of sparse workload ``sw``. Returns (o [E*qhead, D], m, l)."""
+def sparse_forward(sw, edge_meta=None, block_tables=None, q_pos=None):
+    """Block-sparse edge forward of sparse workload ``sw``. Returns (o [E*qhead, D], m, l).
+    ``q_pos`` (int32 [Tq]) adds the causal mask: key position > q_pos[q_idx] is excluded."""
     lib = _load()
     em = _c(sw["edge_meta"] if edge_meta is None else edge_meta, np.int32)
     bt = _c(sw["block_tables"] if block_tables is None else block_tables, np.int32)
@@ -204,5 +205,6 @@ def sparse_forward(sw, edge_meta=None, block_tables=None):
                               sw["page_size"], sw["max_pages"], _p(_c(sw["q_buf"], np.float32)),
                               _p(_c(sw["k_pages"], np.float32)),
                               _p(_c(sw["v_pages"], np.float32)), _p(em), _p(bt),
-                              float(sw["softmax_scale"]), _p(o), _p(m), _p(l))
+                              float(sw["softmax_scale"]), _p(_c(q_pos, np.int32)), _p(o),
+                              _p(m), _p(l))
     return o, m, l

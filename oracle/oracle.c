@@ -505,12 +505,15 @@ void oracle_split_combine(const float *o_part, const float *m_part, const float 
  * k_pages[pid][h][t % page_size][:] gives s_t = (q . k) * scale. m = max(-1e30, max_t s_t);
  * p_t = exp(s_t - m) when s_t > -5e29, else 0; l = sum_t p_t; o = sum over mapped t with
  * p_t != 0 of p_t * v_t. Results are stored as float32.
+ * q_pos (int32 [Tq], or NULL for no mask) adds the right-aligned causal mask the page lists as
+ * unimplemented: key t of the edge's block is seen only when blk*block_size + t <= q_pos[q_idx].
  */
 void oracle_sparse_forward(int E, int hkv, int qhead, int D, int block_size, int page_size,
                            int max_pages, const float *q_buf, const float *k_pages,
                            const float *v_pages, const int32_t *edge_meta,
                            const int32_t *block_tables, double softmax_scale,
-                           float *o_partial, float *m_partial, float *l_partial)
+                           const int32_t *q_pos, float *o_partial, float *m_partial,
+                           float *l_partial)
 {
     const double NEG_LARGE = (double)-1.0e30f;
     const int hq = hkv * qhead;
@@ -542,7 +545,12 @@ void oracle_sparse_forward(int E, int hkv, int qhead, int D, int block_size, int
                 const int pid = block_tables[(long long)batch * max_pages +
                                              (long long)blk * ppb + t / page_size];
                 double st = NEG_LARGE;
-                if (pid >= 0) {
+                /* causal (the mask the page leaves unimplemented): a key whose absolute position
+                 * blk * block_size + t lies after the query row's position q_pos[q_idx] is
+                 * excluded exactly like a key on an unmapped page */
+                const int visible =
+                    !q_pos || (long long)blk * block_size + t <= (long long)q_pos[q_idx];
+                if (pid >= 0 && visible) {
                     const float *k =
                         k_pages + (((long long)pid * hkv + h) * page_size + t % page_size) * D;
                     double dot = 0.0;

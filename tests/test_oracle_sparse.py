@@ -38,9 +38,10 @@ def _key_position_rows(sw, b, h):
     return K, V, mapped
 
 
-def _dense_reference(sw):
+def _dense_reference(sw, q_pos=None):
     """For each (q, h) group: SDPA over the keys its edges cover (t < block_len of each edge's
-    block) that sit on mapped pages. Returns [Tq, hq, D] float64."""
+    block) that sit on mapped pages (and, with q_pos, at positions <= q_pos[q]). Returns
+    [Tq, hq, D] float64."""
     out = np.zeros((sw["Tq"], sw["hq"], sw["D"]))
     em = sw["edge_meta"]
     gp = sw["group_ptr"]
@@ -59,6 +60,8 @@ def _dense_reference(sw):
             for (_, _, blk, _, blen) in edges:
                 sel[blk * bs: blk * bs + max(0, blen)] = True
             sel &= mapped
+            if q_pos is not None:
+                sel &= np.arange(K.shape[0]) <= q_pos[q]
             if not sel.any():
                 continue
             qv = torch.from_numpy(sw["q_buf"][q, h * sw["qhead"]:(h + 1) * sw["qhead"]]
@@ -144,3 +147,52 @@ def test_partials_are_block_local(oracle):
     rows = np.repeat(~touched, sw["qhead"])
     assert np.array_equal(o[rows], o2[rows]) and np.array_equal(m[rows], m2[rows])
     assert np.array_equal(l[rows], l2[rows])
+
+
+# ------------------------------------------------------------------ right-aligned causal mask
+@pytest.mark.parametrize("all_blocks,unmapped", [(True, 0.0), (True, 0.2), (False, 0.15)])
+def test_causal_merged_equals_dense_causal_attention(oracle, all_blocks, unmapped):
+    """With q_pos the merged partials equal SDPA over the covered, mapped keys at positions
+    <= q_pos[q] (torch, float64)."""
+    sw = _sw(60, all_blocks=all_blocks, unmapped=unmapped)
+    o, m, l = oracle.sparse_forward(sw, q_pos=sw["q_pos"])
+    merged = _merge(oracle, sw, o, m, l).reshape(sw["Tq"], sw["hq"], sw["D"])
+    ref = _dense_reference(sw, q_pos=sw["q_pos"])
+    assert np.allclose(merged, ref, rtol=1e-5, atol=1e-6)
+
+
+def test_causal_far_positions_change_nothing(oracle):
+    sw = _sw(61, all_blocks=True)
+    far = np.full(sw["Tq"], 10 ** 9, dtype=np.int32)
+    a = oracle.sparse_forward(sw)
+    b = oracle.sparse_forward(sw, q_pos=far)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_causal_blocks_after_the_position_give_sentinel(oracle):
+    sw = _sw(62, all_blocks=True)
+    em = sw["edge_meta"]
+    o, m, l = oracle.sparse_forward(sw, q_pos=sw["q_pos"])
+    after = em[:, 2] * sw["block_size"] > sw["q_pos"][em[:, 0]]
+    assert after.any()
+    rows = np.repeat(after, sw["qhead"])
+    assert np.all(o[rows] == 0) and np.all(m[rows] == np.float32(-1e30)) and np.all(l[rows] == 0)
+
+
+def test_causal_equals_block_cut_at_the_position(oracle):
+    """An edge whose block holds the query position gives the same bits as the unmasked edge with
+    block_len cut to q_pos - blk * block_size + 1: the mask is a prefix of the block."""
+    sw = _sw(63, all_blocks=True)
+    em = sw["edge_meta"].copy()
+    qp = sw["q_pos"][em[:, 0]]
+    start = em[:, 2] * sw["block_size"]
+    inside = (qp >= start) & (qp - start + 1 < em[:, 4])
+    assert inside.any()
+    cut = em.copy()
+    cut[inside, 4] = (qp - start + 1)[inside]
+    a = oracle.sparse_forward(sw, q_pos=sw["q_pos"])
+    b = oracle.sparse_forward(sw, edge_meta=cut)
+    rows = np.repeat(inside, sw["qhead"])
+    for x, y in zip(a, b):
+        assert np.array_equal(x[rows], y[rows])
