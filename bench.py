@@ -254,6 +254,14 @@ def run_extra(args, torch, np, pa, dev, W):
     kt = {k: pa.pa_timing_get(k) for k in ("sparse_forward", "combine")}
     pa.pa_timing_reset()
     us = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
+    # the same edges under the right-aligned causal mask
+    pa.pa_timing_reset()
+    pa.pa_timing_enable(True)
+    timed(lambda: s.forward(causal=True), steps, 1, torch)
+    pa.pa_timing_enable(False)
+    t_c = pa.pa_timing_get("sparse_forward")
+    pa.pa_timing_reset()
+    us_causal = t_c[0] / max(1, t_c[1]) * 1e3
     E, q, D = sw["E"], sw["qhead"], sw["D"]
     part_bytes = E * q * (D + 2) * 4
     rows = sw["Tq"] * sw["hq"]
@@ -278,6 +286,7 @@ def run_extra(args, torch, np, pa, dev, W):
         "forward_frac_fp32_mfma": round(flops / (us.get("sparse_forward", 1e9) * 1e-6) / 1e12
                                         / FP32_MFMA_PEAK_TFS, 4),
         "forward_flops": flops,
+        "causal_forward_us": round(us_causal, 2),
     }
     return out
 

@@ -25,6 +25,7 @@ PA_SPLITS_AUTO, PA_SPLITS_PAGE_RULE = 0, -1
 EXPORTED = ("pa_kv_append", "pa_kv_append_rotate_query", "pa_paged_attention_workspace_size",
             "pa_paged_attention",
             "pa_split_combine", "pa_sparse_forward_workspace_size", "pa_sparse_forward",
+            "pa_sparse_forward_causal",
             "pa_status_string", "pa_timing_enable", "pa_timing_reset", "pa_timing_get")
 
 
@@ -80,6 +81,9 @@ def lib():
     L.pa_sparse_forward.argtypes = ([ss] + [_vp] * 5 + [C.c_float, _i32, _vp, C.c_size_t]
                                     + [_vp] * 4)
     L.pa_sparse_forward.restype = _i32
+    L.pa_sparse_forward_causal.argtypes = ([ss] + [_vp] * 6 + [C.c_float, _vp, C.c_size_t]
+                                           + [_vp] * 4)
+    L.pa_sparse_forward_causal.restype = _i32
     L.pa_status_string.argtypes = [_i32]
     L.pa_status_string.restype = C.c_char_p
     L.pa_timing_enable.argtypes = [_i32]
@@ -193,6 +197,16 @@ def pa_sparse_forward(shape, q_buf, k_pages, v_pages, edge_meta, block_tables, s
         float(softmax_scale), int(causal), _p(workspace), int(workspace_bytes), _p(o_partial),
         _p(m_partial), _p(l_partial), _s(stream))
     return _check(st, "pa_sparse_forward", check)
+
+
+def pa_sparse_forward_causal(shape, q_buf, k_pages, v_pages, edge_meta, block_tables, q_pos,
+                             softmax_scale, workspace, workspace_bytes, o_partial, m_partial,
+                             l_partial, stream=None, check=True):
+    st = lib().pa_sparse_forward_causal(
+        C.byref(shape), _p(q_buf), _p(k_pages), _p(v_pages), _p(edge_meta), _p(block_tables),
+        _p(q_pos), float(softmax_scale), _p(workspace), int(workspace_bytes), _p(o_partial),
+        _p(m_partial), _p(l_partial), _s(stream))
+    return _check(st, "pa_sparse_forward_causal", check)
 
 
 def pa_timing_enable(on=True):

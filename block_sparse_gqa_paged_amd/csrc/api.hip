@@ -499,15 +499,14 @@ size_t pa_sparse_forward_workspace_size(const pa_sparse_shape *shape) {
                                   shape->head_dim);
 }
 
-pa_status pa_sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
-                            const float *k_pages, const float *v_pages,
-                            const int32_t *edge_meta, const int32_t *block_tables,
-                            float softmax_scale, int32_t causal, void *workspace,
-                            size_t workspace_bytes, float *o_partial, float *m_partial,
-                            float *l_partial, void *stream) {
+static pa_status sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
+                                const float *k_pages, const float *v_pages,
+                                const int32_t *edge_meta, const int32_t *block_tables,
+                                const int32_t *q_pos, float softmax_scale, void *workspace,
+                                size_t workspace_bytes, float *o_partial, float *m_partial,
+                                float *l_partial, void *stream) {
     pa_status st = check_sparse(shape);
     if (st != PA_OK) return st;
-    if (causal != 0) return PA_ERR_UNSUPPORTED;
     const pa_sparse_shape &s = *shape;
     if (s.num_edges == 0) return PA_OK;
     if (!q_buf || !k_pages || !v_pages || !edge_meta || !block_tables || !o_partial ||
@@ -524,6 +523,7 @@ pa_status pa_sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
     a.vp = v_pages;
     a.edge_meta = edge_meta;
     a.bt = block_tables;
+    a.q_pos = q_pos;
     a.o = o_partial;
     a.m = m_partial;
     a.l = l_partial;
@@ -543,6 +543,34 @@ pa_status pa_sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
     a.nblk = units / (s.batch * s.hkv);
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
     return launch_sparse(a, (hipStream_t)stream);
+}
+
+pa_status pa_sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
+                            const float *k_pages, const float *v_pages,
+                            const int32_t *edge_meta, const int32_t *block_tables,
+                            float softmax_scale, int32_t causal, void *workspace,
+                            size_t workspace_bytes, float *o_partial, float *m_partial,
+                            float *l_partial, void *stream) {
+    pa_status st = check_sparse(shape);
+    if (st != PA_OK) return st;
+    if (causal != 0) return PA_ERR_UNSUPPORTED;  // the mask needs positions: the causal entry
+    return sparse_forward(shape, q_buf, k_pages, v_pages, edge_meta, block_tables, nullptr,
+                          softmax_scale, workspace, workspace_bytes, o_partial, m_partial,
+                          l_partial, stream);
+}
+
+pa_status pa_sparse_forward_causal(const pa_sparse_shape *shape, const float *q_buf,
+                                   const float *k_pages, const float *v_pages,
+                                   const int32_t *edge_meta, const int32_t *block_tables,
+                                   const int32_t *q_pos, float softmax_scale, void *workspace,
+                                   size_t workspace_bytes, float *o_partial, float *m_partial,
+                                   float *l_partial, void *stream) {
+    pa_status st = check_sparse(shape);
+    if (st != PA_OK) return st;
+    if (shape->num_edges > 0 && !q_pos) return PA_ERR_NULL;
+    return sparse_forward(shape, q_buf, k_pages, v_pages, edge_meta, block_tables, q_pos,
+                          softmax_scale, workspace, workspace_bytes, o_partial, m_partial,
+                          l_partial, stream);
 }
 
 }  // extern "C"

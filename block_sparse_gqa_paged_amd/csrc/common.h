@@ -182,6 +182,7 @@ struct SparseArgs {
     float *o;
     float *m;
     float *l;
+    const int32_t *q_pos;  // key position of each query row (causal limit), or NULL
     int32_t *ws;  // workspace (int32 words)
     int E, tq, hkv, qhead, D, block_size, page_size, ppb, max_pages, batch, num_pages;
     int units;    // batch * hkv * nblk

@@ -27,6 +27,8 @@
 //    an edge reads its rows ready for the MFMA, and the item's edge list sits in LDS.
 //
 // Edges whose batch, head, block or query index lie outside the shapes write the sentinel.
+// With q_pos (the causal entry), an edge sees only keys at positions <= q_pos[q_idx]: its length
+// is cut to that prefix when the item's edge list is staged.
 #include "common.h"
 
 namespace pa {
@@ -234,7 +236,10 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
         const int e = w.perm[ebeg + threadIdx.x];
         s_e[threadIdx.x] = e;
         s_q[threadIdx.x] = a.edge_meta[5LL * e];
-        s_len[threadIdx.x] = min(a.edge_meta[5LL * e + 4], a.block_size);
+        int len = min(a.edge_meta[5LL * e + 4], a.block_size);
+        // causal: keys at positions after the query row's are cut off (a prefix stays)
+        if (a.q_pos) len = min(len, a.q_pos[s_q[threadIdx.x]] - blk * a.block_size + 1);
+        s_len[threadIdx.x] = len;
     }
 
     auto page_of = [&](int t) {

@@ -9,7 +9,7 @@ import torch
 
 from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, pa_kv_append, pa_kv_append_rotate_query,
                pa_paged_attention,
-               pa_paged_attention_workspace_size, pa_sparse_forward,
+               pa_paged_attention_workspace_size, pa_sparse_forward, pa_sparse_forward_causal,
                pa_sparse_forward_workspace_size, pa_split_combine, paged_shape, sparse_shape)
 
 
@@ -113,12 +113,22 @@ class SparseCase:
         n = pa_sparse_forward_workspace_size(self.shape)
         self.ws = workspace(n, device)
         self.ws_bytes = n
+        self.q_pos = None
 
-    def forward(self, stream=None):
+    def forward(self, causal=False, stream=None):
+        """Partials of every edge; causal=True masks keys past each row's q_pos."""
         sw = self.sw
-        pa_sparse_forward(self.shape, self.q, self.k, self.v, self.edge_meta, self.block_tables,
-                          sw["softmax_scale"], 0, self.ws, self.ws_bytes, self.o, self.m, self.l,
-                          stream=stream)
+        if causal:
+            if self.q_pos is None:
+                self.q_pos = to_dev(sw["q_pos"], self.device)
+            pa_sparse_forward_causal(self.shape, self.q, self.k, self.v, self.edge_meta,
+                                     self.block_tables, self.q_pos, sw["softmax_scale"],
+                                     self.ws, self.ws_bytes, self.o, self.m, self.l,
+                                     stream=stream)
+        else:
+            pa_sparse_forward(self.shape, self.q, self.k, self.v, self.edge_meta,
+                              self.block_tables, sw["softmax_scale"], 0, self.ws, self.ws_bytes,
+                              self.o, self.m, self.l, stream=stream)
         return self.o, self.m, self.l
 
     def combine(self, out_dtype=PA_F32, out=None, stream=None):

@@ -7,6 +7,7 @@
  *   pa_split_combine    log-sum-exp merge of (o, m, l) partials
  *   pa_sparse_forward   fp32 block-sparse "edge" forward emitting (o, m, l) partials
  *   pa_kv_append_rotate_query  the append plus the same rotation of the new query rows
+ *   pa_sparse_forward_causal   the sparse forward with a per-row causal key limit
  *
  * Sources. Argument names and layouts follow three web pages:
  *   [manifest] "com.microsoft.PagedAttention ... manifest.json": the op's inputs, outputs,
@@ -239,7 +240,8 @@ size_t pa_sparse_forward_workspace_size(const pa_sparse_shape *shape);
  * block_len <= 0 or no mapped key writes the sentinel o = 0, m = -1e30, l = 0.
  *   q_buf   f32 [tq, hkv*qhead, D];  k_pages, v_pages  f32 [num_pages, hkv, page_size, D]
  *   edge_meta int32 [E, 5];  block_tables int32 [batch, max_pages]
- *   causal  must be 0: the page leaves the right-aligned causal mask unimplemented
+ *   causal  must be 0: the page leaves the right-aligned causal mask unimplemented (the mask
+ *           needs each row's key position: pa_sparse_forward_causal)
  *   workspace  at least pa_sparse_forward_workspace_size(shape) bytes, 256-byte aligned
  * Edges may come in any order; the kernel groups them by (batch, h, blk) so each block of keys
  * is read once per group. Merge the partials with pa_split_combine.
@@ -252,6 +254,24 @@ pa_status pa_sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
                             float softmax_scale, int32_t causal, void *workspace,
                             size_t workspace_bytes, float *o_partial, float *m_partial,
                             float *l_partial, void *stream);
+
+/*
+ * pa_sparse_forward_causal - pa_sparse_forward with the right-aligned causal mask that the
+ * [sparse] page lists as unimplemented (its header: the host must set causal = 0).
+ *
+ * q_pos  int32 [tq]: the absolute key position of each query row; key t of an edge's block is
+ *        seen only when blk*block_size + t <= q_pos[q_idx], otherwise it is excluded like a key
+ *        on an unmapped page. Right-aligned rows of a batch with Tq_b rows and used_b keys have
+ *        q_pos = used_b - Tq_b + j for row j. An edge with no key left writes the sentinel.
+ * Other arguments, layouts and the workspace size are those of pa_sparse_forward.
+ * Errors: as pa_sparse_forward; PA_ERR_NULL when q_pos is NULL and num_edges > 0.
+ */
+pa_status pa_sparse_forward_causal(const pa_sparse_shape *shape, const float *q_buf,
+                                   const float *k_pages, const float *v_pages,
+                                   const int32_t *edge_meta, const int32_t *block_tables,
+                                   const int32_t *q_pos, float softmax_scale, void *workspace,
+                                   size_t workspace_bytes, float *o_partial, float *m_partial,
+                                   float *l_partial, void *stream);
 
 /* Static description of a status code. */
 const char *pa_status_string(pa_status status);

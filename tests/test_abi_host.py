@@ -183,6 +183,17 @@ def test_sparse_rejects_bad_arguments():
     assert fwd(sh(), edge_meta=None) == pa.PA_ERR_NULL
     assert fwd(sh(), workspace_bytes=8) == pa.PA_ERR_WORKSPACE
     assert fwd(sh(num_edges=0), q_buf=None) == pa.PA_OK
+
+    def cfwd(shape, **kw):
+        a = dict(q_buf=FAKE, k_pages=FAKE, v_pages=FAKE, edge_meta=FAKE, block_tables=FAKE,
+                 q_pos=FAKE, softmax_scale=0.1, workspace=FAKE, workspace_bytes=0,
+                 o_partial=FAKE, m_partial=FAKE, l_partial=FAKE, stream=0, check=False)
+        a.update(kw)
+        return pa.pa_sparse_forward_causal(shape, **a)
+    assert cfwd(sh(), q_pos=None) == pa.PA_ERR_NULL            # the mask needs positions
+    assert cfwd(sh(block_size=60)) == pa.PA_ERR_SHAPE
+    assert cfwd(sh(), workspace_bytes=8) == pa.PA_ERR_WORKSPACE
+    assert cfwd(sh(num_edges=0), q_pos=None) == pa.PA_OK
     assert pa.pa_sparse_forward_workspace_size(sh()) > 0
     assert pa.pa_sparse_forward_workspace_size(sh(hkv=0)) == 0
 

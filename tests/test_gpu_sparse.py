@@ -54,6 +54,22 @@ def test_tiny_partials_and_merge(case):
     assert_sparse_out_close(out, merged, "merged")
 
 
+@pytest.mark.parametrize("case", TINY[:4] + TINY[5:], ids=lambda c: str(c["seed"]))
+def test_tiny_causal_partials_and_merge(case):
+    """Right-aligned causal mask: partials and merged rows against the oracle with q_pos."""
+    case = dict(case)
+    sw = _tiny(case.pop("seed"), **case)
+    ref = oracle.sparse_forward(sw, q_pos=sw["q_pos"])
+    c = dev.SparseCase(sw)
+    got = c.forward(causal=True)
+    out = c.combine()
+    torch.cuda.synchronize()
+    assert_sparse_partials_close(got, ref, "causal partials")
+    merged = oracle.split_combine(*ref, lanes=sw["qhead"], head_dim=sw["D"],
+                                  group_ptr=sw["group_ptr"], out_dtype=np.float32)
+    assert_sparse_out_close(out, merged, "causal merged")
+
+
 def test_sentinels_and_out_of_range_edges():
     sw = _tiny(210)
     em = sw["edge_meta"].copy()
@@ -98,15 +114,14 @@ def full():
     return sw, o.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy(), out.cpu().numpy()
 
 
-def test_full_size_sampled_groups(full):
-    sw, o, m, l, out = full
+def _check_sampled_groups(sw, o, m, l, out, q_pos=None):
     G = sw["Tq"] * sw["hkv"]
     groups = np.random.default_rng(7).choice(G, size=96, replace=False)
     groups.sort()
     gp = sw["group_ptr"]
     edges = np.concatenate([np.arange(gp[g], gp[g + 1]) for g in groups])
     sub_gp = np.concatenate([[0], np.cumsum(gp[groups + 1] - gp[groups])]).astype(np.int32)
-    ro, rm, rl = oracle.sparse_forward(sw, edge_meta=sw["edge_meta"][edges])
+    ro, rm, rl = oracle.sparse_forward(sw, edge_meta=sw["edge_meta"][edges], q_pos=q_pos)
     q = sw["qhead"]
     prow = (edges[:, None] * q + np.arange(q)[None, :]).reshape(-1)
     assert_sparse_partials_close((o[prow], m[prow], l[prow]), (ro, rm, rl), "sampled partials")
@@ -114,6 +129,22 @@ def test_full_size_sampled_groups(full):
                                   out_dtype=np.float32)
     orow = (groups[:, None] * q + np.arange(q)[None, :]).reshape(-1)
     assert_sparse_out_close(out[orow], merged, "sampled merged rows")
+
+
+def test_full_size_sampled_groups(full):
+    _check_sampled_groups(*full)
+
+
+def test_full_size_causal_sampled_groups(full):
+    """The same workload under the right-aligned causal mask (its random blocks past a row's
+    position become sentinels, the row's own block is cut at the position)."""
+    sw = full[0]
+    c = dev.SparseCase(sw)
+    o, m, l = c.forward(causal=True)
+    out = c.combine()
+    torch.cuda.synchronize()
+    _check_sampled_groups(sw, o.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy(),
+                          out.cpu().numpy(), q_pos=sw["q_pos"])
 
 
 def test_full_size_invariants(full):
