@@ -233,7 +233,9 @@ def sparse_workload(seed, *, Tq, hkv, qhead, head_dim, block_size, page_size, ba
     Edges (q_idx, h, blk, batch, block_len) are sorted by (q_idx, h, blk), with
     block_len = clamp(used_b - blk * block_size, 0, block_size) as the page's host does.
     group_ptr[q * hkv + h] is the CSR offset of that (q, h) group's first edge. q_pos[q] is that
-    right-aligned key position (the causal limit when the mask is applied).
+    right-aligned key position (the causal limit when the mask is applied). block_mask
+    [Tq, hkv, nblk] (uint8) and q_batch [Tq] are the kept-block mask and each row's batch, the
+    inputs an edge-list builder turns into edge_meta and group_ptr.
     """
     rng = np.random.default_rng(seed)
     ppb = block_size // page_size
@@ -281,6 +283,8 @@ def sparse_workload(seed, *, Tq, hkv, qhead, head_dim, block_size, page_size, ba
         num_pages=num_pages, max_pages=max_pages, used_kv_lens=used.astype(np.int32),
         q_buf=q_buf, k_pages=k_pages, v_pages=v_pages, block_tables=block_tables,
         edge_meta=edge_meta, group_ptr=group_ptr, E=int(edge_meta.shape[0]), q_pos=q_pos,
+        block_mask=keep.astype(np.uint8), q_batch=(np.arange(Tq) // qpb).astype(np.int32),
+        nblk=nblk,
         softmax_scale=float(softmax_scale) if softmax_scale is not None
         else 1.0 / math.sqrt(head_dim),
         causal=0,

@@ -47,6 +47,8 @@ def _load():
     lib.oracle_kv_append.restype = None
     lib.oracle_rotate_query.argtypes = [_i] * 5 + [_vp] * 5 + [_i, _i, _vp]
     lib.oracle_rotate_query.restype = None
+    lib.oracle_build_edges.argtypes = [_i] * 4 + [_vp] * 5
+    lib.oracle_build_edges.restype = None
     lib.oracle_paged_attention.argtypes = ([_i] * 7 + [_vp, _ll, _vp, _vp, _vp, _vp, _vp, _d, _i,
                                                        _vp])
     lib.oracle_paged_attention.restype = None
@@ -133,6 +135,20 @@ def rotate_query(w, rotary_mode=None, rotary_dim=None):
                             int(w["rotary_mode"] if rotary_mode is None else rotary_mode),
                             _p(out))
     return out.view(np.float16)
+
+
+def build_edges(mask, q_batch, used_kv_lens, block_size):
+    """Edge list from a kept-block mask [tq, hkv, nblk]: (edge_meta [E, 5] int32,
+    group_ptr [tq*hkv + 1] int32)."""
+    lib = _load()
+    mk = np.ascontiguousarray(mask != 0, dtype=np.uint8)
+    tq, hkv, nblk = mk.shape
+    E = int(mk.sum())
+    em = np.zeros((max(E, 1), 5), dtype=np.int32)
+    gp = np.zeros(tq * hkv + 1, dtype=np.int32)
+    lib.oracle_build_edges(tq, hkv, nblk, int(block_size), _p(mk), _p(_c(q_batch, np.int32)),
+                           _p(_c(used_kv_lens, np.int32)), _p(em), _p(gp))
+    return em[:E], gp
 
 
 def _q_stride(w):

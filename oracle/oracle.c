@@ -262,6 +262,42 @@ void oracle_rotate_query(int B, int H, int G, int D, int packed, const uint16_t 
     }
 }
 
+/* Edge list of the block-sparse forward from a kept-block mask (the [sparse] page's host step:
+ * block_len from used_kv_lens clamped by the block). Rows (q, h) are taken in order, blocks in
+ * order within a row; every nonzero mask[q][h][blk] gives edge (q, h, blk, b, block_len) with
+ * b = q_batch[q] and block_len = clamp(used_kv_lens[b] - blk*block_size, 0, block_size).
+ * group_ptr[q*hkv + h] is the index of the row's first edge, group_ptr[tq*hkv] the edge count.
+ * edge_meta must hold as many edges as the mask has nonzero entries. */
+void oracle_build_edges(int tq, int hkv, int nblk, int block_size, const uint8_t *mask,
+                        const int32_t *q_batch, const int32_t *used_kv_lens, int32_t *edge_meta,
+                        int32_t *group_ptr)
+{
+    long long e = 0;
+    for (int q = 0; q < tq; ++q) {
+        const int b = q_batch[q];
+        for (int h = 0; h < hkv; ++h) {
+            group_ptr[(long long)q * hkv + h] = (int32_t)e;
+            for (int blk = 0; blk < nblk; ++blk) {
+                if (!mask[((long long)q * hkv + h) * nblk + blk])
+                    continue;
+                long long len = (long long)used_kv_lens[b] - (long long)blk * block_size;
+                if (len < 0)
+                    len = 0;
+                if (len > block_size)
+                    len = block_size;
+                int32_t *m = edge_meta + 5 * e;
+                m[0] = q;
+                m[1] = h;
+                m[2] = blk;
+                m[3] = b;
+                m[4] = (int32_t)len;
+                ++e;
+            }
+        }
+    }
+    group_ptr[(long long)tq * hkv] = (int32_t)e;
+}
+
 /* ---------------------------------------------------------------------------------------- */
 /* Paged attention: gather to contiguous, then dense softmax attention.                      */
 /* ---------------------------------------------------------------------------------------- */

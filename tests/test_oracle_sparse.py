@@ -196,3 +196,42 @@ def test_causal_equals_block_cut_at_the_position(oracle):
     rows = np.repeat(inside, sw["qhead"])
     for x, y in zip(a, b):
         assert np.array_equal(x[rows], y[rows])
+
+
+# ------------------------------------------------------------------ edge-list builder
+@pytest.mark.parametrize("all_blocks", [False, True])
+def test_built_edges_equal_the_generators(oracle, all_blocks):
+    """The generator forms its edges with numpy (nonzero of the mask in row-major order, block_len
+    clipped by numpy); the oracle's loop gives the same list and CSR offsets."""
+    sw = _sw(70, all_blocks=all_blocks, Tq=20, key_capacity=160)
+    em, gp = oracle.build_edges(sw["block_mask"], sw["q_batch"], sw["used_kv_lens"],
+                                sw["block_size"])
+    assert np.array_equal(em, sw["edge_meta"])
+    assert np.array_equal(gp, sw["group_ptr"])
+
+
+def test_built_edges_counts_and_lengths(oracle):
+    rng = np.random.default_rng(71)
+    tq, hkv, nblk, bs = 7, 3, 11, 16
+    mask = (rng.random((tq, hkv, nblk)) < 0.4).astype(np.uint8)
+    mask[2] = 0                                    # a row with no edge at all
+    q_batch = rng.integers(0, 2, size=tq).astype(np.int32)
+    used = np.array([5 * bs + 3, 0], dtype=np.int32)   # batch 1 has no keys
+    em, gp = oracle.build_edges(mask, q_batch, used, bs)
+    assert np.array_equal(np.diff(gp), mask.reshape(tq * hkv, nblk).sum(axis=1))
+    assert gp[-1] == len(em) == int(mask.sum())
+    blk, b, blen = em[:, 2], em[:, 3], em[:, 4]
+    assert np.array_equal(b, q_batch[em[:, 0]])
+    assert np.all(blen[b == 1] == 0)
+    full = (b == 0) & (blk < 5)
+    assert np.all(blen[full] == bs) and np.all(blen[(b == 0) & (blk == 5)] == 3)
+    assert np.all(blen[(b == 0) & (blk > 5)] == 0)
+    # sorted by (q, h, blk)
+    key = (em[:, 0].astype(np.int64) * hkv + em[:, 1]) * nblk + blk
+    assert np.all(np.diff(key) > 0)
+
+
+def test_built_edges_empty_mask(oracle):
+    em, gp = oracle.build_edges(np.zeros((4, 2, 5), np.uint8), np.zeros(4, np.int32),
+                                np.array([70], np.int32), 16)
+    assert len(em) == 0 and np.all(gp == 0)
