@@ -254,6 +254,17 @@ def run_extra(args, torch, np, pa, dev, W):
     kt = {k: pa.pa_timing_get(k) for k in ("sparse_forward", "combine")}
     pa.pa_timing_reset()
     us = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
+    # the edge list itself, built on the device from the kept-block mask
+    eb = dev.EdgeBuilder(sw)
+    pa.pa_timing_reset()
+    pa.pa_timing_enable(True)
+    timed(eb.build, steps, 1, torch)
+    pa.pa_timing_enable(False)
+    t_e = pa.pa_timing_get("build_edges")
+    pa.pa_timing_reset()
+    us_edges = t_e[0] / max(1, t_e[1]) * 1e3
+    edge_bytes = sw["block_mask"].size + sw["E"] * 20 + (sw["Tq"] * sw["hkv"] + 1) * 4
+    del eb
     # the same edges under the right-aligned causal mask
     pa.pa_timing_reset()
     pa.pa_timing_enable(True)
@@ -287,6 +298,8 @@ def run_extra(args, torch, np, pa, dev, W):
                                         / FP32_MFMA_PEAK_TFS, 4),
         "forward_flops": flops,
         "causal_forward_us": round(us_causal, 2),
+        "build_edges_us": round(us_edges, 2), "build_edges_bytes": edge_bytes,
+        "build_edges_GBps": round(edge_bytes / (us_edges * 1e-6) / 1e9, 1),
     }
     return out
 

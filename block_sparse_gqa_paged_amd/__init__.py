@@ -25,7 +25,8 @@ PA_SPLITS_AUTO, PA_SPLITS_PAGE_RULE = 0, -1
 EXPORTED = ("pa_kv_append", "pa_kv_append_rotate_query", "pa_paged_attention_workspace_size",
             "pa_paged_attention",
             "pa_split_combine", "pa_sparse_forward_workspace_size", "pa_sparse_forward",
-            "pa_sparse_forward_causal",
+            "pa_sparse_forward_causal", "pa_sparse_build_edges_workspace_size",
+            "pa_sparse_build_edges",
             "pa_status_string", "pa_timing_enable", "pa_timing_reset", "pa_timing_get")
 
 
@@ -84,6 +85,11 @@ def lib():
     L.pa_sparse_forward_causal.argtypes = ([ss] + [_vp] * 6 + [C.c_float, _vp, C.c_size_t]
                                            + [_vp] * 4)
     L.pa_sparse_forward_causal.restype = _i32
+    L.pa_sparse_build_edges_workspace_size.argtypes = [_i32, _i32]
+    L.pa_sparse_build_edges_workspace_size.restype = C.c_size_t
+    L.pa_sparse_build_edges.argtypes = ([_i32] * 5 + [_vp] * 3 + [C.c_int64, _vp, _vp, _vp,
+                                        C.c_size_t, _vp])
+    L.pa_sparse_build_edges.restype = _i32
     L.pa_status_string.argtypes = [_i32]
     L.pa_status_string.restype = C.c_char_p
     L.pa_timing_enable.argtypes = [_i32]
@@ -207,6 +213,20 @@ def pa_sparse_forward_causal(shape, q_buf, k_pages, v_pages, edge_meta, block_ta
         _p(q_pos), float(softmax_scale), _p(workspace), int(workspace_bytes), _p(o_partial),
         _p(m_partial), _p(l_partial), _s(stream))
     return _check(st, "pa_sparse_forward_causal", check)
+
+
+def pa_sparse_build_edges_workspace_size(tq, hkv):
+    return int(lib().pa_sparse_build_edges_workspace_size(int(tq), int(hkv)))
+
+
+def pa_sparse_build_edges(tq, hkv, nblk, block_size, batch, block_mask, q_batch, used_kv_lens,
+                          edge_capacity, edge_meta, group_ptr, workspace, workspace_bytes,
+                          stream=None, check=True):
+    st = lib().pa_sparse_build_edges(
+        int(tq), int(hkv), int(nblk), int(block_size), int(batch), _p(block_mask), _p(q_batch),
+        _p(used_kv_lens), int(edge_capacity), _p(edge_meta), _p(group_ptr), _p(workspace),
+        int(workspace_bytes), _s(stream))
+    return _check(st, "pa_sparse_build_edges", check)
 
 
 def pa_timing_enable(on=True):

@@ -573,4 +573,40 @@ pa_status pa_sparse_forward_causal(const pa_sparse_shape *shape, const float *q_
                           l_partial, stream);
 }
 
+size_t pa_sparse_build_edges_workspace_size(int32_t tq, int32_t hkv) {
+    if (tq < 0 || hkv < 1) return 0;
+    return std::max<size_t>(256, edge_workspace_bytes((long long)tq * hkv));
+}
+
+pa_status pa_sparse_build_edges(int32_t tq, int32_t hkv, int32_t nblk, int32_t block_size,
+                                int32_t batch, const uint8_t *block_mask,
+                                const int32_t *q_batch, const int32_t *used_kv_lens,
+                                int64_t edge_capacity, int32_t *edge_meta, int32_t *group_ptr,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    if (tq < 0 || hkv < 1 || nblk < 1 || block_size < 1 || batch < 1 || edge_capacity < 0)
+        return PA_ERR_SHAPE;
+    const long long rows = (long long)tq * hkv;
+    if (rows * nblk >= (1LL << 31)) return PA_ERR_UNSUPPORTED;  // int32 edge offsets
+    if (!group_ptr || !workspace) return PA_ERR_NULL;
+    if (rows > 0 && (!block_mask || !q_batch || !used_kv_lens)) return PA_ERR_NULL;
+    if (edge_capacity > 0 && !edge_meta) return PA_ERR_NULL;
+    if (workspace_bytes < pa_sparse_build_edges_workspace_size(tq, hkv) ||
+        ((uintptr_t)workspace % 256) != 0)
+        return PA_ERR_WORKSPACE;
+    EdgeArgs a;
+    a.mask = block_mask;
+    a.q_batch = q_batch;
+    a.used = used_kv_lens;
+    a.edge_meta = edge_meta;
+    a.group_ptr = group_ptr;
+    a.wg = (int32_t *)workspace;
+    a.rows = rows;
+    a.capacity = edge_capacity;
+    a.hkv = hkv;
+    a.nblk = nblk;
+    a.block_size = block_size;
+    a.batch = batch;
+    return launch_build_edges(a, (hipStream_t)stream);
+}
+
 }  // extern "C"

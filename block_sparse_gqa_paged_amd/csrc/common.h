@@ -190,6 +190,21 @@ struct SparseArgs {
     float scale_log2;
 };
 pa_status launch_sparse(const SparseArgs &a, hipStream_t stream);
+
+// Edge list of the block-sparse forward from a kept-block mask.
+struct EdgeArgs {
+    const uint8_t *mask;     // [tq, hkv, nblk], nonzero = keep
+    const int32_t *q_batch;  // [tq]
+    const int32_t *used;     // used_kv_lens [batch]
+    int32_t *edge_meta;      // [capacity, 5]
+    int32_t *group_ptr;      // [tq * hkv + 1]
+    int32_t *wg;             // workspace: per-workgroup totals, then offsets
+    long long rows;          // tq * hkv
+    long long capacity;      // edges edge_meta can hold
+    int hkv, nblk, block_size, batch;
+};
+pa_status launch_build_edges(const EdgeArgs &a, hipStream_t stream);
+size_t edge_workspace_bytes(long long rows);
 size_t sparse_workspace_bytes(int E, int units, long long qrows, int D);
 
 // ---------------------------------------------------------------------------------------------

@@ -9,7 +9,8 @@ import torch
 
 from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, pa_kv_append, pa_kv_append_rotate_query,
                pa_paged_attention,
-               pa_paged_attention_workspace_size, pa_sparse_forward, pa_sparse_forward_causal,
+               pa_paged_attention_workspace_size, pa_sparse_build_edges,
+               pa_sparse_build_edges_workspace_size, pa_sparse_forward, pa_sparse_forward_causal,
                pa_sparse_forward_workspace_size, pa_split_combine, paged_shape, sparse_shape)
 
 
@@ -137,6 +138,32 @@ class SparseCase:
         pa_split_combine(self.o, self.m, self.l, self.group_ptr, sw["Tq"] * sw["hkv"],
                          sw["qhead"], 0, sw["D"], out_dtype, out, stream=stream)
         return out
+
+
+class EdgeBuilder:
+    """A sparse workload's kept-block mask on the device, turned into (edge_meta, group_ptr)."""
+
+    def __init__(self, sw, capacity=None, device="cuda"):
+        self.sw = sw
+        self.mask = to_dev(np.ascontiguousarray(sw["block_mask"], dtype=np.uint8), device)
+        self.q_batch = to_dev(sw["q_batch"].astype(np.int32), device)
+        self.used = to_dev(sw["used_kv_lens"].astype(np.int32), device)
+        tq, hkv, nblk = sw["block_mask"].shape
+        self.dims = (tq, hkv, nblk)
+        self.capacity = tq * hkv * nblk if capacity is None else capacity
+        self.edge_meta = torch.empty((max(1, self.capacity), 5), dtype=torch.int32,
+                                     device=device)
+        self.group_ptr = torch.empty(tq * hkv + 1, dtype=torch.int32, device=device)
+        n = pa_sparse_build_edges_workspace_size(tq, hkv)
+        self.ws = workspace(n, device)
+        self.ws_bytes = n
+
+    def build(self, stream=None):
+        tq, hkv, nblk = self.dims
+        pa_sparse_build_edges(tq, hkv, nblk, self.sw["block_size"], self.sw["batch"], self.mask,
+                              self.q_batch, self.used, self.capacity, self.edge_meta,
+                              self.group_ptr, self.ws, self.ws_bytes, stream=stream)
+        return self.edge_meta, self.group_ptr
 
 
 def combine(o, m, l, *, lanes, head_dim, group_ptr=None, num_groups=None, num_splits=0,

@@ -8,6 +8,7 @@
  *   pa_sparse_forward   fp32 block-sparse "edge" forward emitting (o, m, l) partials
  *   pa_kv_append_rotate_query  the append plus the same rotation of the new query rows
  *   pa_sparse_forward_causal   the sparse forward with a per-row causal key limit
+ *   pa_sparse_build_edges      the sparse forward's edge list from a kept-block mask
  *
  * Sources. Argument names and layouts follow three web pages:
  *   [manifest] "com.microsoft.PagedAttention ... manifest.json": the op's inputs, outputs,
@@ -272,6 +273,36 @@ pa_status pa_sparse_forward_causal(const pa_sparse_shape *shape, const float *q_
                                    const int32_t *q_pos, float softmax_scale, void *workspace,
                                    size_t workspace_bytes, float *o_partial, float *m_partial,
                                    float *l_partial, void *stream);
+
+/*
+ * pa_sparse_build_edges - the edge list of pa_sparse_forward, built on the device from a mask.
+ *
+ * The [sparse] page's host prepares edge_meta on the CPU (its layout notes: block_len computed
+ * from used_kv_lens, clamped by the block). Rows (q, h) are taken in order and blocks in order
+ * within a row; every nonzero block_mask[q][h][blk] gives the edge
+ *   (q, h, blk, b = q_batch[q], block_len = clamp(used_kv_lens[b] - blk*block_size, 0, block_size))
+ * and group_ptr[q*hkv + h] is the index of row (q, h)'s first edge; group_ptr[tq*hkv] is the edge
+ * count E. The list is sorted by (q_idx, h, blk) and group_ptr is the CSR offset array that
+ * pa_split_combine takes to merge each row's partials.
+ *   block_mask    uint8 [tq, hkv, nblk], nonzero = keep
+ *   q_batch       int32 [tq], the batch of each query row (an entry outside [0, batch) is
+ *                 written as given and reads used_kv_lens of a clamped index)
+ *   used_kv_lens  int32 [batch]
+ *   edge_meta     int32 [edge_capacity, 5]: edges with index >= edge_capacity are not written
+ *                 (E is still counted: read group_ptr[tq*hkv] to size the forward)
+ *   group_ptr     int32 [tq*hkv + 1]
+ *   workspace     pa_sparse_build_edges_workspace_size(tq, hkv) bytes, 256-byte aligned
+ * The edge count lives in device memory: the caller reads it back before sizing
+ * pa_sparse_forward's num_edges.
+ * Errors: PA_ERR_SHAPE (negative sizes), PA_ERR_UNSUPPORTED (tq*hkv*nblk >= 2^31),
+ * PA_ERR_NULL, PA_ERR_WORKSPACE, PA_ERR_HIP.
+ */
+size_t pa_sparse_build_edges_workspace_size(int32_t tq, int32_t hkv);
+pa_status pa_sparse_build_edges(int32_t tq, int32_t hkv, int32_t nblk, int32_t block_size,
+                                int32_t batch, const uint8_t *block_mask,
+                                const int32_t *q_batch, const int32_t *used_kv_lens,
+                                int64_t edge_capacity, int32_t *edge_meta, int32_t *group_ptr,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *pa_status_string(pa_status status);

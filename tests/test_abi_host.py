@@ -202,3 +202,24 @@ def test_status_strings():
     for s in range(6):
         assert pa.status_string(s)
     assert "unknown" in pa.status_string(99)
+
+
+def test_build_edges_rejects_bad_arguments():
+    def be(**kw):
+        a = dict(tq=4, hkv=2, nblk=8, block_size=16, batch=1, block_mask=FAKE, q_batch=FAKE,
+                 used_kv_lens=FAKE, edge_capacity=64, edge_meta=FAKE, group_ptr=FAKE,
+                 workspace=FAKE, workspace_bytes=1 << 20, stream=0, check=False)
+        a.update(kw)
+        return pa.pa_sparse_build_edges(**a)
+    assert be(tq=-1) == pa.PA_ERR_SHAPE
+    assert be(hkv=0) == pa.PA_ERR_SHAPE
+    assert be(nblk=0) == pa.PA_ERR_SHAPE
+    assert be(edge_capacity=-1) == pa.PA_ERR_SHAPE
+    assert be(tq=1 << 20, hkv=64, nblk=64) == pa.PA_ERR_UNSUPPORTED   # >= 2^31 mask entries
+    assert be(group_ptr=None) == pa.PA_ERR_NULL
+    assert be(block_mask=None) == pa.PA_ERR_NULL
+    assert be(edge_meta=None) == pa.PA_ERR_NULL
+    assert be(workspace_bytes=4) == pa.PA_ERR_WORKSPACE
+    assert be(workspace=FAKE + 4) == pa.PA_ERR_WORKSPACE
+    assert pa.pa_sparse_build_edges_workspace_size(4, 2) >= 256
+    assert pa.pa_sparse_build_edges_workspace_size(-1, 2) == 0
