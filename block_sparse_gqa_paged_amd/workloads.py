@@ -213,6 +213,54 @@ def append_stress(seed=5):
     return mixed_prefill_decode(seed, prefill_tokens=8192, n_prefill=8, n_decode=0)
 
 
+def bnsh_workload(seed, *, batch, seq_len, num_heads, kv_num_heads, head_size, max_seq,
+                  key_total, total_seq=None, packed=False, rotary_mode=ROTARY_NONE,
+                  rotary_dim=None, rotary_positions=None, theta=10000.0, name="bnsh"):
+    """The append page's own layout: new rows in a padded batch [B, seq_len] and a contiguous
+    BNSH cache [B, KVH, max_seq, D] (present_key / present_value, filled with N(0,1)).
+
+    key_total: per-batch total sequence lengths (a list, or a callable of the generator);
+    total_seq: the scalar total_sequence_length (defaults to max(key_total); equal to seq_len
+    makes the call a prompt, where every row's past length is 0).
+    Draw order: key_total (when callable); present_key; present_value; the new rows.
+    """
+    rng = np.random.default_rng(seed)
+    B, S, H, KVH, D = batch, seq_len, num_heads, kv_num_heads, head_size
+    kt = np.asarray(key_total(rng) if callable(key_total) else key_total, dtype=np.int32)
+    total = int(kt.max()) if total_seq is None else int(total_seq)
+    present_key = _fill_normal(rng, (B, KVH, max_seq, D), np.float16)
+    present_value = _fill_normal(rng, (B, KVH, max_seq, D), np.float16)
+    if packed:
+        query = _fill_normal(rng, (B * S, (H + 2 * KVH) * D), np.float16)
+        key = value = None
+    else:
+        query = None
+        key = _fill_normal(rng, (B * S, KVH * D), np.float16)
+        value = _fill_normal(rng, (B * S, KVH * D), np.float16)
+    cos = sin = None
+    R = 0
+    P = 0
+    if rotary_mode != ROTARY_NONE:
+        R = D if rotary_dim is None else rotary_dim
+        P = max_seq if rotary_positions is None else rotary_positions
+        cos, sin = rotary_tables(P, R, theta)
+    return dict(name=name, seed=seed, B=B, S=S, H=H, KVH=KVH, D=D, max_seq=max_seq,
+                packed=packed, query=query, key=key, value=value, present_key=present_key,
+                present_value=present_value, total_seq=total, key_total=kt, cos=cos, sin=sin,
+                rotary_dim=R, rotary_mode=rotary_mode, rotary_positions=P)
+
+
+def bnsh_append(seed=6):
+    """Contiguous-cache append at the mixed workload's prefill shape: 8 sequences x 512 new
+    tokens of one padded batch, H=32, KVH=8, D=128, packed QKV, NeoX rotary on all dims, cache
+    [8, 8, 4096, 128] per K and V, per-batch totals ~ U[512, 2560] (past = total - 512)."""
+    return bnsh_workload(seed, batch=8, seq_len=512, num_heads=32, kv_num_heads=8,
+                         head_size=128, max_seq=4096,
+                         key_total=lambda r: r.integers(512, 2561, size=8), packed=True,
+                         rotary_mode=ROTARY_NEOX, rotary_dim=128, rotary_positions=4096,
+                         name="bnsh_b8_s512_h32kv8_d128")
+
+
 # --------------------------------------------------------------------------------------------
 # Block-sparse "edge" workloads (the fp32 KV-outer forward page).
 # --------------------------------------------------------------------------------------------

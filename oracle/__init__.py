@@ -49,6 +49,8 @@ def _load():
     lib.oracle_rotate_query.restype = None
     lib.oracle_build_edges.argtypes = [_i] * 4 + [_vp] * 5
     lib.oracle_build_edges.restype = None
+    lib.oracle_kv_append_bnsh.argtypes = [_i] * 7 + [_vp] * 5 + [_i, _vp, _vp, _vp, _i, _i, _i]
+    lib.oracle_kv_append_bnsh.restype = None
     lib.oracle_paged_attention.argtypes = ([_i] * 7 + [_vp, _ll, _vp, _vp, _vp, _vp, _vp, _d, _i,
                                                        _vp])
     lib.oracle_paged_attention.restype = None
@@ -135,6 +137,22 @@ def rotate_query(w, rotary_mode=None, rotary_dim=None):
                             int(w["rotary_mode"] if rotary_mode is None else rotary_mode),
                             _p(out))
     return out.view(np.float16)
+
+
+def kv_append_bnsh(bw):
+    """The append page's pass over a contiguous BNSH cache for workload ``bw`` (see
+    workloads.bnsh_workload). Returns updated (present_key, present_value) copies,
+    fp16 [B, KVH, max_cache_seq, D]."""
+    lib = _load()
+    pk = _h(bw["present_key"]).copy()
+    pv = _h(bw["present_value"]).copy()
+    lib.oracle_kv_append_bnsh(bw["B"], bw["S"], bw["H"], bw["KVH"], bw["D"], bw["max_seq"],
+                              int(bw["packed"]), _p(_h(bw["query"])), _p(_h(bw["key"])),
+                              _p(_h(bw["value"])), _p(pk), _p(pv), int(bw["total_seq"]),
+                              _p(_c(bw["key_total"], np.int32)), _p(_h(bw["cos"])),
+                              _p(_h(bw["sin"])), int(bw["rotary_dim"]), int(bw["rotary_mode"]),
+                              int(bw["rotary_positions"]))
+    return pk.view(np.float16), pv.view(np.float16)
 
 
 def build_edges(mask, q_batch, used_kv_lens, block_size):

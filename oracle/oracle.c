@@ -221,6 +221,65 @@ void oracle_kv_append(int T, int B, int H, int G, int D, int bs, int MB, int pac
     }
 }
 
+/* The [append] page's own pass over a contiguous BNSH cache [B, KVH, max_cache_seq, D]: one
+ * write per (batch, kv head, new token t < seq_len, component d), at position
+ * past + t with past = oracle_past_length_padded(total_sequence_length,
+ * key_total_sequence_lengths[b], seq_len); the key is rotated at that position (as in
+ * oracle_kv_append), the value copied. Sources: padded rows (b*seq_len + t) of packed
+ * [Q | K | V] rows or of separate [B*seq_len, KVH*D] arrays. A row whose position falls at or
+ * past max_cache_seq (or, with rotary, at or past rotary_positions) is not written: the page
+ * leaves that to the caller, this oracle and the library skip it. */
+void oracle_kv_append_bnsh(int B, int seq_len, int H, int KVH, int D, int max_cache_seq,
+                           int packed, const uint16_t *query, const uint16_t *key,
+                           const uint16_t *value, uint16_t *present_key,
+                           uint16_t *present_value, int total_sequence_length,
+                           const int32_t *key_total_sequence_lengths,
+                           const uint16_t *cos_cache, const uint16_t *sin_cache,
+                           int rotary_dim, int rotary_mode, int rotary_positions)
+{
+    const int half = rotary_dim / 2;
+    const long long qstride = (long long)(H + 2 * KVH) * D;
+    for (int b = 0; b < B; ++b) {
+        const int past = oracle_past_length_padded(total_sequence_length,
+                                                   key_total_sequence_lengths[b], seq_len);
+        for (int h = 0; h < KVH; ++h) {
+            for (int t = 0; t < seq_len; ++t) {
+                const long long pos = (long long)past + t;
+                if (pos >= max_cache_seq)
+                    continue;
+                if (rotary_mode != ORACLE_ROTARY_NONE && pos >= rotary_positions)
+                    continue;
+                const long long row = (long long)b * seq_len + t;
+                const uint16_t *ks, *vs;
+                if (packed) {
+                    ks = query + row * qstride + (long long)H * D + (long long)h * D;
+                    vs = query + row * qstride + (long long)(H + KVH) * D + (long long)h * D;
+                } else {
+                    ks = key + row * KVH * D + (long long)h * D;
+                    vs = value + row * KVH * D + (long long)h * D;
+                }
+                const long long dst = (((long long)b * KVH + h) * max_cache_seq + pos) * D;
+                for (int d = 0; d < D; ++d) {
+                    if (rotary_mode != ORACLE_ROTARY_NONE && d < rotary_dim) {
+                        const int c = rotary_column(d, half, rotary_mode);
+                        const float cs = (float)oracle_f16_to_f64(cos_cache[pos * half + c]);
+                        const float sn = (float)oracle_f16_to_f64(sin_cache[pos * half + c]);
+                        const float own = (float)oracle_f16_to_f64(ks[d]);
+                        const float partner =
+                            (float)oracle_f16_to_f64(ks[rotary_partner(d, half, rotary_mode)]);
+                        present_key[dst + d] = oracle_f32_to_f16(
+                            rotary_component(own, partner, cs, sn,
+                                             rotary_is_first(d, half, rotary_mode)));
+                    } else {
+                        present_key[dst + d] = ks[d];
+                    }
+                    present_value[dst + d] = vs[d];
+                }
+            }
+        }
+    }
+}
+
 /* Query rotation at the same positions (the first "next" step past the pages, which rotate only
  * keys in the append and hand queries to attention already positioned): new query row t of
  * sequence b sits at pos = past[b] + t, and each of its H head rows gets the same per-pair

@@ -316,3 +316,57 @@ def test_query_rotation_none_copies(oracle):
     got = oracle.rotate_query(w)
     src = np.ascontiguousarray(w["query"].reshape(w["T"], -1)[:, :4 * 64])
     assert np.array_equal(got.view(np.uint16), src.view(np.uint16))
+
+
+# ------------------------------------------------------------------ contiguous BNSH append
+def _bnsh(seed, **kw):
+    args = dict(batch=3, seq_len=5, num_heads=4, kv_num_heads=2, head_size=64, max_seq=24,
+                key_total=[9, 5, 21], name="bnsh_small")
+    args.update(kw)
+    return W.bnsh_workload(seed, **args)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("mode", [W.ROTARY_NONE, W.ROTARY_NEOX, W.ROTARY_INTERLEAVED])
+def test_bnsh_equals_paged_append_with_one_block_per_sequence(oracle, packed, mode):
+    """A BNSH cache [B, KVH, S_max, D] is a paged cache [B, S_max, KVH, D] (one block of S_max
+    keys per sequence, identity table) with the two middle axes swapped. Feeding the padded rows
+    to the (separately pinned) paged append with past = the padded-batch rule must give the same
+    cache bits."""
+    bw = _bnsh(40, packed=packed, rotary_mode=mode,
+               rotary_dim=None if mode == W.ROTARY_NONE else 64)
+    pk, pv = oracle.kv_append_bnsh(bw)
+    B, S, KVH, D, M = bw["B"], bw["S"], bw["KVH"], bw["D"], bw["max_seq"]
+    past = np.array([oracle.past_length_padded(bw["total_seq"], int(k), S)
+                     for k in bw["key_total"]], dtype=np.int32)
+    w = dict(T=B * S, B=B, H=bw["H"], G=KVH, D=D, bs=M, MB=1, NB=B, packed=packed,
+             query=bw["query"], key=bw["key"], value=bw["value"],
+             key_cache=np.ascontiguousarray(bw["present_key"].transpose(0, 2, 1, 3)),
+             value_cache=np.ascontiguousarray(bw["present_value"].transpose(0, 2, 1, 3)),
+             cu=np.arange(B + 1, dtype=np.int32) * S, past=past,
+             block_table=np.arange(B, dtype=np.int32).reshape(B, 1), slot_mapping=None,
+             cos=bw["cos"], sin=bw["sin"], rotary_dim=bw["rotary_dim"],
+             rotary_mode=bw["rotary_mode"])
+    kc, vc = oracle.kv_append(w)
+    assert np.array_equal(pk.view(np.uint16), kc.transpose(0, 2, 1, 3).view(np.uint16))
+    assert np.array_equal(pv.view(np.uint16), vc.transpose(0, 2, 1, 3).view(np.uint16))
+
+
+def test_bnsh_prompt_mode_writes_from_position_zero(oracle):
+    """Scalar total == seq_len: every row (even one whose own total is larger) starts at 0."""
+    bw = _bnsh(41, key_total=[5, 12, 3], total_seq=5)
+    pk, _ = oracle.kv_append_bnsh(bw)
+    B, S, KVH, D = bw["B"], bw["S"], bw["KVH"], bw["D"]
+    k = bw["key"].reshape(B, S, KVH, D).transpose(0, 2, 1, 3)
+    assert np.array_equal(pk[:, :, :S].view(np.uint16), k.view(np.uint16))
+    assert np.array_equal(pk[:, :, S:].view(np.uint16), bw["present_key"][:, :, S:].view(np.uint16))
+
+
+def test_bnsh_rows_past_the_cache_are_not_written(oracle):
+    bw = _bnsh(42, key_total=[26, 5, 21])       # batch 0: past 21, rows 21..25, cache holds 24
+    pk, pv = oracle.kv_append_bnsh(bw)
+    k = bw["key"].reshape(3, 5, 2, 64).transpose(0, 2, 1, 3)
+    assert np.array_equal(pk[0, :, 21:24].view(np.uint16), k[0, :, :3].view(np.uint16))
+    changed = pk.view(np.uint16) != bw["present_key"].view(np.uint16)
+    assert changed[0, :, 21:24].any() and not changed[0, :, :21].any()
+    assert not changed[1, :, 5:].any() and not changed[2, :, :16].any()
