@@ -244,6 +244,27 @@ def run_extra(args, torch, np, pa, dev, W):
     del c
     torch.cuda.empty_cache()
 
+    # the append page's own pass: contiguous BNSH cache, padded batch
+    print("# generating the contiguous-cache append workload", file=sys.stderr, flush=True)
+    bw = W.bnsh_append()
+    bc = dev.BnshCase(bw)
+    pa.pa_timing_reset()
+    pa.pa_timing_enable(True)
+    timed(bc.append, steps, 2, torch)
+    pa.pa_timing_enable(False)
+    t_b = pa.pa_timing_get("kv_append_bnsh")
+    pa.pa_timing_reset()
+    us_b = t_b[0] / max(1, t_b[1]) * 1e3
+    rows = bw["B"] * bw["S"]
+    b_bytes = rows * bw["KVH"] * bw["D"] * 2 * 4 + rows * (bw["rotary_dim"] // 2) * 2 * 2
+    out["append_bnsh"] = {
+        "workload": bw["name"], "append_bytes": b_bytes, "kernel_us": round(us_b, 2),
+        "append_GBps": round(b_bytes / (us_b * 1e-6) / 1e9, 1),
+        "pct_hbm": round(100 * b_bytes / (us_b * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+    }
+    del bc
+    torch.cuda.empty_cache()
+
     print("# generating the block-sparse workload", file=sys.stderr, flush=True)
     sw = W.block_sparse_forward()
     s = dev.SparseCase(sw)

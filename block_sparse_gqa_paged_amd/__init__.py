@@ -26,7 +26,7 @@ EXPORTED = ("pa_kv_append", "pa_kv_append_rotate_query", "pa_paged_attention_wor
             "pa_paged_attention",
             "pa_split_combine", "pa_sparse_forward_workspace_size", "pa_sparse_forward",
             "pa_sparse_forward_causal", "pa_sparse_build_edges_workspace_size",
-            "pa_sparse_build_edges",
+            "pa_sparse_build_edges", "pa_kv_append_bnsh",
             "pa_status_string", "pa_timing_enable", "pa_timing_reset", "pa_timing_get")
 
 
@@ -42,6 +42,12 @@ class SparseShape(C.Structure):
                 ("qhead", C.c_int32), ("head_dim", C.c_int32), ("block_size", C.c_int32),
                 ("page_size", C.c_int32), ("num_pages", C.c_int32), ("max_pages", C.c_int32),
                 ("batch", C.c_int32)]
+
+
+class BnshShape(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("seq_len", C.c_int32), ("num_heads", C.c_int32),
+                ("kv_num_heads", C.c_int32), ("head_size", C.c_int32),
+                ("max_cache_seq", C.c_int32), ("packed_qkv", C.c_int32)]
 
 
 class PAError(RuntimeError):
@@ -90,6 +96,8 @@ def lib():
     L.pa_sparse_build_edges.argtypes = ([_i32] * 5 + [_vp] * 3 + [C.c_int64, _vp, _vp, _vp,
                                         C.c_size_t, _vp])
     L.pa_sparse_build_edges.restype = _i32
+    L.pa_kv_append_bnsh.argtypes = [C.POINTER(BnshShape)] + [_vp] * 9 + [_i32] * 3 + [_vp]
+    L.pa_kv_append_bnsh.restype = _i32
     L.pa_status_string.argtypes = [_i32]
     L.pa_status_string.restype = C.c_char_p
     L.pa_timing_enable.argtypes = [_i32]
@@ -227,6 +235,23 @@ def pa_sparse_build_edges(tq, hkv, nblk, block_size, batch, block_mask, q_batch,
         _p(used_kv_lens), int(edge_capacity), _p(edge_meta), _p(group_ptr), _p(workspace),
         int(workspace_bytes), _s(stream))
     return _check(st, "pa_sparse_build_edges", check)
+
+
+def pa_kv_append_bnsh(shape, query, key, value, present_key, present_value,
+                      total_sequence_length, key_total_sequence_lengths, cos_cache=None,
+                      sin_cache=None, rotary_dim=0, rotary_mode=PA_ROTARY_NONE,
+                      rotary_positions=0, stream=None, check=True):
+    st = lib().pa_kv_append_bnsh(
+        C.byref(shape), _p(query), _p(key), _p(value), _p(present_key), _p(present_value),
+        _p(total_sequence_length), _p(key_total_sequence_lengths), _p(cos_cache), _p(sin_cache),
+        int(rotary_dim), int(rotary_mode), int(rotary_positions), _s(stream))
+    return _check(st, "pa_kv_append_bnsh", check)
+
+
+def bnsh_shape(batch, seq_len, num_heads, kv_num_heads, head_size, max_cache_seq,
+               packed_qkv=False):
+    return BnshShape(batch, seq_len, num_heads, kv_num_heads, head_size, max_cache_seq,
+                     int(bool(packed_qkv)))
 
 
 def pa_timing_enable(on=True):

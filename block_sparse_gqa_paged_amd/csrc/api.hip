@@ -573,6 +573,64 @@ pa_status pa_sparse_forward_causal(const pa_sparse_shape *shape, const float *q_
                           l_partial, stream);
 }
 
+pa_status pa_kv_append_bnsh(const pa_bnsh_shape *shape, const void *query, const void *key,
+                            const void *value, void *present_key, void *present_value,
+                            const int32_t *total_sequence_length,
+                            const int32_t *key_total_sequence_lengths, const void *cos_cache,
+                            const void *sin_cache, int32_t rotary_dim, int32_t rotary_mode,
+                            int32_t rotary_positions, void *stream) {
+    if (!shape) return PA_ERR_NULL;
+    const pa_bnsh_shape &s = *shape;
+    if (s.batch < 1 || s.seq_len < 0 || s.num_heads <= 0 || s.kv_num_heads <= 0 ||
+        s.num_heads % s.kv_num_heads != 0 || s.head_size <= 0 || s.max_cache_seq < 1 ||
+        (s.packed_qkv != 0 && s.packed_qkv != 1))
+        return PA_ERR_SHAPE;
+    if (s.head_size != 64 && s.head_size != 128) return PA_ERR_UNSUPPORTED;
+    if (s.packed_qkv) {
+        if (key || value) return PA_ERR_SHAPE;
+        if (!query) return PA_ERR_NULL;
+    } else {
+        if ((key == nullptr) != (value == nullptr)) return PA_ERR_SHAPE;
+        if (!key) return PA_ERR_NULL;
+    }
+    if (rotary_mode != PA_ROTARY_NONE && rotary_mode != PA_ROTARY_NEOX &&
+        rotary_mode != PA_ROTARY_INTERLEAVED)
+        return PA_ERR_SHAPE;
+    if (rotary_mode != PA_ROTARY_NONE) {
+        if (rotary_dim <= 0 || rotary_dim % 2 != 0 || rotary_dim > s.head_size ||
+            rotary_positions < 1)
+            return PA_ERR_SHAPE;
+        if (!cos_cache || !sin_cache) return PA_ERR_NULL;
+    }
+    if (s.seq_len == 0) return PA_OK;
+    if (!present_key || !present_value || !total_sequence_length || !key_total_sequence_lengths)
+        return PA_ERR_NULL;
+    const int H = s.num_heads, G = s.kv_num_heads, D = s.head_size;
+    BnshArgs a;
+    a.query = s.packed_qkv ? (const half_t *)query : nullptr;
+    a.key = (const half_t *)key;
+    a.value = (const half_t *)value;
+    a.pk = (half_t *)present_key;
+    a.pv = (half_t *)present_value;
+    a.total_seq = total_sequence_length;
+    a.key_total = key_total_sequence_lengths;
+    a.cos = (const half_t *)cos_cache;
+    a.sin = (const half_t *)sin_cache;
+    a.src_stride = s.packed_qkv ? (int64_t)(H + 2 * G) * D : (int64_t)G * D;
+    a.k_off = s.packed_qkv ? (int64_t)H * D : 0;
+    a.v_off = s.packed_qkv ? (int64_t)(H + G) * D : 0;
+    a.B = s.batch;
+    a.S = s.seq_len;
+    a.H = H;
+    a.KVH = G;
+    a.D = D;
+    a.max_seq = s.max_cache_seq;
+    a.rotary_dim = rotary_mode == PA_ROTARY_NONE ? 0 : rotary_dim;
+    a.rotary_mode = rotary_mode;
+    a.rotary_positions = rotary_mode == PA_ROTARY_NONE ? 0 : rotary_positions;
+    return launch_kv_append_bnsh(a, (hipStream_t)stream);
+}
+
 size_t pa_sparse_build_edges_workspace_size(int32_t tq, int32_t hkv) {
     if (tq < 0 || hkv < 1) return 0;
     return std::max<size_t>(256, edge_workspace_bytes((long long)tq * hkv));

@@ -74,6 +74,24 @@ struct AppendArgs {
 };
 pa_status launch_kv_append(const AppendArgs &a, hipStream_t stream);
 
+// Append into a contiguous BNSH cache [B, KVH, max_seq, D] (the append page's own layout).
+struct BnshArgs {
+    const half_t *query;  // packed rows, or NULL
+    const half_t *key;
+    const half_t *value;
+    half_t *pk;
+    half_t *pv;
+    const int32_t *total_seq;  // [1]: scalar total_sequence_length
+    const int32_t *key_total;  // [B]: per-batch totals
+    const half_t *cos;
+    const half_t *sin;
+    int64_t src_stride;  // elements per source row
+    int64_t k_off, v_off;
+    int B, S, H, KVH, D, max_seq;
+    int rotary_dim, rotary_mode, rotary_positions;
+};
+pa_status launch_kv_append_bnsh(const BnshArgs &a, hipStream_t stream);
+
 // Work item of the attention kernels, written by the device planner.
 struct AttnItem {
     int32_t b;     // sequence

@@ -51,8 +51,8 @@ __device__ __forceinline__ float rot_f32(float own, float partner, float cs, flo
 }
 
 // Rotate one 16-byte chunk at dims d0 .. d0+7 (MODE kNeox / kNeoxFull / kInter / kGeneric).
-template <int MODE>
-__device__ __forceinline__ half8_t rotate_chunk(const AppendArgs &a, const half_t *ks, half8_t kv,
+template <int MODE, typename Args>
+__device__ __forceinline__ half8_t rotate_chunk(const Args &a, const half_t *ks, half8_t kv,
                                                 half8_t pk, half8_t cs, half8_t sn, int d0,
                                                 int pos) {
     const int R = a.rotary_dim, half = R >> 1;
@@ -92,8 +92,8 @@ __device__ __forceinline__ half8_t rotate_chunk(const AppendArgs &a, const half_
 
 // cos/sin chunk for dims d0 .. d0+7 at pos (NeoX: 8 columns; interleaved: 4 columns). Chunks
 // past the rotary dims load column 0 of the row instead (unused), so the loads are unconditional.
-template <int MODE>
-__device__ __forceinline__ void load_cs(const AppendArgs &a, int d0, int pos, half8_t &cs,
+template <int MODE, typename Args>
+__device__ __forceinline__ void load_cs(const Args &a, int d0, int pos, half8_t &cs,
                                         half8_t &sn) {
     const int R = a.rotary_dim, half = R >> 1;
     cs = half8_t{};
@@ -296,7 +296,86 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         append_pairs<MODE, LANECU, true>(a, gid - a.nkv_pad, a.nq, s_cu, s_past);
 }
 
+// The append page's own pass over a contiguous BNSH cache [B, KVH, max_seq, D]: thread gid takes
+// chunk pair j of new token t of (batch b, kv head h), with j fastest, then t, so a wave's
+// stores run along consecutive cache rows of one head. past(b) is the padded-batch rule.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void bnsh_kernel(BnshArgs a) {
+    const int lhc = a.D == 128 ? 3 : 2;
+    const long long n = (long long)a.B * a.KVH * a.S << lhc;
+    const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= n) return;
+    const int j = (int)(gid & ((1 << lhc) - 1));
+    long long rest = gid >> lhc;
+    const int t = (int)(rest % a.S);
+    rest /= a.S;
+    const int h = (int)(rest % a.KVH);
+    const int b = (int)(rest / a.KVH);
+    // past length: zero when the scalar total equals seq_len (a prompt), else own total - S
+    const uint32_t total = (uint32_t)a.total_seq[0], own = (uint32_t)a.key_total[b];
+    const uint32_t S = (uint32_t)a.S;
+    const long long past = total == S ? 0 : (own >= S ? (long long)(own - S) : 0);
+    const long long pos = past + t;
+    if (pos >= a.max_seq) return;  // outside the cache: not written
+    if (MODE != kCopy && pos >= a.rotary_positions) return;
+    const int dA = j << 3, dB = dA + (a.D >> 1);
+    const long long row = (long long)b * a.S + t;
+    const half_t *ks = (a.query ? a.query : a.key) + row * a.src_stride + a.k_off +
+                       (long long)h * a.D;
+    const half_t *vs = (a.query ? a.query : a.value) + row * a.src_stride + a.v_off +
+                       (long long)h * a.D;
+    const half8_t kA = gload<half8_t>(ks + dA), kB = gload<half8_t>(ks + dB);
+    const half8_t vA = gload<half8_t>(vs + dA), vB = gload<half8_t>(vs + dB);
+    half8_t oA = kA, oB = kB;
+    if (MODE != kCopy) {
+        half8_t pA = kB, pB = kA;  // kNeoxFull: each other's partners
+        if (MODE == kNeox) {
+            const int R = a.rotary_dim, half = R >> 1;
+            pA = gload<half8_t>(ks + (dA >= R ? 0 : (dA < half ? dA + half : dA - half)));
+            pB = gload<half8_t>(ks + (dB >= R ? 0 : (dB < half ? dB + half : dB - half)));
+        }
+        half8_t cA, sA, cB, sB;
+        load_cs<MODE>(a, dA, (int)pos, cA, sA);
+        if (MODE == kNeoxFull) {
+            cB = cA;
+            sB = sA;
+        } else {
+            load_cs<MODE>(a, dB, (int)pos, cB, sB);
+        }
+        oA = rotate_chunk<MODE>(a, ks, kA, pA, cA, sA, dA, (int)pos);
+        oB = rotate_chunk<MODE>(a, ks, kB, pB, cB, sB, dB, (int)pos);
+    }
+    const long long dst = (((long long)b * a.KVH + h) * a.max_seq + pos) * a.D;
+    *(half8_t *)(a.pk + dst + dA) = oA;
+    *(half8_t *)(a.pk + dst + dB) = oB;
+    *(half8_t *)(a.pv + dst + dA) = vA;
+    *(half8_t *)(a.pv + dst + dB) = vB;
+}
+
 }  // namespace
+
+pa_status launch_kv_append_bnsh(const BnshArgs &a, hipStream_t stream) {
+    LaunchScope scope("kv_append_bnsh", stream);
+    const long long n = ((long long)a.B * a.KVH * a.S) * (a.D >> 4);
+    if (n == 0) return PA_OK;
+    const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
+    const int R = a.rotary_dim;
+    int mode = kCopy;
+    if (a.rotary_mode == PA_ROTARY_NEOX)
+        mode = R == a.D ? kNeoxFull : (R % 16 == 0 ? kNeox : kGeneric);
+    else if (a.rotary_mode == PA_ROTARY_INTERLEAVED)
+        mode = (R % 8 == 0) ? kInter : kGeneric;
+    switch (mode) {
+        case kCopy: scope.launch(bnsh_kernel<kCopy>, dim3(grid), dim3(kThreads), 0, a); break;
+        case kNeoxFull:
+            scope.launch(bnsh_kernel<kNeoxFull>, dim3(grid), dim3(kThreads), 0, a);
+            break;
+        case kNeox: scope.launch(bnsh_kernel<kNeox>, dim3(grid), dim3(kThreads), 0, a); break;
+        case kInter: scope.launch(bnsh_kernel<kInter>, dim3(grid), dim3(kThreads), 0, a); break;
+        default: scope.launch(bnsh_kernel<kGeneric>, dim3(grid), dim3(kThreads), 0, a); break;
+    }
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
 
 pa_status launch_kv_append(const AppendArgs &a_in, hipStream_t stream) {
     LaunchScope scope("kv_append", stream);

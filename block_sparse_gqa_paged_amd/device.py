@@ -7,7 +7,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, pa_kv_append, pa_kv_append_rotate_query,
+from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, bnsh_shape, pa_kv_append, pa_kv_append_bnsh,
+               pa_kv_append_rotate_query,
                pa_paged_attention,
                pa_paged_attention_workspace_size, pa_sparse_build_edges,
                pa_sparse_build_edges_workspace_size, pa_sparse_forward, pa_sparse_forward_causal,
@@ -138,6 +139,33 @@ class SparseCase:
         pa_split_combine(self.o, self.m, self.l, self.group_ptr, sw["Tq"] * sw["hkv"],
                          sw["qhead"], 0, sw["D"], out_dtype, out, stream=stream)
         return out
+
+
+class BnshCase:
+    """A contiguous-cache (BNSH) append workload resident on the device."""
+
+    def __init__(self, bw, device="cuda"):
+        self.bw = bw
+        self.device = device
+        self.shape = bnsh_shape(bw["B"], bw["S"], bw["H"], bw["KVH"], bw["D"], bw["max_seq"],
+                                bw["packed"])
+        self.query = to_dev(bw["query"], device)
+        self.key = to_dev(bw["key"], device)
+        self.value = to_dev(bw["value"], device)
+        self.present_key = to_dev(bw["present_key"], device)
+        self.present_value = to_dev(bw["present_value"], device)
+        self.total = to_dev(np.array([bw["total_seq"]], dtype=np.int32), device)
+        self.key_total = to_dev(bw["key_total"].astype(np.int32), device)
+        self.cos = to_dev(bw["cos"], device)
+        self.sin = to_dev(bw["sin"], device)
+
+    def append(self, stream=None):
+        bw = self.bw
+        pa_kv_append_bnsh(self.shape, self.query, self.key, self.value, self.present_key,
+                          self.present_value, self.total, self.key_total, self.cos, self.sin,
+                          bw["rotary_dim"], bw["rotary_mode"], bw["rotary_positions"],
+                          stream=stream)
+        return self.present_key, self.present_value
 
 
 class EdgeBuilder:

@@ -9,6 +9,7 @@
  *   pa_kv_append_rotate_query  the append plus the same rotation of the new query rows
  *   pa_sparse_forward_causal   the sparse forward with a per-row causal key limit
  *   pa_sparse_build_edges      the sparse forward's edge list from a kept-block mask
+ *   pa_kv_append_bnsh          the append into a contiguous BNSH cache (the append page's own)
  *
  * Sources. Argument names and layouts follow three web pages:
  *   [manifest] "com.microsoft.PagedAttention ... manifest.json": the op's inputs, outputs,
@@ -303,6 +304,44 @@ pa_status pa_sparse_build_edges(int32_t tq, int32_t hkv, int32_t nblk, int32_t b
                                 const int32_t *q_batch, const int32_t *used_kv_lens,
                                 int64_t edge_capacity, int32_t *edge_meta, int32_t *group_ptr,
                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Shape of a contiguous-cache append: the [append] page's own layout, one padded batch of
+ * seq_len new tokens per sequence and a BNSH cache [batch, kv_num_heads, max_cache_seq,
+ * head_size] (present_key / present_value, the same allocation as past_key / past_value).
+ */
+typedef struct pa_bnsh_shape {
+    int32_t batch;          /* B >= 1                                                    */
+    int32_t seq_len;        /* S: new tokens per sequence (padded), >= 0                 */
+    int32_t num_heads;      /* H (packed rows carry H query heads first)                 */
+    int32_t kv_num_heads;   /* KVH, H % KVH == 0                                         */
+    int32_t head_size;      /* D in {64, 128}                                            */
+    int32_t max_cache_seq;  /* positions per (batch, kv head) in the cache               */
+    int32_t packed_qkv;     /* 1: query rows are [Q|K|V], key/value == NULL              */
+} pa_bnsh_shape;
+
+/*
+ * pa_kv_append_bnsh - the [append] page's KV append pass over a contiguous BNSH cache.
+ *
+ * One write per (batch b, kv head h, new token t < S, component d) at
+ * present[((b*KVH + h)*max_cache_seq + past_b + t)*D + d], with the page's padded-batch rule
+ * (past-length macro): past_b = 0 when total_sequence_length[0] == S (a prompt), else
+ * key_total_sequence_lengths[b] - S, or 0 when that total is below S. The key is rotated at its
+ * position exactly as in pa_kv_append; the value is copied. Source row of (b, t):
+ * b*S + t of query (packed) or key / value [B*S, KVH*D].
+ *   total_sequence_length       int32 [1] (device)
+ *   key_total_sequence_lengths  int32 [B] (device)
+ *   cos_cache, sin_cache, rotary_dim, rotary_mode, rotary_positions: as pa_kv_append
+ * A row whose position is >= max_cache_seq (or >= rotary_positions with rotary on) is not
+ * written (the page leaves the bound to its caller).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (D not 64/128), PA_ERR_HIP.
+ */
+pa_status pa_kv_append_bnsh(const pa_bnsh_shape *shape, const void *query, const void *key,
+                            const void *value, void *present_key, void *present_value,
+                            const int32_t *total_sequence_length,
+                            const int32_t *key_total_sequence_lengths, const void *cos_cache,
+                            const void *sin_cache, int32_t rotary_dim, int32_t rotary_mode,
+                            int32_t rotary_positions, void *stream);
 
 /* Static description of a status code. */
 const char *pa_status_string(pa_status status);

@@ -223,3 +223,31 @@ def test_build_edges_rejects_bad_arguments():
     assert be(workspace=FAKE + 4) == pa.PA_ERR_WORKSPACE
     assert pa.pa_sparse_build_edges_workspace_size(4, 2) >= 256
     assert pa.pa_sparse_build_edges_workspace_size(-1, 2) == 0
+
+
+def test_bnsh_append_rejects_bad_arguments():
+    def sh(**kw):
+        a = dict(batch=2, seq_len=4, num_heads=4, kv_num_heads=2, head_size=64, max_cache_seq=32,
+                 packed_qkv=False)
+        a.update(kw)
+        return pa.bnsh_shape(**a)
+
+    def ap(shape, **kw):
+        a = dict(query=None, key=FAKE, value=FAKE, present_key=FAKE, present_value=FAKE,
+                 total_sequence_length=FAKE, key_total_sequence_lengths=FAKE, stream=0,
+                 check=False)
+        a.update(kw)
+        return pa.pa_kv_append_bnsh(shape, **a)
+    assert ap(sh(batch=0)) == pa.PA_ERR_SHAPE
+    assert ap(sh(num_heads=6, kv_num_heads=4)) == pa.PA_ERR_SHAPE
+    assert ap(sh(max_cache_seq=0)) == pa.PA_ERR_SHAPE
+    assert ap(sh(head_size=96)) == pa.PA_ERR_UNSUPPORTED
+    assert ap(sh(), value=None) == pa.PA_ERR_SHAPE
+    assert ap(sh(packed_qkv=True)) == pa.PA_ERR_SHAPE                  # packed: no key/value
+    assert ap(sh(packed_qkv=True), key=None, value=None) == pa.PA_ERR_NULL
+    assert ap(sh(), rotary_mode=pa.PA_ROTARY_NEOX, rotary_dim=64, rotary_positions=8) == \
+        pa.PA_ERR_NULL                                                # tables missing
+    assert ap(sh(), rotary_mode=pa.PA_ROTARY_NEOX, rotary_dim=63, rotary_positions=8,
+              cos_cache=FAKE, sin_cache=FAKE) == pa.PA_ERR_SHAPE
+    assert ap(sh(), present_key=None) == pa.PA_ERR_NULL
+    assert ap(sh(seq_len=0), present_key=None) == pa.PA_OK

@@ -165,6 +165,47 @@ def test_append_rotate_query_mixed_full_size(mixed):
     assert_bits_equal(q_out, qref, "q_out")
 
 
+# Contiguous BNSH cache append (the append page's own pass): whole caches bit-identical.
+BNSH = [
+    dict(seed=140, batch=3, seq_len=5, num_heads=4, kv_num_heads=2, head_size=64, max_seq=24,
+         key_total=[9, 5, 21]),                                       # no rotary
+    dict(seed=141, batch=3, seq_len=7, num_heads=8, kv_num_heads=8, head_size=128,
+         max_seq=40, key_total=[12, 3, 30], rotary_mode=W.ROTARY_NEOX),  # past 0 (total < S)
+    dict(seed=142, batch=2, seq_len=33, num_heads=32, kv_num_heads=8, head_size=128,
+         max_seq=96, key_total=[90, 40], packed=True, rotary_mode=W.ROTARY_NEOX,
+         rotary_dim=64),                                             # rows past the cache
+    dict(seed=143, batch=4, seq_len=6, num_heads=6, kv_num_heads=2, head_size=128, max_seq=32,
+         key_total=[6, 12, 7, 9], total_seq=6, rotary_mode=W.ROTARY_INTERLEAVED),  # prompt
+    dict(seed=144, batch=2, seq_len=9, num_heads=4, kv_num_heads=1, head_size=64, max_seq=40,
+         key_total=[20, 35], packed=True, rotary_mode=W.ROTARY_NEOX, rotary_dim=40),
+    dict(seed=145, batch=2, seq_len=9, num_heads=4, kv_num_heads=2, head_size=64, max_seq=40,
+         key_total=[20, 35], rotary_mode=W.ROTARY_INTERLEAVED, rotary_dim=36,
+         rotary_positions=30),                                       # rows past the table
+]
+
+
+@pytest.mark.parametrize("case", BNSH, ids=lambda c: str(c["seed"]))
+def test_bnsh_append(case):
+    case = dict(case)
+    bw = W.bnsh_workload(case.pop("seed"), name="bnsh", **case)
+    pk, pv = oracle.kv_append_bnsh(bw)
+    c = dev.BnshCase(bw)
+    gk, gv = c.append()
+    torch.cuda.synchronize()
+    assert_bits_equal(gk, pk, "present_key")
+    assert_bits_equal(gv, pv, "present_value")
+
+
+def test_bnsh_append_full_size():
+    bw = W.bnsh_append()
+    pk, pv = oracle.kv_append_bnsh(bw)
+    c = dev.BnshCase(bw)
+    gk, gv = c.append()
+    torch.cuda.synchronize()
+    assert_bits_equal(gk, pk, "present_key")
+    assert_bits_equal(gv, pv, "present_value")
+
+
 def test_append_stress_bit_exact():
     """The append bandwidth workload (65536 packed rows, NeoX rotary on all dims): both caches
     bit-identical to the oracle's, every slot."""
