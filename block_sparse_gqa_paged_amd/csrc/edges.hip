@@ -6,13 +6,15 @@
 // CSR offsets group_ptr[q*hkv + h] of each (q, h) row, which the merge of the partials reads.
 //
 // Stream compaction in three passes over the mask [tq, hkv, nblk] (one byte per block):
-//  * eb_count: a wave takes rows of the mask 64 bytes at a time; the popcount of a ballot of
-//    the nonzero bytes counts a row's edges with no reduction; each workgroup writes the total
-//    of its rows.
+//  * count: each workgroup writes the number of kept blocks in its rows.
 //  * eb_scan: one workgroup turns the workgroup totals into exclusive offsets (in place) and
 //    writes the edge count into group_ptr[tq*hkv].
-//  * eb_emit: the count pass again, then each row's offset, and every set byte writes its edge
-//    at the row offset plus its rank in the ballot (mbcnt).
+//  * emit: the rows are read again, each row's offset is formed, and every kept block writes
+//    its edge at the row offset plus its rank within the row.
+// Power-of-two nblk from 16 to 1024 (16-byte aligned mask): a lane reads 16 mask bytes, a wave
+// covers 64*16/nblk rows per load, nonzero bytes are counted four at a time in a register, and
+// ranks come from a segmented scan over each row's lanes. Other nblk: a wave reads a row 64
+// bytes at a time and counts with the popcount of a ballot; ranks are mbcnt.
 #include "common.h"
 
 namespace pa {
@@ -115,6 +117,120 @@ __global__ __launch_bounds__(kEbThreads) void eb_emit(EdgeArgs a) {
     }
 }
 
+// ---- 16-byte path. cpr = nblk / 16 lanes per row (a power of two <= 64), rpl = 64 / cpr rows
+// per wave load; a wave takes kVecGroups loads, i.e. kVecGroups * rpl consecutive rows.
+constexpr int kVecGroups = 8;
+
+__device__ __forceinline__ int nz_bytes(uint32_t x) {  // nonzero bytes of a word
+    uint32_t t = x | (x >> 4);
+    t |= t >> 2;
+    t |= t >> 1;
+    return __popc(t & 0x01010101u);
+}
+
+__device__ __forceinline__ int nz16(const uint4 &v) {
+    return nz_bytes(v.x) + nz_bytes(v.y) + nz_bytes(v.z) + nz_bytes(v.w);
+}
+
+struct VecRows {
+    uint4 v[kVecGroups];
+    long long row[kVecGroups];  // this lane's row in each load (or >= rows)
+};
+
+__device__ __forceinline__ VecRows vec_load(const EdgeArgs &a, long long w0, int lcpr,
+                                            int lane) {
+    VecRows r;
+    const int cpr = 1 << lcpr, rpl = 64 >> lcpr;
+    for (int g = 0; g < kVecGroups; ++g) {
+        r.row[g] = w0 + (long long)g * rpl + (lane >> lcpr);
+        const long long rr = r.row[g] < a.rows ? r.row[g] : a.rows - 1;
+        r.v[g] = *(const uint4 *)(a.mask + rr * a.nblk + 16 * (lane & (cpr - 1)));
+        if (r.row[g] >= a.rows) r.v[g] = uint4{0u, 0u, 0u, 0u};
+    }
+    return r;
+}
+
+__global__ __launch_bounds__(kEbThreads) void eb_count_vec(EdgeArgs a, int lcpr) {
+    __shared__ int s_tot[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wrows = kVecGroups * (64 >> lcpr);
+    const long long w0 = ((long long)blockIdx.x * 4 + wave) * wrows;
+    const VecRows r = vec_load(a, w0, lcpr, lane);
+    int c = 0;
+    for (int g = 0; g < kVecGroups; ++g) c += nz16(r.v[g]);
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    if (lane == 0) s_tot[wave] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) a.wg[blockIdx.x] = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
+}
+
+__global__ __launch_bounds__(kEbThreads) void eb_emit_vec(EdgeArgs a, int lcpr) {
+    __shared__ int s_tot[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cpr = 1 << lcpr;
+    const int wrows = kVecGroups * (64 >> lcpr);
+    const long long w0 = ((long long)blockIdx.x * 4 + wave) * wrows;
+    const VecRows r = vec_load(a, w0, lcpr, lane);
+    int cnt[kVecGroups];
+    int wt = 0;
+    for (int g = 0; g < kVecGroups; ++g) {
+        cnt[g] = nz16(r.v[g]);
+        wt += cnt[g];
+    }
+    for (int o = 32; o > 0; o >>= 1) wt += __shfl_xor(wt, o, 64);
+    if (lane == 0) s_tot[wave] = wt;
+    __syncthreads();
+    long long e = a.wg[blockIdx.x];  // offset of this wave's first row
+    for (int w = 0; w < wave; ++w) e += s_tot[w];
+    const int seg = lane & (cpr - 1);  // lane's place inside its row
+    for (int g = 0; g < kVecGroups; ++g) {
+        // inclusive scan of the counts over each row's cpr lanes
+        int x = cnt[g];
+        for (int o = 1; o < cpr; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (seg >= o) x += y;
+        }
+        // rows of this load in order: offset of the lane's row = e + totals of earlier rows
+        int before = 0;
+        for (int q = 0; q < (64 >> lcpr); ++q) {
+            const int tq_ = __shfl(x, (q << lcpr) | (cpr - 1), 64);
+            if (q < (lane >> lcpr)) before += tq_;
+        }
+        int load_tot = 0;
+        for (int q = 0; q < (64 >> lcpr); ++q) load_tot += __shfl(x, (q << lcpr) | (cpr - 1), 64);
+        const long long row = r.row[g];
+        if (row < a.rows) {
+            const long long rbase = e + before;
+            if (seg == 0) a.group_ptr[row] = (int32_t)rbase;
+            long long k = rbase + x - cnt[g];  // first edge of this lane's 16 blocks
+            const int q = (int)(row / a.hkv), h = (int)(row - (long long)q * a.hkv);
+            const int b = a.q_batch[q];
+            const int used = a.used[min(max(b, 0), a.batch - 1)];
+            // bit i of `set`: byte i of the lane's 16 is nonzero; visit only those
+            const uint32_t wv[4] = {r.v[g].x, r.v[g].y, r.v[g].z, r.v[g].w};
+            uint32_t set = 0;
+            for (int i = 0; i < 16; ++i)
+                set |= (((wv[i >> 2] >> (8 * (i & 3))) & 0xffu) != 0u ? 1u : 0u) << i;
+            while (set) {
+                const int i = __ffs(set) - 1;
+                set &= set - 1;
+                if (k < a.capacity) {
+                    const int blk = 16 * seg + i;
+                    const long long len = (long long)used - (long long)blk * a.block_size;
+                    int32_t *o = a.edge_meta + 5 * k;
+                    o[0] = q;
+                    o[1] = h;
+                    o[2] = blk;
+                    o[3] = b;
+                    o[4] = (int32_t)(len < 0 ? 0 : (len > a.block_size ? a.block_size : len));
+                }
+                ++k;
+            }
+        }
+        e += load_tot;
+    }
+}
+
 }  // namespace
 
 size_t edge_workspace_bytes(long long rows) {
@@ -131,6 +247,17 @@ pa_status launch_build_edges(const EdgeArgs &a, hipStream_t stream) {
         return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
     }
     LaunchScope scope("build_edges", stream, 3);
+    int lcpr = -1;  // 16-byte path when nblk = 16 * 2^lcpr <= 1024 and the mask is aligned
+    for (int l = 0; l <= 6; ++l)
+        if (a.nblk == 16 << l) lcpr = l;
+    if (lcpr >= 0 && ((uintptr_t)a.mask % 16) == 0) {
+        const long long wg_rows = 4LL * kVecGroups * (64 >> lcpr);
+        const long long nv = (a.rows + wg_rows - 1) / wg_rows;  // <= nwg: workspace fits
+        scope.launch(eb_count_vec, dim3((unsigned)nv), dim3(kEbThreads), 0, a, lcpr);
+        scope.launch(eb_scan, dim3(1), dim3(1024), 0, a, (int)nv);
+        scope.launch(eb_emit_vec, dim3((unsigned)nv), dim3(kEbThreads), 0, a, lcpr);
+        return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+    }
     scope.launch(eb_count, dim3((unsigned)nwg), dim3(kEbThreads), 0, a);
     scope.launch(eb_scan, dim3(1), dim3(1024), 0, a, (int)nwg);
     scope.launch(eb_emit, dim3((unsigned)nwg), dim3(kEbThreads), 0, a);

@@ -34,6 +34,11 @@ CASES = [
     dict(seed=302, tq=33, hkv=4, nblk=130, batch=2, density=0.1),
     dict(seed=303, tq=70, hkv=1, nblk=1, batch=4, density=0.7),
     dict(seed=304, tq=3, hkv=8, nblk=512, batch=1, density=0.9),
+    # 16-byte path: nblk = 16 * 2^k up to 1024, row counts that leave partial loads
+    dict(seed=306, tq=37, hkv=3, nblk=16, batch=2, density=0.5),
+    dict(seed=307, tq=11, hkv=5, nblk=128, batch=3, density=0.2),
+    dict(seed=308, tq=9, hkv=2, nblk=1024, batch=2, density=0.05),
+    dict(seed=309, tq=200, hkv=8, nblk=512, batch=2, density=0.06),
 ]
 
 
@@ -60,9 +65,20 @@ def test_empty_query_set():
                 used_kv_lens=np.array([5], np.int32), block_size=16, batch=1))
 
 
-def test_capacity_below_edge_count():
-    sw = _random_case(305, tq=20, hkv=2, nblk=40, batch=2, density=0.5)
+@pytest.mark.parametrize("nblk", [40, 64])
+def test_capacity_below_edge_count(nblk):
+    sw = _random_case(305, tq=20, hkv=2, nblk=nblk, batch=2, density=0.5)
     _check(sw, capacity=int(sw["block_mask"].sum()) // 3)
+
+
+def test_nonbinary_mask_bytes():
+    """Any nonzero byte keeps its block (on both paths)."""
+    for nblk in (24, 32):
+        sw = _random_case(310, tq=6, hkv=2, nblk=nblk, batch=2, density=0.5)
+        rng = np.random.default_rng(311)
+        sw["block_mask"] = (sw["block_mask"] * rng.integers(1, 256, size=sw["block_mask"].shape)
+                            ).astype(np.uint8)
+        _check(sw)
 
 
 def test_full_block_sparse_mask():
