@@ -87,6 +87,15 @@ __device__ __forceinline__ void block_scan(const int (&v)[NV], int (&excl)[NV], 
 }
 
 __device__ __forceinline__ int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Prefill items are listed longest first (by 64-key tiles, counting-sorted in LDS; items of
+// kPreBins - 1 or more tiles share the top bin), so that the persistent prefill workgroups take
+// the long items early and the short ones fill the tail.
+constexpr int kPreBins = 4 * kPlanThreads;
+constexpr int kPreBinKeys = 64;
+__device__ __forceinline__ int pre_bin(int k1) {
+    return min(kPreBins - 1, (k1 + kPreBinKeys - 1) / kPreBinKeys);
+}
 __device__ __forceinline__ int round_tile(long long x) {
     return (int)((x + kTileKeys - 1) / kTileKeys * kTileKeys);
 }
@@ -103,15 +112,22 @@ __device__ __forceinline__ int round_tile(long long x) {
 //    dynamic counter.
 //  * Every query row of a sequence cut into >= 2 pieces gets nsplit partial units and one entry
 //    of the combine list; a sequence left whole writes its output directly.
-//  * Longer sequences get tiles of tpi_pre rows, the last (longest causal) tile of each first.
+//  * Longer sequences get tiles of tpi_pre rows; the prefill list holds them longest key range
+//    first across all sequences.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __shared__ long long sh_ll[kPlanThreads / 64];
     __shared__ int sh_i[kPlanThreads / 64 * 4];
+    __shared__ int sh_bin[kPreBins];  // prefill items per length bin, then list offsets
     const int tid = threadIdx.x;
+    for (int i = tid; i < kPreBins; i += kPlanThreads) sh_bin[i] = 0;
     const bool streamk = a.mode == 0;
 
     auto decode_like = [&](int n) { return n >= 1 && n <= a.tpi_dec; };
     auto piece_keys = [&](int L) { return round_tile(ceil_div_i(L, a.splits)); };
+    // key range end of prefill item `tile` of a sequence with n new tokens after `past`
+    auto pre_k1 = [&](int tile, int n, int past) {
+        return a.causal ? past + min(n, (tile + 1) * a.tpi_pre) : past + n;
+    };
 
     // Pass 1: tiles of decode-like sequences; in even mode, the count of whole pieces.
     long long ntiles = 0, nfull = 0;
@@ -211,22 +227,45 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                     a.comb[idx] = ci;
                 }
             }
-            for (int j = 0; j < cnt[3]; ++j) {
-                const int idx = carry[3] + ex[3] + j;
-                if (idx < a.cap_pre) {
-                    const int tile = cnt[3] - 1 - j;   // longest (last) tile first
-                    const int tlast = min(n, (tile + 1) * a.tpi_pre) - 1;
-                    AttnItem it;
-                    it.b = b; it.t0 = tile * a.tpi_pre; it.k0 = 0;
-                    it.k1 = a.causal ? past + tlast + 1 : L;
-                    it.base = -1; it.nsplit = 1; it.split = 0; it.comb = -1;
-                    a.pre[idx] = it;
-                }
-            }
+            for (int tile = 0; tile < cnt[3]; ++tile)
+                atomicAdd(&sh_bin[pre_bin(pre_k1(tile, n, past))], 1);
         }
         for (int k = 0; k < 4; ++k) carry[k] += tot[k];
         carry_tiles += ttot[0];
         carry_tail += tltot[0];
+    }
+    // Pass 3: prefill items, longest first. Bin offsets in descending bin order, then each item
+    // takes the next place of its bin (the order inside a bin is arbitrary; every item writes
+    // its own output rows, so the results do not depend on it).
+    {
+        __syncthreads();
+        int c4[4], s4 = 0;
+        for (int i = 0; i < 4; ++i) {
+            c4[i] = sh_bin[kPreBins - 1 - (4 * tid + i)];
+            s4 += c4[i];
+        }
+        int sv[1] = {s4}, sex[1], stot[1];
+        block_scan<1>(sv, sex, stot, sh_i);
+        int run = sex[0];
+        for (int i = 0; i < 4; ++i) {
+            sh_bin[kPreBins - 1 - (4 * tid + i)] = run;
+            run += c4[i];
+        }
+        __syncthreads();
+    }
+    for (int b = tid; b < a.B; b += kPlanThreads) {
+        const int n = a.cu[b + 1] - a.cu[b];
+        if (n <= a.tpi_dec) continue;
+        const int past = a.past[b];
+        const int ntile = ceil_div_i(n, a.tpi_pre);
+        for (int tile = 0; tile < ntile; ++tile) {
+            AttnItem it;
+            it.b = b; it.t0 = tile * a.tpi_pre; it.k0 = 0;
+            it.k1 = pre_k1(tile, n, past);
+            it.base = -1; it.nsplit = 1; it.split = 0; it.comb = -1;
+            const int idx = atomicAdd(&sh_bin[pre_bin(it.k1)], 1);
+            if (idx < a.cap_pre) a.pre[idx] = it;
+        }
     }
     const int ndec_items = min(carry[0], a.cap_dec);
     if (streamk)

@@ -10,12 +10,15 @@
 // of one sequence, so its (token, head) columns fill four waves of 32 columns each, and the
 // workgroup's four waves share every key tile:
 //  * 64-key tiles of K (row-major) and V (transposed) are staged in LDS as fp16, once per
-//    workgroup; the next tile's global loads are issued before the current tile is computed.
+//    workgroup; the next tile's global loads are issued before the current tile is computed,
+//    and the block-table entries they need are read one tile earlier still.
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_f16 with keys as rows (K read from LDS in the row order
 //    pkappa, so each lane's accumulator holds 8 consecutive keys of one column: the k-slots of
 //    the P^T operand) and O^T = V^T . P^T with V^T rows read as 16-byte operands. O^T gives each
 //    lane its own column, so the softmax rescale needs no shuffles and stores are 8 bytes wide.
-//  * Online base-2 softmax per column; the two column blocks of a wave share each K and V read.
+//  * Online base-2 softmax per column with a lazily raised maximum (O is rescaled only when the
+//    maximum grows by more than 2^8); the column reductions use row-swap permutes, not LDS.
+//    The two column blocks of a wave share each K and V read.
 #include "common.h"
 
 namespace pa {
@@ -38,24 +41,58 @@ __device__ __forceinline__ int kswz(int row, int c) {
 }
 __device__ __forceinline__ int vswz(int d, int c) { return c ^ (((d >> 1) ^ (d >> 4)) & 7); }
 
+// Reductions over the four lanes n16, n16 + 16, n16 + 32, n16 + 48 (one column of the S^T
+// accumulator) with the gfx950 row-swap permutes: each swap exchanges rows between two copies of
+// the value, so combining the two results gives the reduction without a trip through LDS.
+__device__ __forceinline__ float col_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const uint32_t v = __float_as_uint(x);
+    const auto t = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const uint32_t v = __float_as_uint(x);
+    const auto t = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// The running maximum of a column is raised only when a tile's maximum exceeds it by more than
+// this many powers of two, so the O rescale runs rarely; P entries then stay below 2^kSlack
+// (exact in fp16 range) and the final O / l does not depend on which reference maximum was used.
+constexpr float kSlack = 8.f;
+
 template <int D>
 struct PfTile {            // one thread's share of a tile: 4 consecutive keys x 8 dims, K and V
     half8_t k[4], v[4];
 };
 
-// Global loads of this thread's part of the tile at kt: keys kt + 4*kq .. +3, dims 8*c .. +7.
-// Keys past k1 - 1 load key k1 - 1 (masked later), so no table entry or row outside the
-// sequence's range is read.
+// Physical block of keys k4 .. k4 + 3 when the four share one block and all lie before k1, else
+// -1 (the per-key path below). Loaded one tile ahead, so that the next tile's key and value loads
+// do not wait on the table lookup.
+__device__ __forceinline__ int pf_block(const AttnArgs &a, const int32_t *bt, int k4, int k1) {
+    if ((a.bs & 3) == 0 && k4 + 3 < k1) {
+        const int j = a.log2bs >= 0 ? (k4 >> a.log2bs) : k4 / a.bs;
+        return bt[j];
+    }
+    return -1;
+}
+
+// Global loads of this thread's part of the tile holding keys k4 .. k4 + 3 (k4 = kt + 4*kq),
+// dims 8*c .. +7; pb is pf_block(k4). Keys past k1 - 1 load key k1 - 1 (masked later), so no
+// table entry or row outside the sequence's range is read.
 template <int D>
 __device__ __forceinline__ void pf_load(PfTile<D> &t, const AttnArgs &a, const int32_t *bt,
-                                        const half_t *kcg, const half_t *vcg, int kt, int k1,
-                                        int kq, int c) {
-    const int k4 = kt + 4 * kq;
+                                        const half_t *kcg, const half_t *vcg, int pb, int k4,
+                                        int k1, int c) {
     const uint32_t ke = a.key_elems;  // < 2^24 (checked on the host): 24-bit multiplies
-    if ((a.bs & 3) == 0 && k4 + 3 < k1) {
-        // the 4 keys sit in one block: one table lookup
+    if (pb >= 0) {
         const int j = a.log2bs >= 0 ? (k4 >> a.log2bs) : k4 / a.bs;
-        const size_t off = (size_t)bt[j] * a.block_elems + __umul24(k4 - j * a.bs, ke) + 8 * c;
+        const size_t off = (size_t)pb * a.block_elems + __umul24(k4 - j * a.bs, ke) + 8 * c;
         for (int r = 0; r < 4; ++r) {
             t.k[r] = gload<half8_t>(kcg + off + __umul24(r, ke));
             t.v[r] = gload<half8_t>(vcg + off + __umul24(r, ke));
@@ -102,7 +139,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a) {
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g16 = lane >> 4, n16 = lane & 15;
-    const bool loader = threadIdx.x < TASKS;
+    const bool loader = TASKS == kPfThreads || threadIdx.x < TASKS;
     const int kq = threadIdx.x / KC, c = threadIdx.x % KC;
     const int n_work = a.n_items[0] * a.G;
     if (n_work == 0) return;
@@ -156,12 +193,24 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a) {
         const half_t *vcg = a.vc + (size_t)g * D;
         const int k1 = it.k1;
         PfTile<D> tl;
-        if (loader && k1 > 0) pf_load<D>(tl, a, bt, kcg, vcg, 0, k1, kq, c);
+        int pbn = -1;  // pf_block of this thread's keys in the tile after the one in flight
+        if (loader && k1 > 0) {
+            pf_load<D>(tl, a, bt, kcg, vcg, pf_block(a, bt, 4 * kq, k1), 4 * kq, k1, c);
+            if (kKT < k1) pbn = pf_block(a, bt, kKT + 4 * kq, k1);
+        }
+        // Drain the query and first-tile loads here. Without this wait the compiler treats the
+        // query registers as possibly in flight inside the tile loop, and since the vector-memory
+        // counter retires in order, its wait before the first score product would also cover the
+        // next tile's prefetch.
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         for (int kt = 0; kt < k1; kt += kKT) {
             __syncthreads();  // every wave is done with the previous tile
             if (loader) pf_store<D>(tl, Ks, Vt, kq, c);
             __syncthreads();
-            if (loader && kt + kKT < k1) pf_load<D>(tl, a, bt, kcg, vcg, kt + kKT, k1, kq, c);
+            if (loader && kt + kKT < k1) {
+                pf_load<D>(tl, a, bt, kcg, vcg, pbn, kt + kKT + 4 * kq, k1, c);
+                pbn = kt + 2 * kKT < k1 ? pf_block(a, bt, kt + 2 * kKT + 4 * kq, k1) : -1;
+            }
             if (kt >= wave_end) continue;  // every column of this wave ends before the tile
 
             // S^T: keys 32s + 8*g16 + 4u + i of columns n16 (both column blocks per K read).
@@ -195,11 +244,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a) {
                 for (int s = 0; s < 2; ++s)
                     for (int u = 0; u < 2; ++u)
                         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[cb][s][u][i]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float m_new = fmaxf(m[cb], mx * a.scale_log2);
+                const float mt = col_max(mx) * a.scale_log2;
+                const bool raise = mt > m[cb] + kSlack;  // false while the whole tile is masked
+                const float m_new = raise ? mt : m[cb];
                 const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = (m_new == m[cb]) ? 1.f : __builtin_amdgcn_exp2f(m[cb] - m_use);
+                const float alpha = raise ? __builtin_amdgcn_exp2f(m[cb] - m_use) : 1.f;
                 float ps = 0.f;
                 for (int s = 0; s < 2; ++s)
                     for (int u = 0; u < 2; ++u)
@@ -212,7 +261,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a) {
                 l[cb] = l[cb] * alpha + ps;
                 m[cb] = m_new;
                 // O^T columns are this lane's own column: rescale in place
-                if (__ballot(alpha != 1.f))
+                if (__ballot(raise))
                     for (int dt = 0; dt < NDT; ++dt) o[cb][dt] *= alpha;
             }
             // O^T += V^T . P^T: A operand = 8 keys of dim 16*dt + n16 from a V^T row; the
@@ -229,8 +278,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a) {
 
         // Column totals; lane (g16, n16) writes dims 16*dt + 4*g16 .. +3 of column n16.
         for (int cb = 0; cb < 2; ++cb) {
-            float lt = l[cb] + __shfl_xor(l[cb], 16, 64);
-            lt += __shfl_xor(lt, 32, 64);
+            const float lt = col_sum(l[cb]);
             const int col = 32 * wave + 16 * cb + n16;
             if (col >= ncols) continue;
             const int t = col / a.Q, qh = col - t * a.Q;
