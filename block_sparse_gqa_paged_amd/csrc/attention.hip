@@ -45,17 +45,6 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *sh) {
     return t;
 }
 
-__device__ __forceinline__ int block_max_i(int v, long long *sh) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-    __syncthreads();
-    if (lane == 0) sh[wid] = v;
-    __syncthreads();
-    int t = 0;
-    for (int i = 0; i < kPlanThreads / 64; ++i) t = max(t, (int)sh[i]);
-    return t;
-}
-
 // Exclusive scan of NV counters across the workgroup; returns totals in tot[].
 template <int NV>
 __device__ __forceinline__ void block_scan(const int (&v)[NV], int (&excl)[NV], int (&tot)[NV],
