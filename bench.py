@@ -106,7 +106,7 @@ def main():
     ms, wall = timed(step, args.steps, args.warmup, torch)
     pa.pa_timing_enable(False)
     n_launch = args.steps + args.warmup
-    kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "attn_prefill",
+    kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "prefill_combine",
                                            "combine")}
     pa.pa_timing_reset()
     # the same steps without the library's event records, for the step time itself
@@ -184,7 +184,7 @@ def run_extra(args, torch, np, pa, dev, W):
     pa.pa_timing_enable(True)
     ms, _ = timed(lambda: (c.append(), c.attention(pa.PA_SPLITS_AUTO)), steps, 2, torch)
     pa.pa_timing_enable(False)
-    kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "attn_prefill",
+    kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "prefill_combine",
                                            "combine")}
     pa.pa_timing_reset()
     us = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
@@ -200,8 +200,8 @@ def run_extra(args, torch, np, pa, dev, W):
     out["mixed_prefill_decode"] = {
         "workload": w["name"], "ms_per_step": round(ms, 4), "kernel_us": us,
         "kv_bytes": kv, "step_kv_GBps": round(kv / (ms * 1e-3) / 1e9, 1),
-        "prefill_TFLOPs": round(flops / (us.get("attn_prefill", 1e9) * 1e-6) / 1e12, 2),
-        "prefill_mfma_frac": round(flops / (us.get("attn_prefill", 1e9) * 1e-6) / 1e12
+        "prefill_TFLOPs": round(flops / (us.get("prefill_combine", 1e9) * 1e-6) / 1e12, 2),
+        "prefill_mfma_frac": round(flops / (us.get("prefill_combine", 1e9) * 1e-6) / 1e12
                                    / MFMA_F16_PEAK_TFS, 4),
         "append_GBps": round(app_bytes / (us.get("kv_append", 1e9) * 1e-6) / 1e9, 1),
         "append_pct_hbm": round(100 * app_bytes / (us.get("kv_append", 1e9) * 1e-6) / 1e9

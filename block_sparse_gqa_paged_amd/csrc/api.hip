@@ -428,25 +428,22 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     a.gw = 1;
     const long long pre_units = (long long)p.cap_pre * G;
     const int pblocks = (int)std::min(pre_units, (long long)cus * 2);
-    if ((st = launch_prefill(a, D, pblocks, strm)) != PA_OK) return st;
 
-    if (p.unit_cap > 0) {
-        CombineArgs c;
-        c.o = a.o_part;
-        c.m = a.m_part;
-        c.l = a.l_part;
-        c.group_ptr = nullptr;
-        c.items = pl.comb;
-        c.n_items = &pl.hdr->n_comb;
-        c.num_groups = 0;
-        c.lanes = H;
-        c.splits = 0;
-        c.D = D;
-        c.out_f32 = 0;
-        c.out = output;
-        if ((st = launch_combine(c, p.cap_comb, strm)) != PA_OK) return st;
-    }
-    return PA_OK;
+    // The split decode rows are merged by extra workgroups of the prefill launch.
+    CombineArgs c;
+    c.o = a.o_part;
+    c.m = a.m_part;
+    c.l = a.l_part;
+    c.group_ptr = nullptr;
+    c.items = pl.comb;
+    c.n_items = &pl.hdr->n_comb;
+    c.num_groups = 0;
+    c.lanes = H;
+    c.splits = 0;
+    c.D = D;
+    c.out_f32 = 0;
+    c.out = output;
+    return launch_prefill(a, D, pblocks, p.unit_cap > 0 ? &c : nullptr, p.cap_comb, strm);
 }
 
 pa_status pa_split_combine(const float *o_partial, const float *m_partial,

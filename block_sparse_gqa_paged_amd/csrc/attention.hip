@@ -46,9 +46,10 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *sh) {
 }
 
 // Exclusive scan of NV counters across the workgroup; returns totals in tot[].
-template <int NV>
+template <int NV, int M>
 __device__ __forceinline__ void block_scan(const int (&v)[NV], int (&excl)[NV], int (&tot)[NV],
-                                           int *sh) {
+                                           int (&sh)[M]) {
+    static_assert(M >= kPlanThreads / 64 * NV, "scan scratch: one entry per wave and counter");
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     int inc[NV];
     for (int k = 0; k < NV; ++k) {
@@ -105,7 +106,7 @@ __device__ __forceinline__ int round_tile(long long x) {
 //    first across all sequences.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __shared__ long long sh_ll[kPlanThreads / 64];
-    __shared__ int sh_i[kPlanThreads / 64 * 4];
+    __shared__ int sh_i[kPlanThreads / 64 * 5];  // block_scan<NV> needs (waves x NV)
     __shared__ int sh_bin[kPreBins];  // prefill items per length bin, then list offsets
     const int tid = threadIdx.x;
     for (int i = tid; i < kPreBins; i += kPlanThreads) sh_bin[i] = 0;
@@ -118,12 +119,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         return a.causal ? past + min(n, (tile + 1) * a.tpi_pre) : past + n;
     };
 
+    // Sequence b's first token, new tokens and past length. The first kPlanThreads sequences are
+    // read once, here, and kept in registers for all passes (one memory round trip instead of
+    // three); later chunks are read where they are needed.
+    int r_cu0 = 0, r_n = 0, r_past = 0;
+    if (tid < a.B) {
+        r_cu0 = a.cu[tid];
+        r_n = a.cu[tid + 1] - r_cu0;
+        r_past = a.past[tid];
+    }
+    auto seq = [&](int b, int &cu0, int &n, int &past) {
+        if (b < kPlanThreads) {  // b == tid
+            cu0 = r_cu0; n = r_n; past = r_past;
+        } else {
+            cu0 = a.cu[b]; n = a.cu[b + 1] - cu0; past = a.past[b];
+        }
+    };
+
     // Pass 1: tiles of decode-like sequences; in even mode, the count of whole pieces.
     long long ntiles = 0, nfull = 0;
     for (int b = tid; b < a.B; b += kPlanThreads) {
-        const int n = a.cu[b + 1] - a.cu[b];
+        int cu0, n, past;
+        seq(b, cu0, n, past);
         if (!decode_like(n)) continue;
-        const int L = a.past[b] + n;
+        const int L = past + n;
         ntiles += ceil_div_i(L, kTileKeys);
         if (!streamk) {
             const int Cb = piece_keys(L);
@@ -150,9 +169,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         const int b = base + tid;
         int n = 0, L = 0, past = 0, cu0 = 0, T = 0;
         if (b < a.B) {
-            cu0 = a.cu[b];
-            n = a.cu[b + 1] - cu0;
-            past = a.past[b];
+            seq(b, cu0, n, past);
             L = past + n;
             if (decode_like(n)) T = ceil_div_i(L, kTileKeys);
         }
@@ -160,7 +177,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         block_scan<1>(tv, tex, ttot, sh_i);
         const long long TB = carry_tiles + tex[0];   // first global tile of sequence b
         int c = 0, Cb = 1, tail = 0;
-        int cnt[4] = {0, 0, 0, 0};
+        int cnt[5] = {0, 0, 0, 0, 0};  // items, partial units, combine rows, prefill, tail
         if (b < a.B) {
             if (decode_like(n)) {
                 if (streamk) {
@@ -179,10 +196,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                 cnt[3] = ceil_div_i(n, a.tpi_pre);
             }
         }
-        int ex[4], tot[4];
-        block_scan<4>(cnt, ex, tot, sh_i);
-        int tl_[1] = {tail}, tlex[1], tltot[1];
-        block_scan<1>(tl_, tlex, tltot, sh_i);
+        cnt[4] = tail;
+        int ex[5], tot[5];
+        block_scan<5>(cnt, ex, tot, sh_i);
+        const int tlex = ex[4];
         if (b < a.B) {
             const int ubase = carry[1] + ex[1];
             const int cbase = carry[2] + ex[2];
@@ -201,8 +218,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                     if (t0 == j * q && j < a.slots) a.slot_ptr[j] = idx;
                 } else {
                     const bool is_tail = sp >= c - tail;
-                    idx = is_tail ? full_total + carry_tail + tlex[0] : carry[0] - carry_tail +
-                                                                            (ex[0] - tlex[0]) + sp;
+                    idx = is_tail ? full_total + carry_tail + tlex : carry[0] - carry_tail +
+                                                                         (ex[0] - tlex) + sp;
                     it.k0 = sp * Cb;
                     it.k1 = min(L, (sp + 1) * Cb);
                 }
@@ -221,12 +238,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
         for (int k = 0; k < 4; ++k) carry[k] += tot[k];
         carry_tiles += ttot[0];
-        carry_tail += tltot[0];
+        carry_tail += tot[4];
     }
     // Pass 3: prefill items, longest first. Bin offsets in descending bin order, then each item
     // takes the next place of its bin (the order inside a bin is arbitrary; every item writes
     // its own output rows, so the results do not depend on it).
-    {
+    if (carry[3] > 0) {  // block-uniform
         __syncthreads();
         int c4[4], s4 = 0;
         for (int i = 0; i < 4; ++i) {
@@ -242,10 +259,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
         __syncthreads();
     }
-    for (int b = tid; b < a.B; b += kPlanThreads) {
-        const int n = a.cu[b + 1] - a.cu[b];
+    for (int b = tid; b < a.B && carry[3] > 0; b += kPlanThreads) {
+        int cu0, n, past;
+        seq(b, cu0, n, past);
         if (n <= a.tpi_dec) continue;
-        const int past = a.past[b];
         const int ntile = ceil_div_i(n, a.tpi_pre);
         for (int tile = 0; tile < ntile; ++tile) {
             AttnItem it;

@@ -175,7 +175,11 @@ pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, const 
 // Prefill items (a.tpi = kPrefillCols / Q tokens each) on four-wave workgroups, one per
 // (item, kv head) taken from the planner's counter.
 constexpr int kPrefillCols = 128;
-pa_status launch_prefill(const AttnArgs &a, int D, int blocks, hipStream_t stream);
+// cmb (may be NULL): planner-list combine of the split decode partials (max_groups list
+// entries), run by extra workgroups of the same launch.
+struct CombineArgs;
+pa_status launch_prefill(const AttnArgs &a, int D, int blocks, const CombineArgs *cmb,
+                         int max_groups, hipStream_t stream);
 
 struct CombineArgs {
     const float *o;

@@ -1,5 +1,5 @@
 // Chunked-prefill attention for gfx950: the query rows of sequences with more new tokens than a
-// decode item holds.
+// decode item holds. The same launch also merges the split decode partials (see prefill_kernel).
 //
 // Operation: the PagedAttention op of the "com.microsoft.PagedAttention ... manifest.json" page
 // (pass "main") for those rows: each (token, head) column attends, through the block table, to
@@ -19,7 +19,7 @@
 //  * Online base-2 softmax per column with a lazily raised maximum (O is rescaled only when the
 //    maximum grows by more than 2^8); the column reductions use row-swap permutes, not LDS.
 //    The two column blocks of a wave share each K and V read.
-#include "common.h"
+#include "combine_rows.h"
 
 namespace pa {
 namespace {
@@ -126,8 +126,14 @@ __device__ __forceinline__ void pf_store(const PfTile<D> &t, half_t *Ks, half_t 
     }
 }
 
+// The launch after the decode kernel: the first gridDim.x - pre_blocks workgroups merge the
+// split decode partials (combine role, at most one per CU), the other pre_blocks run the
+// persistent prefill loop. The two roles are independent (prefill rows are written directly),
+// so one launch serves both and the step has one launch fewer. The combine workgroups come
+// first: placed last they would wait for the persistent prefill workgroups to leave.
 template <int D>
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, CombineArgs cmb,
+                                                                 int pre_blocks) {
     constexpr int KB = D / 32;           // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;          // 16-dim output tiles
     constexpr int KC = D / 8;
@@ -137,6 +143,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) half_t Vt[D * kKT];
     __shared__ int s_unit;
 
+    if ((int)blockIdx.x < (int)gridDim.x - pre_blocks) {
+        constexpr int kWg = kPfThreads / 64;
+        combine_rows<D>(cmb, 2, blockIdx.x * kWg + (threadIdx.x >> 6),
+                        (gridDim.x - pre_blocks) * kWg);
+        return;
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g16 = lane >> 4, n16 = lane & 15;
     const bool loader = TASKS == kPfThreads || threadIdx.x < TASKS;
@@ -296,13 +308,24 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a) {
 
 }  // namespace
 
-pa_status launch_prefill(const AttnArgs &a, int D, int blocks, hipStream_t stream) {
-    LaunchScope scope("attn_prefill", stream);
-    if (blocks <= 0) return PA_OK;
+pa_status launch_prefill(const AttnArgs &a, int D, int blocks, const CombineArgs *cmb,
+                         int max_groups, hipStream_t stream) {
+    LaunchScope scope("prefill_combine", stream);
+    int comb_blocks = 0;
+    CombineArgs c{};
+    if (cmb && max_groups > 0) {
+        c = *cmb;
+        // At most one combine workgroup per CU: max_groups is a bound (every row split); the
+        // waves loop when more rows are split than they cover in one pass.
+        comb_blocks = (int)std::min<long long>((combine_waves(max_groups, c.lanes, D) + 3) / 4,
+                                               device_cu_count());
+    }
+    const int grid = blocks + comb_blocks;
+    if (grid <= 0) return PA_OK;
     if (D == 128)
-        scope.launch(prefill_kernel<128>, dim3(blocks), dim3(kPfThreads), 0, a);
+        scope.launch(prefill_kernel<128>, dim3(grid), dim3(kPfThreads), 0, a, c, blocks);
     else if (D == 64)
-        scope.launch(prefill_kernel<64>, dim3(blocks), dim3(kPfThreads), 0, a);
+        scope.launch(prefill_kernel<64>, dim3(grid), dim3(kPfThreads), 0, a, c, blocks);
     else
         return PA_ERR_UNSUPPORTED;
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
