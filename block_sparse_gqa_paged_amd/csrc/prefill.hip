@@ -9,13 +9,17 @@
 // MI355X design: the work unit is (planner item, kv head). An item is up to 128 / Q new tokens
 // of one sequence, so its (token, head) columns fill four waves of 32 columns each, and the
 // workgroup's four waves share every key tile:
-//  * 64-key tiles of K (row-major) and V (transposed) are staged in LDS as fp16, once per
-//    workgroup; the next tile's global loads are issued before the current tile is computed,
-//    and the block-table entries they need are read one tile earlier still.
+//  * 64-key tiles of K and V are copied straight from the cache into LDS (global_load_lds,
+//    16 bytes per lane: no registers, no LDS store instructions), into two stages: the next
+//    tile's copies are issued right after the one barrier per tile and land while the current
+//    tile is computed. The XOR swizzles of the LDS rows are applied on the source side: lane p
+//    of a row copies the cache chunk that belongs at LDS chunk p.
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_f16 with keys as rows (K read from LDS in the row order
 //    pkappa, so each lane's accumulator holds 8 consecutive keys of one column: the k-slots of
-//    the P^T operand) and O^T = V^T . P^T with V^T rows read as 16-byte operands. O^T gives each
-//    lane its own column, so the softmax rescale needs no shuffles and stores are 8 bytes wide.
+//    the P^T operand) and O^T = V^T . P^T, whose V^T operand comes from the row-major V tile
+//    through the gfx950 transposing LDS read (ds_read_b64_tr_b16: within 16 lanes, lane i gets
+//    element i % 4 of the rows addressed by lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4). O^T gives
+//    each lane its own column, so the softmax rescale needs no shuffles and stores are 8 bytes.
 //  * Online base-2 softmax per column with a lazily raised maximum (O is rescaled only when the
 //    maximum grows by more than 2^8); the column reductions use row-swap permutes, not LDS.
 //    The two column blocks of a wave share each K and V read.
@@ -31,15 +35,75 @@ constexpr int kKT = 64;          // keys per tile
 // that the S^T accumulator of lane (g16, n16) holds keys 8*g16 + 4u + i: 8*g16 .. 8*g16 + 7.
 __device__ __forceinline__ int pkappa(int u, int m) { return 8 * (m >> 2) + 4 * u + (m & 3); }
 
-// XOR swizzles of 16-byte chunks. K rows are read 16 at a time in the order pkappa (rows
-// 8*(m>>2) + (m&3) + 4u): kswz gives those 16 rows distinct chunk offsets. V^T rows are read as
-// 16 consecutive rows (two per 256-byte bank line) and written as 16 rows 8 apart: vswz spreads
-// both patterns.
+// XOR swizzles of the 16-byte chunks of a tile row (row = key within the tile), as masks:
+// LDS chunk position p of row r holds cache chunk p ^ mask(r).
+//  * K rows are read 16 at a time in the order pkappa (rows 8*(m>>2) + (m&3) + 4u): kmask gives
+//    those 16 rows distinct chunk positions.
+//  * V rows are read by the transposing read: per half wave, keys {b..b+3, b+8..b+11} at two
+//    adjacent chunks each (32 bytes); vmask spreads those 16 chunks over all LDS banks.
 template <int KC>
-__device__ __forceinline__ int kswz(int row, int c) {
-    return c ^ (((row & 3) | ((row >> 1) & 12)) & (KC - 1));
+__device__ __forceinline__ int kmask(int r) {
+    return ((r & 3) | ((r >> 1) & 12)) & (KC - 1);
 }
-__device__ __forceinline__ int vswz(int d, int c) { return c ^ (((d >> 1) ^ (d >> 4)) & 7); }
+template <int KC>
+__device__ __forceinline__ int vmask(int r) {
+    if (KC == 16) return 2 * ((r & 3) | ((r >> 1) & 4));          // 256-byte rows
+    return 2 * (((r >> 1) & 1) | ((r >> 2) & 2));                 // 128-byte rows: two per bank line
+}
+
+// One 16-byte global -> LDS copy per lane: lane l writes LDS bytes [16 l, 16 l + 16) of the
+// wave-uniform destination dst.
+__device__ __forceinline__ void dma16(const half_t *src, half_t *dst) {
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1))) *)src,
+        (void __attribute__((address_space(3))) *)dst, 16, 0, 0);
+}
+
+// Issue this wave's share of the copies of the tile at kt into the stage (Kd, Vd): keys
+// kt + 16*wave .. +15 of K and of V. A copy instruction moves RPI whole rows (lane l: row l / KC,
+// chunk position l % KC). Keys past k1 - 1 copy key k1 - 1 (masked later), so no table entry or
+// row outside the sequence's range is read. When the block size is a multiple of 16 and the
+// wave's 16 keys are all valid they share one cache block: one wave-uniform table lookup.
+template <int D>
+__device__ __forceinline__ void pf_copy(const AttnArgs &a, const int32_t *bt, const half_t *kcg,
+                                        const half_t *vcg, int kt, int k1, half_t *Kd, half_t *Vd,
+                                        int wave, int lane) {
+    constexpr int KC = D / 8;          // 16-byte chunks per row
+    constexpr int RPI = 64 / KC;       // rows per copy instruction
+    constexpr int IPW = 16 / RPI;      // copy instructions per wave and matrix
+    const int pos = lane % KC, rsub = lane / KC;
+    const int k16 = kt + 16 * wave;
+    const uint32_t ke = a.key_elems;  // < 2^24 (checked on the host): 24-bit multiplies
+    const bool one_block = (a.bs & 15) == 0 && k16 + 15 < k1;
+    int j16 = 0;
+    size_t blk16 = 0;
+    if (one_block) {
+        j16 = a.log2bs >= 0 ? (k16 >> a.log2bs) : k16 / a.bs;
+        blk16 = (size_t)bt[j16] * a.block_elems;
+    }
+    for (int t = 0; t < IPW; ++t) {
+        const int r = 16 * wave + t * RPI + rsub;  // row within the tile
+        size_t row;
+        if (one_block) {
+            row = blk16 + __umul24(kt + r - j16 * a.bs, ke);
+        } else {
+            const int key = min(kt + r, k1 - 1);
+            const int j = a.log2bs >= 0 ? (key >> a.log2bs) : key / a.bs;
+            row = (size_t)bt[j] * a.block_elems + __umul24(key - j * a.bs, ke);
+        }
+        const int r0 = 16 * wave + t * RPI;        // first row of this instruction
+        dma16(kcg + row + 8 * (pos ^ kmask<KC>(r)), Kd + r0 * D);
+        dma16(vcg + row + 8 * (pos ^ vmask<KC>(r)), Vd + r0 * D);
+    }
+}
+
+// Transposing LDS read of 4 halves (ds_read_b64_tr_b16).
+__device__ __forceinline__ half4_t lds_read_tr(const half_t *p) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s4 __attribute__((address_space(3))) *)p);
+    return __builtin_bit_cast(half4_t, v);
+}
 
 // Reductions over the four lanes n16, n16 + 16, n16 + 32, n16 + 48 (one column of the S^T
 // accumulator) with the gfx950 row-swap permutes: each swap exchanges rows between two copies of
@@ -66,66 +130,6 @@ __device__ __forceinline__ float col_sum(float x) {
 // (exact in fp16 range) and the final O / l does not depend on which reference maximum was used.
 constexpr float kSlack = 8.f;
 
-template <int D>
-struct PfTile {            // one thread's share of a tile: 4 consecutive keys x 8 dims, K and V
-    half8_t k[4], v[4];
-};
-
-// Physical block of keys k4 .. k4 + 3 when the four share one block and all lie before k1, else
-// -1 (the per-key path below). Loaded one tile ahead, so that the next tile's key and value loads
-// do not wait on the table lookup.
-__device__ __forceinline__ int pf_block(const AttnArgs &a, const int32_t *bt, int k4, int k1) {
-    if ((a.bs & 3) == 0 && k4 + 3 < k1) {
-        const int j = a.log2bs >= 0 ? (k4 >> a.log2bs) : k4 / a.bs;
-        return bt[j];
-    }
-    return -1;
-}
-
-// Global loads of this thread's part of the tile holding keys k4 .. k4 + 3 (k4 = kt + 4*kq),
-// dims 8*c .. +7; pb is pf_block(k4). Keys past k1 - 1 load key k1 - 1 (masked later), so no
-// table entry or row outside the sequence's range is read.
-template <int D>
-__device__ __forceinline__ void pf_load(PfTile<D> &t, const AttnArgs &a, const int32_t *bt,
-                                        const half_t *kcg, const half_t *vcg, int pb, int k4,
-                                        int k1, int c) {
-    const uint32_t ke = a.key_elems;  // < 2^24 (checked on the host): 24-bit multiplies
-    if (pb >= 0) {
-        const int j = a.log2bs >= 0 ? (k4 >> a.log2bs) : k4 / a.bs;
-        const size_t off = (size_t)pb * a.block_elems + __umul24(k4 - j * a.bs, ke) + 8 * c;
-        for (int r = 0; r < 4; ++r) {
-            t.k[r] = gload<half8_t>(kcg + off + __umul24(r, ke));
-            t.v[r] = gload<half8_t>(vcg + off + __umul24(r, ke));
-        }
-        return;
-    }
-    for (int r = 0; r < 4; ++r) {
-        const int key = min(k4 + r, k1 - 1);
-        const int j = a.log2bs >= 0 ? (key >> a.log2bs) : key / a.bs;
-        const size_t off = (size_t)bt[j] * a.block_elems + __umul24(key - j * a.bs, ke) + 8 * c;
-        t.k[r] = gload<half8_t>(kcg + off);
-        t.v[r] = gload<half8_t>(vcg + off);
-    }
-}
-
-// Store the thread's part into LDS: K rows [kKT][D] and V^T rows [D][kKT], both with 16-byte
-// chunks XOR-swizzled by row.
-template <int D>
-__device__ __forceinline__ void pf_store(const PfTile<D> &t, half_t *Ks, half_t *Vt, int kq,
-                                         int c) {
-    constexpr int KC = D / 8;     // 16-byte chunks per K row
-    static_assert(kKT / 8 == 8, "vswz assumes 8 chunks per V^T row");
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * kq + r;
-        *(half8_t *)(Ks + row * D + 8 * kswz<KC>(row, c)) = t.k[r];
-    }
-    for (int x = 0; x < 8; ++x) {
-        const int d = 8 * c + x;
-        const half4_t q4 = {t.v[0][x], t.v[1][x], t.v[2][x], t.v[3][x]};
-        *(half4_t *)(Vt + d * kKT + 8 * vswz(d, kq >> 1) + 4 * (kq & 1)) = q4;
-    }
-}
-
 // The launch after the decode kernel: the first gridDim.x - pre_blocks workgroups merge the
 // split decode partials (combine role, at most one per CU), the other pre_blocks run the
 // persistent prefill loop. The two roles are independent (prefill rows are written directly),
@@ -137,10 +141,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
     constexpr int KB = D / 32;           // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;          // 16-dim output tiles
     constexpr int KC = D / 8;
-    constexpr int TASKS = kKT / 4 * KC;  // (key quad, 8-dim chunk) pairs per tile
-    static_assert(TASKS <= kPfThreads, "one load task per thread");
-    __shared__ __attribute__((aligned(16))) half_t Ks[kKT * D];
-    __shared__ __attribute__((aligned(16))) half_t Vt[D * kKT];
+    static_assert(kKT == 16 * (kPfThreads / 64), "each wave copies 16 keys of a tile");
+    // Two stages of row-major K and V tiles (64 KB at D = 128: two workgroups per CU).
+    __shared__ __attribute__((aligned(16))) half_t Ks[2][kKT * D];
+    __shared__ __attribute__((aligned(16))) half_t Vs[2][kKT * D];
     __shared__ int s_unit;
 
     if ((int)blockIdx.x < (int)gridDim.x - pre_blocks) {
@@ -151,8 +155,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g16 = lane >> 4, n16 = lane & 15;
-    const bool loader = TASKS == kPfThreads || threadIdx.x < TASKS;
-    const int kq = threadIdx.x / KC, c = threadIdx.x % KC;
     const int n_work = a.n_items[0] * a.G;
     if (n_work == 0) return;
 
@@ -204,25 +206,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
         const half_t *kcg = a.kc + (size_t)g * D;
         const half_t *vcg = a.vc + (size_t)g * D;
         const int k1 = it.k1;
-        PfTile<D> tl;
-        int pbn = -1;  // pf_block of this thread's keys in the tile after the one in flight
-        if (loader && k1 > 0) {
-            pf_load<D>(tl, a, bt, kcg, vcg, pf_block(a, bt, 4 * kq, k1), 4 * kq, k1, c);
-            if (kKT < k1) pbn = pf_block(a, bt, kKT + 4 * kq, k1);
-        }
-        // Drain the query and first-tile loads here. Without this wait the compiler treats the
-        // query registers as possibly in flight inside the tile loop, and since the vector-memory
-        // counter retires in order, its wait before the first score product would also cover the
-        // next tile's prefetch.
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        for (int kt = 0; kt < k1; kt += kKT) {
-            __syncthreads();  // every wave is done with the previous tile
-            if (loader) pf_store<D>(tl, Ks, Vt, kq, c);
-            __syncthreads();
-            if (loader && kt + kKT < k1) {
-                pf_load<D>(tl, a, bt, kcg, vcg, pbn, kt + kKT + 4 * kq, k1, c);
-                pbn = kt + 2 * kKT < k1 ? pf_block(a, bt, kt + 2 * kKT + 4 * kq, k1) : -1;
-            }
+        // Tile ti sits in stage ti & 1. At the top of each tile: wait for this wave's copies
+        // (and, on the first tile, the query loads), one barrier (every wave's copies of tile ti
+        // have landed, and every wave has finished tile ti - 1, whose stage the next copies
+        // overwrite), then issue the copies of tile ti + 1 and compute tile ti. The barrier is a
+        // bare s_barrier: a workgroup fence would also wait for the copies just issued.
+        const int ntl = (k1 + kKT - 1) / kKT;
+        if (ntl > 0) pf_copy<D>(a, bt, kcg, vcg, 0, k1, Ks[0], Vs[0], wave, lane);
+        for (int ti = 0; ti < ntl; ++ti) {
+            const int kt = ti * kKT;
+            const half_t *Kb = Ks[ti & 1], *Vb = Vs[ti & 1];
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+            asm volatile("s_barrier" ::: "memory");
+            if (ti + 1 < ntl)
+                pf_copy<D>(a, bt, kcg, vcg, kt + kKT, k1, Ks[(ti + 1) & 1], Vs[(ti + 1) & 1], wave,
+                           lane);
             if (kt >= wave_end) continue;  // every column of this wave ends before the tile
 
             // S^T: keys 32s + 8*g16 + 4u + i of columns n16 (both column blocks per K read).
@@ -232,8 +230,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
                     float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
                     const int row = 32 * s + pkappa(u, n16);
                     for (int kb = 0; kb < KB; ++kb) {
-                        const half8_t kr =
-                            *(const half8_t *)(Ks + row * D + 8 * kswz<KC>(row, 4 * kb + g16));
+                        const half8_t kr = *(const half8_t *)(
+                            Kb + row * D + 8 * ((4 * kb + g16) ^ kmask<KC>(row)));
                         acc[0] = mfma16x16x32(kr, q[0][kb], acc[0]);
                         acc[1] = mfma16x16x32(kr, q[1][kb], acc[1]);
                     }
@@ -276,13 +274,24 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
                 if (__ballot(raise))
                     for (int dt = 0; dt < NDT; ++dt) o[cb][dt] *= alpha;
             }
-            // O^T += V^T . P^T: A operand = 8 keys of dim 16*dt + n16 from a V^T row; the
-            // accumulator holds dims 16*dt + 4*g16 + i of column n16.
+            // O^T += V^T . P^T: A operand = keys 32s + 8*g16 + 0..7 of dim 16*dt + n16, two
+            // transposing reads of 4 keys (lane r of a 16-lane group addresses key kb + r/4,
+            // dims 16*dt + 4*(r%4) .. +3); the accumulator holds dims 16*dt + 4*g16 + i of column n16.
+            // The operand of output tile dt + 1 is read while tile dt's products run.
+            const int csub = (n16 & 3) >> 1, hoff = 4 * (n16 & 1);
+            auto vop = [&](int s, int dt) {
+                const int k0 = 32 * s + 8 * g16 + (n16 >> 2), k4 = k0 + 4;
+                const int c = 2 * dt + csub;
+                const half4_t lo = lds_read_tr(Vb + k0 * D + 8 * (c ^ vmask<KC>(k0)) + hoff);
+                const half4_t hi = lds_read_tr(Vb + k4 * D + 8 * (c ^ vmask<KC>(k4)) + hoff);
+                return half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            };
+            half8_t vnext = vop(0, 0);
             for (int s = 0; s < 2; ++s)
                 for (int dt = 0; dt < NDT; ++dt) {
-                    const int d = 16 * dt + n16;
-                    const half8_t vb =
-                        *(const half8_t *)(Vt + d * kKT + 8 * vswz(d, 4 * s + g16));
+                    const half8_t vb = vnext;
+                    if (dt + 1 < NDT) vnext = vop(s, dt + 1);
+                    else if (s == 0) vnext = vop(1, 0);
                     o[0][dt] = mfma16x16x32(vb, pf[0][s], o[0][dt]);
                     o[1][dt] = mfma16x16x32(vb, pf[1][s], o[1][dt]);
                 }
