@@ -118,8 +118,10 @@ __global__ __launch_bounds__(kEbThreads) void eb_emit(EdgeArgs a) {
 }
 
 // ---- 16-byte path. cpr = nblk / 16 lanes per row (a power of two <= 64), rpl = 64 / cpr rows
-// per wave load; a wave takes kVecGroups loads, i.e. kVecGroups * rpl consecutive rows.
-constexpr int kVecGroups = 8;
+// per wave load; a wave takes G loads, i.e. G * rpl consecutive rows. G is the smallest of
+// 2, 4, 8 with G * rpl >= 8, so that a workgroup covers at least kEbRows rows (the workspace
+// holds one total per kEbRows rows) while the grid stays large: with 8 loads per wave the
+// 0.99 M-edge mask (32768 rows of 64 blocks) filled only 64 workgroups.
 
 __device__ __forceinline__ int nz_bytes(uint32_t x) {  // nonzero bytes of a word
     uint32_t t = x | (x >> 4);
@@ -132,16 +134,18 @@ __device__ __forceinline__ int nz16(const uint4 &v) {
     return nz_bytes(v.x) + nz_bytes(v.y) + nz_bytes(v.z) + nz_bytes(v.w);
 }
 
+template <int G>
 struct VecRows {
-    uint4 v[kVecGroups];
-    long long row[kVecGroups];  // this lane's row in each load (or >= rows)
+    uint4 v[G];
+    long long row[G];  // this lane's row in each load (or >= rows)
 };
 
-__device__ __forceinline__ VecRows vec_load(const EdgeArgs &a, long long w0, int lcpr,
-                                            int lane) {
-    VecRows r;
+template <int G>
+__device__ __forceinline__ VecRows<G> vec_load(const EdgeArgs &a, long long w0, int lcpr,
+                                               int lane) {
+    VecRows<G> r;
     const int cpr = 1 << lcpr, rpl = 64 >> lcpr;
-    for (int g = 0; g < kVecGroups; ++g) {
+    for (int g = 0; g < G; ++g) {
         r.row[g] = w0 + (long long)g * rpl + (lane >> lcpr);
         const long long rr = r.row[g] < a.rows ? r.row[g] : a.rows - 1;
         r.v[g] = *(const uint4 *)(a.mask + rr * a.nblk + 16 * (lane & (cpr - 1)));
@@ -150,30 +154,32 @@ __device__ __forceinline__ VecRows vec_load(const EdgeArgs &a, long long w0, int
     return r;
 }
 
+template <int G>
 __global__ __launch_bounds__(kEbThreads) void eb_count_vec(EdgeArgs a, int lcpr) {
     __shared__ int s_tot[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wrows = kVecGroups * (64 >> lcpr);
+    const int wrows = G * (64 >> lcpr);
     const long long w0 = ((long long)blockIdx.x * 4 + wave) * wrows;
-    const VecRows r = vec_load(a, w0, lcpr, lane);
+    const VecRows<G> r = vec_load<G>(a, w0, lcpr, lane);
     int c = 0;
-    for (int g = 0; g < kVecGroups; ++g) c += nz16(r.v[g]);
+    for (int g = 0; g < G; ++g) c += nz16(r.v[g]);
     for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
     if (lane == 0) s_tot[wave] = c;
     __syncthreads();
     if (threadIdx.x == 0) a.wg[blockIdx.x] = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
 }
 
+template <int G>
 __global__ __launch_bounds__(kEbThreads) void eb_emit_vec(EdgeArgs a, int lcpr) {
     __shared__ int s_tot[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cpr = 1 << lcpr;
-    const int wrows = kVecGroups * (64 >> lcpr);
+    const int wrows = G * (64 >> lcpr);
     const long long w0 = ((long long)blockIdx.x * 4 + wave) * wrows;
-    const VecRows r = vec_load(a, w0, lcpr, lane);
-    int cnt[kVecGroups];
+    const VecRows<G> r = vec_load<G>(a, w0, lcpr, lane);
+    int cnt[G];
     int wt = 0;
-    for (int g = 0; g < kVecGroups; ++g) {
+    for (int g = 0; g < G; ++g) {
         cnt[g] = nz16(r.v[g]);
         wt += cnt[g];
     }
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(kEbThreads) void eb_emit_vec(EdgeArgs a, int lcpr) 
     long long e = a.wg[blockIdx.x];  // offset of this wave's first row
     for (int w = 0; w < wave; ++w) e += s_tot[w];
     const int seg = lane & (cpr - 1);  // lane's place inside its row
-    for (int g = 0; g < kVecGroups; ++g) {
+    for (int g = 0; g < G; ++g) {
         // inclusive scan of the counts over each row's cpr lanes
         int x = cnt[g];
         for (int o = 1; o < cpr; o <<= 1) {
@@ -251,11 +257,18 @@ pa_status launch_build_edges(const EdgeArgs &a, hipStream_t stream) {
     for (int l = 0; l <= 6; ++l)
         if (a.nblk == 16 << l) lcpr = l;
     if (lcpr >= 0 && ((uintptr_t)a.mask % 16) == 0) {
-        const long long wg_rows = 4LL * kVecGroups * (64 >> lcpr);
-        const long long nv = (a.rows + wg_rows - 1) / wg_rows;  // <= nwg: workspace fits
-        scope.launch(eb_count_vec, dim3((unsigned)nv), dim3(kEbThreads), 0, a, lcpr);
+        const int rpl = 64 >> lcpr;
+        const int G = rpl >= 4 ? 2 : 8 / rpl;  // G * rpl >= 8
+        const long long wg_rows = 4LL * G * rpl;  // >= kEbRows: nv <= nwg, the workspace fits
+        const long long nv = (a.rows + wg_rows - 1) / wg_rows;
+        const dim3 grid((unsigned)nv), block(kEbThreads);
+        if (G == 2) scope.launch(eb_count_vec<2>, grid, block, 0, a, lcpr);
+        else if (G == 4) scope.launch(eb_count_vec<4>, grid, block, 0, a, lcpr);
+        else scope.launch(eb_count_vec<8>, grid, block, 0, a, lcpr);
         scope.launch(eb_scan, dim3(1), dim3(1024), 0, a, (int)nv);
-        scope.launch(eb_emit_vec, dim3((unsigned)nv), dim3(kEbThreads), 0, a, lcpr);
+        if (G == 2) scope.launch(eb_emit_vec<2>, grid, block, 0, a, lcpr);
+        else if (G == 4) scope.launch(eb_emit_vec<4>, grid, block, 0, a, lcpr);
+        else scope.launch(eb_emit_vec<8>, grid, block, 0, a, lcpr);
         return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
     }
     scope.launch(eb_count, dim3((unsigned)nwg), dim3(kEbThreads), 0, a);

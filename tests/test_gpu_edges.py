@@ -39,6 +39,8 @@ CASES = [
     dict(seed=307, tq=11, hkv=5, nblk=128, batch=3, density=0.2),
     dict(seed=308, tq=9, hkv=2, nblk=1024, batch=2, density=0.05),
     dict(seed=309, tq=200, hkv=8, nblk=512, batch=2, density=0.06),
+    dict(seed=311, tq=45, hkv=3, nblk=256, batch=2, density=0.1),    # 4 rows per load
+    dict(seed=312, tq=300, hkv=8, nblk=64, batch=3, density=0.08),   # many workgroups
 ]
 
 
