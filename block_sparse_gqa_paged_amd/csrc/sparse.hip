@@ -347,19 +347,38 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
     const int rows = epg * a.qhead;
     const int hq = a.hkv * a.qhead;
     const int el = n16 / a.qhead, qh = n16 - el * a.qhead;
+    // The next group's query operands are loaded at the start of this group, and the one wait
+    // for them sits right before this group's stores. A wait for a load while stores are
+    // outstanding has to drain the stores too (loads and stores share the counter and may
+    // complete out of order), so without this the next group's first use of its query would
+    // wait for this group's partial stores to reach memory.
+    half8_t nqhi[KB], nqlo[KB];
+    float nqmul = 0.f;
+    auto load_q = [&](int grp) {
+        const int idx = grp * epg + el;
+        const int ix = (n16 < rows && idx < nE) ? idx : 0;
+        const long long qrow = (long long)s_q[ix] * hq + h * a.qhead + qh;
+        for (int kb = 0; kb < KB; ++kb) {
+            nqhi[kb] = gload<half8_t>(w.qhi + qrow * D + 32 * kb + 8 * g16);
+            nqlo[kb] = gload<half8_t>(w.qlo + qrow * D + 32 * kb + 8 * g16);
+        }
+        nqmul = gload<float>(w.qmul + qrow);
+    };
+    if (wave * epg < nE) load_q(wave);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     for (int grp = wave; grp * epg < nE; grp += NW) {
         const int idx = grp * epg + el;
         const bool vrow = n16 < rows && idx < nE;
         const int ix = vrow ? idx : 0;  // rows without an edge read edge 0's query, then drop it
         const int e = s_e[ix];
         const int len = vrow ? s_len[ix] : 0;
-        const long long qrow = (long long)s_q[ix] * hq + h * a.qhead + qh;
         half8_t qhi[KB], qlo[KB];
         for (int kb = 0; kb < KB; ++kb) {
-            qhi[kb] = gload<half8_t>(w.qhi + qrow * D + 32 * kb + 8 * g16);
-            qlo[kb] = gload<half8_t>(w.qlo + qrow * D + 32 * kb + 8 * g16);
+            qhi[kb] = nqhi[kb];
+            qlo[kb] = nqlo[kb];
         }
-        const float mult = ldexpf(gload<float>(w.qmul + qrow), eK);
+        const float mult = ldexpf(nqmul, eK);
+        if ((grp + NW) * epg < nE) load_q(grp + NW);
         // keys this lane scores (16j + 4g16 + i) that are mapped and below the edge's length
         uint64_t lm[MW];
         for (int hw = 0; hw < MW; ++hw) {
@@ -425,6 +444,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
             }
         }
         // Stores: four consecutive dims of o per lane, scaled back by 2^eV; m and l from g16 == 0.
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next group's query loads (above)
         if (vrow) {
             const long long p = (long long)e * a.qhead + qh;
             float *op = a.o + p * D + 4 * g16;
