@@ -127,7 +127,7 @@ bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
     p.ncb_dec = p.Q <= 16 ? 1 : (p.Q <= 32 ? 2 : 4);
     p.tpi_dec = 16 * p.ncb_dec / p.Q;
     p.gw = p.ncb_dec == 1 ? std::gcd(G, 8) : 1;
-    p.tpi_pre = std::max(1, kPrefillCols / p.Q);  // one prefill workgroup: 128 (token, head) columns
+    p.tpi_pre = std::max(1, kPrefillCols / p.Q);  // one prefill workgroup: kPrefillCols columns
     if (num_splits == PA_SPLITS_AUTO) {
         p.mode = 0;
         p.splits = 0;
@@ -427,7 +427,8 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     a.tpi = p.tpi_pre;
     a.gw = 1;
     const long long pre_units = (long long)p.cap_pre * G;
-    const int pblocks = (int)std::min(pre_units, (long long)cus * 2);
+    // persistent prefill workgroups: as many as fit at once (two waves per SIMD)
+    const int pblocks = (int)std::min(pre_units, (long long)cus * 8 / (kPrefillCols / 32));
 
     // The split decode rows are merged by extra workgroups of the prefill launch.
     CombineArgs c;

@@ -172,9 +172,9 @@ struct AttnArgs {
 // workgroups of a.gw waves.
 pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, const char *name,
                            hipStream_t stream);
-// Prefill items (a.tpi = kPrefillCols / Q tokens each) on four-wave workgroups, one per
+// Prefill items (a.tpi = kPrefillCols / Q tokens each) on workgroups of kPrefillCols / 32 waves, one per
 // (item, kv head) taken from the planner's counter.
-constexpr int kPrefillCols = 128;
+constexpr int kPrefillCols = 128;  // (token, head) columns per prefill item: 4 waves of 32
 // cmb (may be NULL): planner-list combine of the split decode partials (max_groups list
 // entries), run by extra workgroups of the same launch.
 struct CombineArgs;

@@ -28,8 +28,10 @@
 namespace pa {
 namespace {
 
-constexpr int kPfThreads = 256;  // four waves
-constexpr int kKT = 64;          // keys per tile
+constexpr int kKT = 64;                       // keys per tile
+constexpr int kPfWaves = kPrefillCols / 32;  // 32 (token, head) columns per wave
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfKpw = kKT / kPfWaves;        // keys of a tile each wave copies
 
 // Key-row order inside a 32-key group: MFMA row m of 16-key half u holds key pkappa(u, m), so
 // that the S^T accumulator of lane (g16, n16) holds keys 8*g16 + 4u + i: 8*g16 .. 8*g16 + 7.
@@ -59,39 +61,42 @@ __device__ __forceinline__ void dma16(const half_t *src, half_t *dst) {
         (void __attribute__((address_space(3))) *)dst, 16, 0, 0);
 }
 
+// Cache block of this wave's keys kt + kPfKpw*wave .. + kPfKpw - 1 when they all lie before k1
+// in one block (block size a multiple of kPfKpw), else -1. Wave-uniform; read one tile ahead of
+// the copies that use it, so that they do not wait on the table lookup.
+__device__ __forceinline__ int pf_wave_block(const AttnArgs &a, const int32_t *bt, int kt, int k1,
+                                             int wave) {
+    const int kw = kt + kPfKpw * wave;
+    if (a.bs % kPfKpw != 0 || kw + kPfKpw - 1 >= k1) return -1;
+    return bt[a.log2bs >= 0 ? (kw >> a.log2bs) : kw / a.bs];
+}
+
 // Issue this wave's share of the copies of the tile at kt into the stage (Kd, Vd): keys
-// kt + 16*wave .. +15 of K and of V. A copy instruction moves RPI whole rows (lane l: row l / KC,
-// chunk position l % KC). Keys past k1 - 1 copy key k1 - 1 (masked later), so no table entry or
-// row outside the sequence's range is read. When the block size is a multiple of 16 and the
-// wave's 16 keys are all valid they share one cache block: one wave-uniform table lookup.
+// kt + kPfKpw*wave .. + kPfKpw - 1 of K and of V; pb is pf_wave_block(kt). A copy instruction
+// moves RPI whole rows (lane l: row l / KC, chunk position l % KC). Keys past k1 - 1 copy key
+// k1 - 1 (masked later), so no table entry or row outside the sequence's range is read.
 template <int D>
 __device__ __forceinline__ void pf_copy(const AttnArgs &a, const int32_t *bt, const half_t *kcg,
-                                        const half_t *vcg, int kt, int k1, half_t *Kd, half_t *Vd,
-                                        int wave, int lane) {
+                                        const half_t *vcg, int kt, int k1, int pb, half_t *Kd,
+                                        half_t *Vd, int wave, int lane) {
     constexpr int KC = D / 8;          // 16-byte chunks per row
     constexpr int RPI = 64 / KC;       // rows per copy instruction
-    constexpr int IPW = 16 / RPI;      // copy instructions per wave and matrix
+    constexpr int IPW = kPfKpw / RPI;  // copy instructions per wave and matrix
     const int pos = lane % KC, rsub = lane / KC;
-    const int k16 = kt + 16 * wave;
     const uint32_t ke = a.key_elems;  // < 2^24 (checked on the host): 24-bit multiplies
-    const bool one_block = (a.bs & 15) == 0 && k16 + 15 < k1;
-    int j16 = 0;
-    size_t blk16 = 0;
-    if (one_block) {
-        j16 = a.log2bs >= 0 ? (k16 >> a.log2bs) : k16 / a.bs;
-        blk16 = (size_t)bt[j16] * a.block_elems;
-    }
+    const int kw = kt + kPfKpw * wave;
+    const int jw = a.log2bs >= 0 ? (kw >> a.log2bs) : kw / a.bs;
     for (int t = 0; t < IPW; ++t) {
-        const int r = 16 * wave + t * RPI + rsub;  // row within the tile
+        const int r = kPfKpw * wave + t * RPI + rsub;  // row within the tile
         size_t row;
-        if (one_block) {
-            row = blk16 + __umul24(kt + r - j16 * a.bs, ke);
+        if (pb >= 0) {
+            row = (size_t)pb * a.block_elems + __umul24(kt + r - jw * a.bs, ke);
         } else {
             const int key = min(kt + r, k1 - 1);
             const int j = a.log2bs >= 0 ? (key >> a.log2bs) : key / a.bs;
             row = (size_t)bt[j] * a.block_elems + __umul24(key - j * a.bs, ke);
         }
-        const int r0 = 16 * wave + t * RPI;        // first row of this instruction
+        const int r0 = kPfKpw * wave + t * RPI;    // first row of this instruction
         dma16(kcg + row + 8 * (pos ^ kmask<KC>(r)), Kd + r0 * D);
         dma16(vcg + row + 8 * (pos ^ vmask<KC>(r)), Vd + r0 * D);
     }
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
     constexpr int KB = D / 32;           // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;          // 16-dim output tiles
     constexpr int KC = D / 8;
-    static_assert(kKT == 16 * (kPfThreads / 64), "each wave copies 16 keys of a tile");
+    static_assert(kPfKpw * kPfWaves == kKT && kPfKpw % 8 == 0, "each wave copies whole rows");
     // Two stages of row-major K and V tiles (64 KB at D = 128: two workgroups per CU).
     __shared__ __attribute__((aligned(16))) half_t Ks[2][kKT * D];
     __shared__ __attribute__((aligned(16))) half_t Vs[2][kKT * D];
@@ -212,15 +217,22 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
         // overwrite), then issue the copies of tile ti + 1 and compute tile ti. The barrier is a
         // bare s_barrier: a workgroup fence would also wait for the copies just issued.
         const int ntl = (k1 + kKT - 1) / kKT;
-        if (ntl > 0) pf_copy<D>(a, bt, kcg, vcg, 0, k1, Ks[0], Vs[0], wave, lane);
+        int pbn = -1;  // pf_wave_block of the tile after the one whose copies are in flight
+        if (ntl > 0) {
+            pf_copy<D>(a, bt, kcg, vcg, 0, k1, pf_wave_block(a, bt, 0, k1, wave), Ks[0], Vs[0],
+                       wave, lane);
+            if (ntl > 1) pbn = pf_wave_block(a, bt, kKT, k1, wave);
+        }
         for (int ti = 0; ti < ntl; ++ti) {
             const int kt = ti * kKT;
             const half_t *Kb = Ks[ti & 1], *Vb = Vs[ti & 1];
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             asm volatile("s_barrier" ::: "memory");
-            if (ti + 1 < ntl)
-                pf_copy<D>(a, bt, kcg, vcg, kt + kKT, k1, Ks[(ti + 1) & 1], Vs[(ti + 1) & 1], wave,
-                           lane);
+            if (ti + 1 < ntl) {
+                pf_copy<D>(a, bt, kcg, vcg, kt + kKT, k1, pbn, Ks[(ti + 1) & 1], Vs[(ti + 1) & 1],
+                           wave, lane);
+                pbn = ti + 2 < ntl ? pf_wave_block(a, bt, kt + 2 * kKT, k1, wave) : -1;
+            }
             if (kt >= wave_end) continue;  // every column of this wave ends before the tile
 
             // S^T: keys 32s + 8*g16 + 4u + i of columns n16 (both column blocks per K read).
@@ -326,8 +338,8 @@ pa_status launch_prefill(const AttnArgs &a, int D, int blocks, const CombineArgs
         c = *cmb;
         // At most one combine workgroup per CU: max_groups is a bound (every row split); the
         // waves loop when more rows are split than they cover in one pass.
-        comb_blocks = (int)std::min<long long>((combine_waves(max_groups, c.lanes, D) + 3) / 4,
-                                               device_cu_count());
+        comb_blocks = (int)std::min<long long>(
+            (combine_waves(max_groups, c.lanes, D) + kPfWaves - 1) / kPfWaves, device_cu_count());
     }
     const int grid = blocks + comb_blocks;
     if (grid <= 0) return PA_OK;
