@@ -34,6 +34,7 @@ namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kTileKeys = 32;
 
+template <int TH>
 __device__ __forceinline__ long long block_sum_ll(long long v, long long *sh) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -41,15 +42,15 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *sh) {
     if (lane == 0) sh[wid] = v;
     __syncthreads();
     long long t = 0;
-    for (int i = 0; i < kPlanThreads / 64; ++i) t += sh[i];
+    for (int i = 0; i < TH / 64; ++i) t += sh[i];
     return t;
 }
 
 // Exclusive scan of NV counters across the workgroup; returns totals in tot[].
-template <int NV, int M>
+template <int TH, int NV, int M>
 __device__ __forceinline__ void block_scan(const int (&v)[NV], int (&excl)[NV], int (&tot)[NV],
                                            int (&sh)[M]) {
-    static_assert(M >= kPlanThreads / 64 * NV, "scan scratch: one entry per wave and counter");
+    static_assert(M >= TH / 64 * NV, "scan scratch: one entry per wave and counter");
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     int inc[NV];
     for (int k = 0; k < NV; ++k) {
@@ -66,7 +67,7 @@ __device__ __forceinline__ void block_scan(const int (&v)[NV], int (&excl)[NV], 
     __syncthreads();
     for (int k = 0; k < NV; ++k) {
         int before = 0, all = 0;
-        for (int i = 0; i < kPlanThreads / 64; ++i) {
+        for (int i = 0; i < TH / 64; ++i) {
             const int x = sh[i * NV + k];
             if (i < wid) before += x;
             all += x;
@@ -78,13 +79,15 @@ __device__ __forceinline__ void block_scan(const int (&v)[NV], int (&excl)[NV], 
 
 __device__ __forceinline__ int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Prefill items are listed longest first (by 64-key tiles, counting-sorted in LDS; items of
-// kPreBins - 1 or more tiles share the top bin), so that the persistent prefill workgroups take
-// the long items early and the short ones fill the tail.
-constexpr int kPreBins = 4 * kPlanThreads;
+// Prefill items are listed longest first (by 64-key tiles, counting-sorted in LDS over four bins
+// per planner thread; items of bins - 1 or more tiles share the top bin), so that the persistent
+// prefill workgroups take the long items early and the short ones fill the tail.
+template <int TH>
+constexpr int pre_bins() { return 4 * TH; }
 constexpr int kPreBinKeys = 64;
+template <int TH>
 __device__ __forceinline__ int pre_bin(int k1) {
-    return min(kPreBins - 1, (k1 + kPreBinKeys - 1) / kPreBinKeys);
+    return min(pre_bins<TH>() - 1, (k1 + kPreBinKeys - 1) / kPreBinKeys);
 }
 __device__ __forceinline__ int round_tile(long long x) {
     return (int)((x + kTileKeys - 1) / kTileKeys * kTileKeys);
@@ -104,12 +107,14 @@ __device__ __forceinline__ int round_tile(long long x) {
 //    of the combine list; a sequence left whole writes its output directly.
 //  * Longer sequences get tiles of tpi_pre rows; the prefill list holds them longest key range
 //    first across all sequences.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-    __shared__ long long sh_ll[kPlanThreads / 64];
-    __shared__ int sh_i[kPlanThreads / 64 * 5];  // block_scan<NV> needs (waves x NV)
+template <int TH>  // threads: 64 (one wave) or kPlanThreads
+__global__ __launch_bounds__(TH) void plan_kernel(PlanArgs a) {
+    constexpr int kPreBins = pre_bins<TH>();
+    __shared__ long long sh_ll[TH / 64];
+    __shared__ int sh_i[TH / 64 * 5];  // block_scan<NV> needs (waves x NV)
     __shared__ int sh_bin[kPreBins];  // prefill items per length bin, then list offsets
     const int tid = threadIdx.x;
-    for (int i = tid; i < kPreBins; i += kPlanThreads) sh_bin[i] = 0;
+    for (int i = tid; i < kPreBins; i += TH) sh_bin[i] = 0;
     const bool streamk = a.mode == 0;
 
     auto decode_like = [&](int n) { return n >= 1 && n <= a.tpi_dec; };
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         return a.causal ? past + min(n, (tile + 1) * a.tpi_pre) : past + n;
     };
 
-    // Sequence b's first token, new tokens and past length. The first kPlanThreads sequences are
+    // Sequence b's first token, new tokens and past length. The first TH sequences are
     // read once, here, and kept in registers for all passes (one memory round trip instead of
     // three); later chunks are read where they are needed.
     int r_cu0 = 0, r_n = 0, r_past = 0;
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         r_past = a.past[tid];
     }
     auto seq = [&](int b, int &cu0, int &n, int &past) {
-        if (b < kPlanThreads) {  // b == tid
+        if (b < TH) {  // b == tid
             cu0 = r_cu0; n = r_n; past = r_past;
         } else {
             cu0 = a.cu[b]; n = a.cu[b + 1] - cu0; past = a.past[b];
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
     // Pass 1: tiles of decode-like sequences; in even mode, the count of whole pieces.
     long long ntiles = 0, nfull = 0;
-    for (int b = tid; b < a.B; b += kPlanThreads) {
+    for (int b = tid; b < a.B; b += TH) {
         int cu0, n, past;
         seq(b, cu0, n, past);
         if (!decode_like(n)) continue;
@@ -150,8 +155,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             nfull += (L % Cb == 0) ? c : c - 1;
         }
     }
-    ntiles = block_sum_ll(ntiles, sh_ll);
-    const int full_total = (int)block_sum_ll(nfull, sh_ll);
+    ntiles = block_sum_ll<TH>(ntiles, sh_ll);
+    const int full_total = (int)block_sum_ll<TH>(nfull, sh_ll);
     long long q = 1;
     int used = 0;
     if (streamk && ntiles > 0) {
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int carry[4] = {0, 0, 0, 0};
     long long carry_tiles = 0;
     int carry_tail = 0;
-    for (int base = 0; base < a.B; base += kPlanThreads) {
+    for (int base = 0; base < a.B; base += TH) {
         const int b = base + tid;
         int n = 0, L = 0, past = 0, cu0 = 0, T = 0;
         if (b < a.B) {
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             if (decode_like(n)) T = ceil_div_i(L, kTileKeys);
         }
         int tv[1] = {T}, tex[1], ttot[1];
-        block_scan<1>(tv, tex, ttot, sh_i);
+        block_scan<TH, 1>(tv, tex, ttot, sh_i);
         const long long TB = carry_tiles + tex[0];   // first global tile of sequence b
         int c = 0, Cb = 1, tail = 0;
         int cnt[5] = {0, 0, 0, 0, 0};  // items, partial units, combine rows, prefill, tail
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
         cnt[4] = tail;
         int ex[5], tot[5];
-        block_scan<5>(cnt, ex, tot, sh_i);
+        block_scan<TH, 5>(cnt, ex, tot, sh_i);
         const int tlex = ex[4];
         if (b < a.B) {
             const int ubase = carry[1] + ex[1];
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                 }
             }
             for (int tile = 0; tile < cnt[3]; ++tile)
-                atomicAdd(&sh_bin[pre_bin(pre_k1(tile, n, past))], 1);
+                atomicAdd(&sh_bin[pre_bin<TH>(pre_k1(tile, n, past))], 1);
         }
         for (int k = 0; k < 4; ++k) carry[k] += tot[k];
         carry_tiles += ttot[0];
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             s4 += c4[i];
         }
         int sv[1] = {s4}, sex[1], stot[1];
-        block_scan<1>(sv, sex, stot, sh_i);
+        block_scan<TH, 1>(sv, sex, stot, sh_i);
         int run = sex[0];
         for (int i = 0; i < 4; ++i) {
             sh_bin[kPreBins - 1 - (4 * tid + i)] = run;
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
         __syncthreads();
     }
-    for (int b = tid; b < a.B && carry[3] > 0; b += kPlanThreads) {
+    for (int b = tid; b < a.B && carry[3] > 0; b += TH) {
         int cu0, n, past;
         seq(b, cu0, n, past);
         if (n <= a.tpi_dec) continue;
@@ -269,13 +274,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             it.b = b; it.t0 = tile * a.tpi_pre; it.k0 = 0;
             it.k1 = pre_k1(tile, n, past);
             it.base = -1; it.nsplit = 1; it.split = 0; it.comb = -1;
-            const int idx = atomicAdd(&sh_bin[pre_bin(it.k1)], 1);
+            const int idx = atomicAdd(&sh_bin[pre_bin<TH>(it.k1)], 1);
             if (idx < a.cap_pre) a.pre[idx] = it;
         }
     }
     const int ndec_items = min(carry[0], a.cap_dec);
     if (streamk)
-        for (int j = used + tid; j <= a.slots; j += kPlanThreads) a.slot_ptr[j] = ndec_items;
+        for (int j = used + tid; j <= a.slots; j += TH) a.slot_ptr[j] = ndec_items;
     if (tid == 0) {
         a.hdr->n_dec = ndec_items;
         a.hdr->units = carry[1];
@@ -289,7 +294,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
 pa_status launch_plan(const PlanArgs &a, hipStream_t stream) {
     LaunchScope scope("plan", stream);
-    scope.launch(plan_kernel, dim3(1), dim3(kPlanThreads), 0, a);
+    // one wave when the batch fits in it: the scans and barriers stay inside the wave
+    if (a.B <= 64) scope.launch(plan_kernel<64>, dim3(1), dim3(64), 0, a);
+    else scope.launch(plan_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), 0, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -218,6 +218,29 @@ def test_append_stress_bit_exact():
     assert_bits_equal(c.value_cache, vc, "value_cache")
 
 
+@pytest.mark.parametrize("B", [100, 300])
+@pytest.mark.parametrize("num_splits", [pa.PA_SPLITS_AUTO, pa.PA_SPLITS_PAGE_RULE, 3],
+                         ids=lambda s: f"S{s}")
+def test_many_sequences_attention(B, num_splits):
+    """More sequences than one planner wave (100) and than one planner chunk (300): one-token
+    decodes on varied past lengths, every 37th sequence a 40-token prefill, one empty sequence."""
+    def past(r):
+        return r.integers(0, 400, size=B)
+
+    def n_new(r):
+        n = np.ones(B, dtype=np.int64)
+        n[::37] = 40
+        n[B // 2] = 0
+        return n
+
+    w = W.paged_workload(150 + B, past=past, n_new=n_new, num_heads=8, kv_num_heads=2,
+                         head_size=64, block_size=16, table="pool", name=f"many{B}")
+    kc, vc, ref = _oracle(w)
+    c, out = _run(w, num_splits)
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_attention_close(out, ref, f"B={B}")
+
+
 @pytest.mark.parametrize("causal", [0, 1])
 def test_non_causal_and_prefill(causal):
     w = W.paged_workload(110, past=[3, 60, 0], n_new=[33, 1, 17], num_heads=8, kv_num_heads=2,
