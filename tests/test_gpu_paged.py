@@ -82,6 +82,10 @@ PREFILL = [
     dict(seed=125, past=[1000, 3], n_new=[300, 1], num_heads=16, kv_num_heads=2,
          head_size=128, block_size=16, packed=True, rotary_mode=W.ROTARY_NEOX,
          rotary_dim=64, rotary_positions=1400),                       # Q = 8, packed, rotary
+    dict(seed=126, past=[50, 7], n_new=[70, 33], num_heads=8, kv_num_heads=2, head_size=128,
+         block_size=48),                      # bs a multiple of 16, not a power of two: divides
+    dict(seed=127, past=[100, 20], n_new=[65, 1], num_heads=4, kv_num_heads=1, head_size=64,
+         block_size=24),                      # bs a multiple of 8, not of 16: per-key lookups
 ]
 
 
