@@ -107,6 +107,10 @@ pa_status check_shape(const pa_paged_shape *s) {
     if (s->head_size != 64 && s->head_size != 128) return PA_ERR_UNSUPPORTED;
     if (s->num_heads / s->kv_num_heads > 64) return PA_ERR_UNSUPPORTED;
     if ((long long)s->kv_num_heads * s->head_size >= (1LL << 24)) return PA_ERR_UNSUPPORTED;
+    // the kernels form in-block row offsets with 24 x 24-bit multiplies: a block's elements
+    // must fit in 32 bits
+    if ((long long)s->block_size * s->kv_num_heads * s->head_size >= (1LL << 32))
+        return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
 

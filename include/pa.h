@@ -108,7 +108,8 @@ typedef struct pa_paged_shape {
  *
  * Rotary arithmetic: two float32 products (each rounded), one float32 add or subtract, then
  * round-to-nearest-even to fp16; the first member of a pair subtracts its partner's sine term.
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_HIP.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (D not 64/128, H/G > 64, G*D >= 2^24,
+ * bs*G*D >= 2^32: the shape limits every paged entry shares), PA_ERR_HIP.
  */
 pa_status pa_kv_append(const pa_paged_shape *shape, const void *query, const void *key,
                        const void *value, void *key_cache, void *value_cache,
@@ -174,9 +175,10 @@ size_t pa_paged_attention_workspace_size(const pa_paged_shape *shape, int32_t nu
  *            pa_paged_attention_workspace_size(shape, num_splits) bytes, 256-byte aligned
  *   output   fp16 [T, H*D]
  * Rows of a sequence with n_b * (H/G) <= 16 (<= 32 or 64 for H/G above 16 or 32) are
- * decode-like and split-KV eligible; longer sequences run as query tiles of 32 (token, head)
- * columns on the chunked-prefill path, each covering its causal key range in one pass.
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (D not 64/128, H/G > 64),
+ * decode-like and split-KV eligible; longer sequences run on the chunked-prefill path as items
+ * of 128 (token, head) columns (128 / (H/G) tokens of one kv head group), each covering its
+ * causal key range in one pass.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (the shape limits of pa_kv_append),
  * PA_ERR_WORKSPACE, PA_ERR_HIP.
  */
 pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,

@@ -53,6 +53,9 @@ def _append(shape, **kw):
     (dict(num_tokens=-1), pa.PA_ERR_SHAPE),
     (dict(head_size=96), pa.PA_ERR_UNSUPPORTED),
     (dict(num_heads=128, kv_num_heads=1), pa.PA_ERR_UNSUPPORTED),  # qPerKv > 64
+    # a block's elements must fit in 32 bits (24-bit in-block offset products)
+    (dict(num_heads=64, kv_num_heads=64, head_size=128, block_size=1 << 19),
+     pa.PA_ERR_UNSUPPORTED),
 ])
 def test_append_rejects_bad_shapes(bad, expect):
     assert _append(_shape(**bad)) == expect
