@@ -245,6 +245,43 @@ def test_many_sequences_attention(B, num_splits):
     assert_attention_close(out, ref, f"B={B}")
 
 
+@pytest.mark.parametrize("num_splits", [pa.PA_SPLITS_AUTO, 3], ids=lambda s: f"S{s}")
+def test_graph_capture_replays_match_eager(num_splits):
+    """The append and the attention call captured into one HIP graph (the library enqueues
+    kernels only: no allocation, memset or synchronization): every replay, with eager library
+    work between replays, is bit-identical to the eager step."""
+    w = W.paged_workload(160, past=[40, 300, 5, 1000], n_new=[1, 70, 1, 33], num_heads=8,
+                         kv_num_heads=2, head_size=128, block_size=16, table="pool",
+                         name="graph")
+    c = dev.PagedCase(w)
+    c.append()
+    ref = c.attention(num_splits).clone()  # eager; also sizes the workspace outside the graph
+    torch.cuda.synchronize()
+    kc_ref, vc_ref = c.key_cache.clone(), c.value_cache.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        c.append()
+        c.attention(num_splits)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        c.append()
+        c.attention(num_splits)
+    for i in range(3):
+        c.output.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(c.output, ref, f"replay {i}")
+        assert_bits_equal(c.key_cache, kc_ref, f"key_cache after replay {i}")
+        assert_bits_equal(c.value_cache, vc_ref, f"value_cache after replay {i}")
+        eager = c.attention(num_splits, out=torch.empty_like(ref))
+        torch.cuda.synchronize()
+        assert_bits_equal(eager, ref, f"eager after replay {i}")
+
+
 @pytest.mark.parametrize("causal", [0, 1])
 def test_non_causal_and_prefill(causal):
     w = W.paged_workload(110, past=[3, 60, 0], n_new=[33, 1, 17], num_heads=8, kv_num_heads=2,
