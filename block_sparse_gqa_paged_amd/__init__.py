@@ -23,7 +23,7 @@ PA_F16, PA_F32 = 0, 1
 PA_SPLITS_AUTO, PA_SPLITS_PAGE_RULE = 0, -1
 
 EXPORTED = ("pa_kv_append", "pa_kv_append_rotate_query", "pa_paged_attention_workspace_size",
-            "pa_paged_attention",
+            "pa_paged_attention", "pa_append_attention",
             "pa_split_combine", "pa_sparse_forward_workspace_size", "pa_sparse_forward",
             "pa_sparse_forward_causal", "pa_sparse_build_edges_workspace_size",
             "pa_sparse_build_edges", "pa_kv_append_bnsh",
@@ -81,6 +81,9 @@ def lib():
     L.pa_paged_attention.argtypes = ([sp] + [_vp] * 6 + [C.c_float, _i32, _i32, _vp, C.c_size_t,
                                                          _vp, _vp])
     L.pa_paged_attention.restype = _i32
+    L.pa_append_attention.argtypes = ([sp] + [_vp] * 11 + [_i32, _i32, _i32, _vp, C.c_float,
+                                      _i32, _i32, _vp, C.c_size_t, _vp, _vp])
+    L.pa_append_attention.restype = _i32
     L.pa_split_combine.argtypes = [_vp] * 4 + [_i32] * 5 + [_vp, _vp]
     L.pa_split_combine.restype = _i32
     L.pa_sparse_forward_workspace_size.argtypes = [ss]
@@ -189,6 +192,21 @@ def pa_paged_attention(shape, query, key_cache, value_cache, cumulative_sequence
         int(causal), int(num_splits), _p(workspace), int(workspace_bytes), _p(output),
         _s(stream))
     return _check(st, "pa_paged_attention", check)
+
+
+def pa_append_attention(shape, query, key, value, key_cache, value_cache,
+                        cumulative_sequence_length, past_seqlens, block_table, scale, causal,
+                        num_splits, workspace, workspace_bytes, output, slot_mapping=None,
+                        cos_cache=None, sin_cache=None, rotary_dim=0,
+                        rotary_mode=PA_ROTARY_NONE, rotary_positions=0, q_out=None,
+                        stream=None, check=True):
+    st = lib().pa_append_attention(
+        C.byref(shape), _p(query), _p(key), _p(value), _p(key_cache), _p(value_cache),
+        _p(cumulative_sequence_length), _p(past_seqlens), _p(block_table), _p(slot_mapping),
+        _p(cos_cache), _p(sin_cache), int(rotary_dim), int(rotary_mode), int(rotary_positions),
+        _p(q_out), float(scale), int(causal), int(num_splits), _p(workspace),
+        int(workspace_bytes), _p(output), _s(stream))
+    return _check(st, "pa_append_attention", check)
 
 
 def pa_split_combine(o_partial, m_partial, l_partial, group_ptr, num_groups, lanes, num_splits,

@@ -238,13 +238,14 @@ pa_status pa_timing_get(const char *kernel, double *total_ms, int64_t *launches)
     return st;
 }
 
-static pa_status kv_append(const pa_paged_shape *shape, const void *query, const void *key,
-                           const void *value, void *key_cache, void *value_cache,
-                           const int32_t *cumulative_sequence_length,
-                           const int32_t *past_seqlens, const int32_t *block_table,
-                           const int32_t *slot_mapping, const void *cos_cache,
-                           const void *sin_cache, int32_t rotary_dim, int32_t rotary_mode,
-                           int32_t rotary_positions, void *q_out, void *stream) {
+// Checks and kernel arguments of one append (nothing is enqueued).
+static pa_status make_append(const pa_paged_shape *shape, const void *query, const void *key,
+                             const void *value, void *key_cache, void *value_cache,
+                             const int32_t *cumulative_sequence_length,
+                             const int32_t *past_seqlens, const int32_t *block_table,
+                             const int32_t *slot_mapping, const void *cos_cache,
+                             const void *sin_cache, int32_t rotary_dim, int32_t rotary_mode,
+                             int32_t rotary_positions, void *q_out, AppendArgs &a) {
     pa_status st = check_shape(shape);
     if (st != PA_OK) return st;
     const pa_paged_shape &s = *shape;
@@ -267,8 +268,6 @@ static pa_status kv_append(const pa_paged_shape *shape, const void *query, const
             return PA_ERR_SHAPE;
         if (!cos_cache || !sin_cache) return PA_ERR_NULL;
     }
-    if (s.num_tokens == 0) return PA_OK;
-    AppendArgs a;
     const int H = s.num_heads, G = s.kv_num_heads, D = s.head_size;
     a.query = s.packed_qkv ? (const half_t *)query : nullptr;
     a.key = (const half_t *)key;
@@ -297,6 +296,22 @@ static pa_status kv_append(const pa_paged_shape *shape, const void *query, const
     a.q_stride = s.packed_qkv ? (int64_t)(H + 2 * G) * D : (int64_t)H * D;
     a.H = H;
     a.nkv = a.nkv_pad = a.nq = 0;  // set by the launcher
+    return s.num_tokens == 0 ? PA_OK : check_kv_append(a);
+}
+
+static pa_status kv_append(const pa_paged_shape *shape, const void *query, const void *key,
+                           const void *value, void *key_cache, void *value_cache,
+                           const int32_t *cumulative_sequence_length,
+                           const int32_t *past_seqlens, const int32_t *block_table,
+                           const int32_t *slot_mapping, const void *cos_cache,
+                           const void *sin_cache, int32_t rotary_dim, int32_t rotary_mode,
+                           int32_t rotary_positions, void *q_out, void *stream) {
+    AppendArgs a;
+    pa_status st = make_append(shape, query, key, value, key_cache, value_cache,
+                               cumulative_sequence_length, past_seqlens, block_table,
+                               slot_mapping, cos_cache, sin_cache, rotary_dim, rotary_mode,
+                               rotary_positions, q_out, a);
+    if (st != PA_OK || shape->num_tokens == 0) return st;
     return launch_kv_append(a, (hipStream_t)stream);
 }
 
@@ -335,12 +350,26 @@ size_t pa_paged_attention_workspace_size(const pa_paged_shape *shape, int32_t nu
     return p.total;
 }
 
-pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
-                             const void *key_cache, const void *value_cache,
-                             const int32_t *cumulative_sequence_length,
-                             const int32_t *past_seqlens, const int32_t *block_table, float scale,
-                             int32_t causal, int32_t num_splits, void *workspace,
-                             size_t workspace_bytes, void *output, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Everything one attention call launches, prepared and checked before anything is enqueued.
+struct AttnCall {
+    PlanArgs pl;
+    AttnArgs a;
+    CombineArgs c;
+    int D, ncb_dec, blocks, pblocks, cap_comb;
+    bool combine;
+};
+
+// q_stride: the query row stride in elements.
+pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t q_stride,
+                         const void *key_cache, const void *value_cache,
+                         const int32_t *cumulative_sequence_length, const int32_t *past_seqlens,
+                         const int32_t *block_table, float scale, int32_t causal,
+                         int32_t num_splits, void *workspace, size_t workspace_bytes,
+                         void *output, AttnCall &call) {
     pa_status st = check_shape(shape);
     if (st != PA_OK) return st;
     if (causal != 0 && causal != 1) return PA_ERR_SHAPE;
@@ -355,11 +384,10 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     if (!workspace) return PA_ERR_NULL;
     if (workspace_bytes < p.total || ((uintptr_t)workspace % kAlign) != 0)
         return PA_ERR_WORKSPACE;
-    hipStream_t strm = (hipStream_t)stream;
     char *ws = (char *)workspace;
     const int H = s.num_heads, G = s.kv_num_heads, D = s.head_size;
 
-    PlanArgs pl;
+    PlanArgs &pl = call.pl;
     pl.cu = cumulative_sequence_length;
     pl.past = past_seqlens;
     pl.B = s.batch;
@@ -380,10 +408,9 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     pl.dec = (AttnItem *)(ws + p.off_dec);
     pl.pre = (AttnItem *)(ws + p.off_pre);
     pl.comb = (CombItem *)(ws + p.off_comb);
-    if ((st = launch_plan(pl, strm)) != PA_OK) return st;
 
     const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)D);
-    AttnArgs a;
+    AttnArgs &a = call.a;
     a.query = (const half_t *)query;
     a.kc = (const half_t *)key_cache;
     a.vc = (const half_t *)value_cache;
@@ -394,7 +421,7 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     a.o_part = (float *)(ws + p.off_o);
     a.m_part = (float *)(ws + p.off_m);
     a.l_part = (float *)(ws + p.off_l);
-    a.q_stride = s.packed_qkv ? (int64_t)(H + 2 * G) * D : (int64_t)H * D;
+    a.q_stride = q_stride;
     a.block_elems = (int64_t)s.block_size * G * D;
     a.key_elems = (uint32_t)(G * D);
     a.H = H;
@@ -412,30 +439,23 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     a.n_items = &pl.hdr->n_dec;
     a.counter = &pl.hdr->next_dec;
     a.tpi = p.tpi_dec;
-    int blocks;
     if (p.mode == 0) {
         a.slot_ptr = pl.slot_ptr;
-        blocks = p.slots;
+        call.blocks = p.slots;
     } else {
         a.slot_ptr = nullptr;
         const long long units = (long long)p.cap_dec * (G / p.gw);
-        blocks = (int)std::min(units, (long long)cus * kWavesPerCu / p.gw);
+        call.blocks = (int)std::min(units, (long long)cus * kWavesPerCu / p.gw);
     }
-    if ((st = launch_attention(a, D, p.ncb_dec, blocks, "attn_decode", strm)) != PA_OK)
-        return st;
-
-    a.items = pl.pre;
-    a.n_items = &pl.hdr->n_pre;
-    a.counter = &pl.hdr->next_pre;
-    a.slot_ptr = nullptr;
-    a.tpi = p.tpi_pre;
-    a.gw = 1;
+    call.D = D;
+    call.ncb_dec = p.ncb_dec;
     const long long pre_units = (long long)p.cap_pre * G;
     // persistent prefill workgroups: as many as fit at once (two waves per SIMD)
-    const int pblocks = (int)std::min(pre_units, (long long)cus * 8 / (kPrefillCols / 32));
-
+    call.pblocks = (int)std::min(pre_units, (long long)cus * 8 / (kPrefillCols / 32));
+    call.cap_comb = p.cap_comb;
+    call.combine = p.unit_cap > 0;
     // The split decode rows are merged by extra workgroups of the prefill launch.
-    CombineArgs c;
+    CombineArgs &c = call.c;
     c.o = a.o_part;
     c.m = a.m_part;
     c.l = a.l_part;
@@ -448,7 +468,78 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     c.D = D;
     c.out_f32 = 0;
     c.out = output;
-    return launch_prefill(a, D, pblocks, p.unit_cap > 0 ? &c : nullptr, p.cap_comb, strm);
+    return PA_OK;
+}
+
+// The decode launch, then the prefill launch (which also merges the split decode rows); the
+// planner has run before them on the same stream.
+pa_status run_attention(const AttnCall &call, int tpi_pre, hipStream_t strm) {
+    AttnArgs a = call.a;
+    pa_status st = launch_attention(a, call.D, call.ncb_dec, call.blocks, "attn_decode", strm);
+    if (st != PA_OK) return st;
+    a.items = call.pl.pre;
+    a.n_items = &call.pl.hdr->n_pre;
+    a.counter = &call.pl.hdr->next_pre;
+    a.slot_ptr = nullptr;
+    a.tpi = tpi_pre;
+    a.gw = 1;
+    return launch_prefill(a, call.D, call.pblocks, call.combine ? &call.c : nullptr,
+                          call.cap_comb, strm);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
+                             const void *key_cache, const void *value_cache,
+                             const int32_t *cumulative_sequence_length,
+                             const int32_t *past_seqlens, const int32_t *block_table, float scale,
+                             int32_t causal, int32_t num_splits, void *workspace,
+                             size_t workspace_bytes, void *output, void *stream) {
+    if (!shape) return PA_ERR_NULL;
+    const int64_t H = shape->num_heads, G = shape->kv_num_heads, D = shape->head_size;
+    AttnCall call;
+    pa_status st = make_attention(shape, query, shape->packed_qkv ? (H + 2 * G) * D : H * D,
+                                  key_cache, value_cache, cumulative_sequence_length,
+                                  past_seqlens, block_table, scale, causal, num_splits,
+                                  workspace, workspace_bytes, output, call);
+    if (st != PA_OK || shape->num_tokens == 0) return st;
+    hipStream_t strm = (hipStream_t)stream;
+    if ((st = launch_plan(call.pl, strm)) != PA_OK) return st;
+    return run_attention(call, call.pl.tpi_pre, strm);
+}
+
+pa_status pa_append_attention(const pa_paged_shape *shape, const void *query, const void *key,
+                              const void *value, void *key_cache, void *value_cache,
+                              const int32_t *cumulative_sequence_length,
+                              const int32_t *past_seqlens, const int32_t *block_table,
+                              const int32_t *slot_mapping, const void *cos_cache,
+                              const void *sin_cache, int32_t rotary_dim, int32_t rotary_mode,
+                              int32_t rotary_positions, void *q_out, float scale,
+                              int32_t causal, int32_t num_splits, void *workspace,
+                              size_t workspace_bytes, void *output, void *stream) {
+    if (!shape) return PA_ERR_NULL;
+    if (!query) return PA_ERR_NULL;
+    if (q_out && q_out == query) return PA_ERR_SHAPE;  // rotated rows go to their own buffer
+    AppendArgs ap;
+    pa_status st = make_append(shape, query, key, value, key_cache, value_cache,
+                               cumulative_sequence_length, past_seqlens, block_table,
+                               slot_mapping, cos_cache, sin_cache, rotary_dim, rotary_mode,
+                               rotary_positions, q_out, ap);
+    if (st != PA_OK) return st;
+    const int64_t H = shape->num_heads, G = shape->kv_num_heads, D = shape->head_size;
+    // attention reads the rotated rows [T, H*D] when q_out is given, else the query as passed
+    const void *q_attn = q_out ? q_out : query;
+    const int64_t q_stride = q_out ? H * D : (shape->packed_qkv ? (H + 2 * G) * D : H * D);
+    AttnCall call;
+    st = make_attention(shape, q_attn, q_stride, key_cache, value_cache,
+                        cumulative_sequence_length, past_seqlens, block_table, scale, causal,
+                        num_splits, workspace, workspace_bytes, output, call);
+    if (st != PA_OK || shape->num_tokens == 0) return st;
+    hipStream_t strm = (hipStream_t)stream;
+    if ((st = launch_append_plan(ap, call.pl, strm)) != PA_OK) return st;
+    return run_attention(call, call.pl.tpi_pre, strm);
 }
 
 pa_status pa_split_combine(const float *o_partial, const float *m_partial,

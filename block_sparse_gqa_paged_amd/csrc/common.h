@@ -143,6 +143,10 @@ struct PlanArgs {
     CombItem *comb;
 };
 pa_status launch_plan(const PlanArgs &a, hipStream_t stream);
+// The key/value append and the planner in one launch (workgroup 0 plans, the rest append).
+pa_status launch_append_plan(const AppendArgs &a, const PlanArgs &p, hipStream_t stream);
+// The checks of launch_kv_append that depend on the launch size, without launching.
+pa_status check_kv_append(const AppendArgs &a);
 
 struct AttnArgs {
     const half_t *query;

@@ -21,7 +21,12 @@
 //
 // Rotary arithmetic is the page's float32 expression with contraction disabled: two rounded
 // products, one rounded add or subtract, then round-to-nearest-even to fp16.
+//
+// append_plan_kernel runs the same append beside the paged-attention planner (plan.h): the
+// planner reads only the sequence lengths, which the append does not change, so the two share
+// one launch when a caller asks for the append and the attention in one call.
 #include "common.h"
+#include "plan.h"
 
 namespace pa {
 namespace {
@@ -296,6 +301,24 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         append_pairs<MODE, LANECU, true>(a, gid - a.nkv_pad, a.nq, s_cu, s_past);
 }
 
+// Workgroup 0 runs the planner (on its first PTH threads; the other waves exit at once); the
+// rest run append_kernel's roles with workgroup indexes shifted by one.
+template <int MODE, bool LANECU, int PTH>
+__global__ __launch_bounds__(kThreads) void append_plan_kernel(AppendArgs a, PlanArgs p) {
+    __shared__ int32_t s_cu[LANECU ? 1 : kLdsCu];
+    __shared__ int32_t s_past[LANECU ? 1 : kLdsCu];
+    if (blockIdx.x == 0) {
+        if ((int)threadIdx.x >= PTH) return;  // whole waves: PTH is a multiple of 64
+        plan_body<PTH>(p);
+        return;
+    }
+    const int gid = (blockIdx.x - 1) * kThreads + threadIdx.x;
+    if (gid < a.nkv_pad)
+        append_pairs<MODE, LANECU, false>(a, gid, a.nkv, s_cu, s_past);
+    else
+        append_pairs<MODE, LANECU, true>(a, gid - a.nkv_pad, a.nq, s_cu, s_past);
+}
+
 // The append page's own pass over a contiguous BNSH cache [B, KVH, max_seq, D]: thread gid takes
 // chunk pair j of new token t of (batch b, kv head h), with j fastest, then t, so a wave's
 // stores run along consecutive cache rows of one head. past(b) is the padded-batch rule.
@@ -377,27 +400,40 @@ pa_status launch_kv_append_bnsh(const BnshArgs &a, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-pa_status launch_kv_append(const AppendArgs &a_in, hipStream_t stream) {
-    LaunchScope scope("kv_append", stream);
-    AppendArgs a = a_in;
+namespace {
+
+// Thread counts and the rotary variant of one append launch; false when the launch would need
+// more than 32-bit thread indexes.
+bool size_append(AppendArgs &a, unsigned &grid, int &mode) {
     const long long pairs = (long long)((a.T + 1) / 2) * (a.D >> 4);  // per head row
     const long long nkv = pairs * a.G;
     const long long nkv_pad = (nkv + kThreads - 1) / kThreads * kThreads;
     const long long nq = a.q_out ? pairs * a.H : 0;
     const long long total = nkv_pad + nq;
-    if (nkv == 0) return PA_OK;
-    if (a.q_out && !a.q_src) return PA_ERR_NULL;
-    if (total + kThreads >= (1LL << 31)) return PA_ERR_UNSUPPORTED;  // 32-bit thread indexing
+    if (total + 2 * kThreads >= (1LL << 31)) return false;  // 32-bit thread indexing
     a.nkv = (int)nkv;
     a.nkv_pad = (int)nkv_pad;
     a.nq = (int)nq;
-    const unsigned grid = (unsigned)((total + kThreads - 1) / kThreads);
+    grid = (unsigned)((total + kThreads - 1) / kThreads);
     const int R = a.rotary_dim;
-    int mode = kCopy;
+    mode = kCopy;
     if (a.rotary_mode == PA_ROTARY_NEOX)
         mode = R == a.D ? kNeoxFull : (R % 16 == 0 ? kNeox : kGeneric);
     else if (a.rotary_mode == PA_ROTARY_INTERLEAVED)
         mode = (R % 8 == 0) ? kInter : kGeneric;
+    return true;
+}
+
+}  // namespace
+
+pa_status launch_kv_append(const AppendArgs &a_in, hipStream_t stream) {
+    LaunchScope scope("kv_append", stream);
+    AppendArgs a = a_in;
+    if (a.T == 0) return PA_OK;
+    if (a.q_out && !a.q_src) return PA_ERR_NULL;
+    unsigned grid;
+    int mode;
+    if (!size_append(a, grid, mode)) return PA_ERR_UNSUPPORTED;
     const bool lanecu = a.B + 1 <= kLaneCu * 64;
 #define PA_APPEND(M)                                                                    \
     if (lanecu)                                                                         \
@@ -412,6 +448,48 @@ pa_status launch_kv_append(const AppendArgs &a_in, hipStream_t stream) {
         default: PA_APPEND(kGeneric); break;
     }
 #undef PA_APPEND
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status check_kv_append(const AppendArgs &a_in) {
+    AppendArgs a = a_in;
+    unsigned grid;
+    int mode;
+    if (a.q_out && !a.q_src) return PA_ERR_NULL;
+    return size_append(a, grid, mode) ? PA_OK : PA_ERR_UNSUPPORTED;
+}
+
+pa_status launch_append_plan(const AppendArgs &a_in, const PlanArgs &p, hipStream_t stream) {
+    LaunchScope scope("append_plan", stream);
+    AppendArgs a = a_in;
+    if (a.q_out && !a.q_src) return PA_ERR_NULL;
+    unsigned grid;
+    int mode;
+    if (!size_append(a, grid, mode)) return PA_ERR_UNSUPPORTED;
+    grid += 1;  // workgroup 0: the planner
+    const bool lanecu = a.B + 1 <= kLaneCu * 64;
+    const bool wave = p.B <= 64;  // the one-wave planner when the batch fits in a wave
+#define PA_AP(M, LC)                                                                         \
+    if (wave)                                                                                \
+        scope.launch(append_plan_kernel<M, LC, 64>, dim3(grid), dim3(kThreads), 0, a, p);    \
+    else                                                                                     \
+        scope.launch(append_plan_kernel<M, LC, kPlanThreads>, dim3(grid), dim3(kThreads), 0, \
+                     a, p);
+#define PA_APM(M)    \
+    if (lanecu) {    \
+        PA_AP(M, true)  \
+    } else {         \
+        PA_AP(M, false) \
+    }
+    switch (mode) {
+        case kCopy: PA_APM(kCopy); break;
+        case kNeoxFull: PA_APM(kNeoxFull); break;
+        case kNeox: PA_APM(kNeox); break;
+        case kInter: PA_APM(kInter); break;
+        default: PA_APM(kGeneric); break;
+    }
+#undef PA_APM
+#undef PA_AP
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

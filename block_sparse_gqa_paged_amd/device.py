@@ -7,8 +7,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, bnsh_shape, pa_kv_append, pa_kv_append_bnsh,
-               pa_kv_append_rotate_query,
+from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, bnsh_shape, pa_append_attention, pa_kv_append,
+               pa_kv_append_bnsh, pa_kv_append_rotate_query,
                pa_paged_attention,
                pa_paged_attention_workspace_size, pa_sparse_build_edges,
                pa_sparse_build_edges_workspace_size, pa_sparse_forward, pa_sparse_forward_causal,
@@ -88,6 +88,23 @@ class PagedCase:
                            w["scale"] if scale is None else scale,
                            w["causal"] if causal is None else causal, num_splits, ws, n, out,
                            stream=stream)
+        return out
+
+    def append_attention(self, num_splits=PA_SPLITS_AUTO, q_out=None, use_slot_mapping=True,
+                         causal=None, scale=None, out=None, stream=None):
+        """The append and the attention in one call (pa_append_attention). With q_out
+        (fp16 [T, H*D]) the query rows are rotated into it and the attention reads them."""
+        w = self.w
+        ws, n = self.workspace_for(num_splits)
+        out = self.output if out is None else out
+        pa_append_attention(
+            self.shape, self.query, self.key, self.value, self.key_cache, self.value_cache,
+            self.cu, self.past, self.block_table, w["scale"] if scale is None else scale,
+            w["causal"] if causal is None else causal, num_splits, ws, n, out,
+            slot_mapping=self.slot_mapping if use_slot_mapping else None, cos_cache=self.cos,
+            sin_cache=self.sin, rotary_dim=w["rotary_dim"], rotary_mode=w["rotary_mode"],
+            rotary_positions=0 if self.cos is None else self.cos.shape[0], q_out=q_out,
+            stream=stream)
         return out
 
 

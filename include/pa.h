@@ -10,6 +10,7 @@
  *   pa_sparse_forward_causal   the sparse forward with a per-row causal key limit
  *   pa_sparse_build_edges      the sparse forward's edge list from a kept-block mask
  *   pa_kv_append_bnsh          the append into a contiguous BNSH cache (the append page's own)
+ *   pa_append_attention        the append and the attention in one call (the manifest's op)
  *
  * Sources. Argument names and layouts follow three web pages:
  *   [manifest] "com.microsoft.PagedAttention ... manifest.json": the op's inputs, outputs,
@@ -187,6 +188,36 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
                              const int32_t *past_seqlens, const int32_t *block_table, float scale,
                              int32_t causal, int32_t num_splits, void *workspace,
                              size_t workspace_bytes, void *output, void *stream);
+
+/*
+ * pa_append_attention - the whole op of [manifest]: pass "scatter" and then the attention
+ * passes ("main", "split_attention", "merge"), in one call.
+ *
+ * Same results, bit for bit, as pa_kv_append (q_out NULL) or pa_kv_append_rotate_query (q_out
+ * given) followed on the same stream by pa_paged_attention over the query as passed (q_out
+ * NULL) or over q_out as fp16 [T, H*D] rows (q_out given). The append and the attention's
+ * planner share one launch: the planner reads only cumulative_sequence_length and past_seqlens,
+ * which the append does not write.
+ *   query     required; packed rows (shape->packed_qkv = 1) or fp16 [T, H*D]
+ *   key, value, key_cache, value_cache, cumulative_sequence_length, past_seqlens,
+ *   block_table, slot_mapping, cos_cache, sin_cache, rotary_dim, rotary_mode,
+ *   rotary_positions  as pa_kv_append (block_table is required here: attention reads it)
+ *   q_out     NULL, or fp16 [T, H*D] for the rotated query rows as pa_kv_append_rotate_query
+ *   scale, causal, num_splits, workspace, workspace_bytes, output  as pa_paged_attention
+ *             (the workspace size is pa_paged_attention_workspace_size(shape, num_splits))
+ * Every argument of both parts is checked before anything is enqueued.
+ * Errors: the union of those of pa_kv_append_rotate_query and pa_paged_attention;
+ * PA_ERR_NULL when query is NULL; PA_ERR_SHAPE when q_out == query.
+ */
+pa_status pa_append_attention(const pa_paged_shape *shape, const void *query, const void *key,
+                              const void *value, void *key_cache, void *value_cache,
+                              const int32_t *cumulative_sequence_length,
+                              const int32_t *past_seqlens, const int32_t *block_table,
+                              const int32_t *slot_mapping, const void *cos_cache,
+                              const void *sin_cache, int32_t rotary_dim, int32_t rotary_mode,
+                              int32_t rotary_positions, void *q_out, float scale,
+                              int32_t causal, int32_t num_splits, void *workspace,
+                              size_t workspace_bytes, void *output, void *stream);
 
 /*
  * pa_split_combine - log-sum-exp merge of partial attention results.

@@ -122,6 +122,38 @@ def test_attention_rejects_bad_arguments():
     assert _attn(_shape(num_tokens=0), workspace=None) == pa.PA_OK
 
 
+def _append_attn(shape, **kw):
+    a = dict(query=FAKE, key=FAKE, value=FAKE, key_cache=FAKE, value_cache=FAKE,
+             cumulative_sequence_length=FAKE, past_seqlens=FAKE, block_table=FAKE, scale=0.0,
+             causal=1, num_splits=pa.PA_SPLITS_AUTO, workspace=FAKE,
+             workspace_bytes=pa.pa_paged_attention_workspace_size(shape), output=FAKE,
+             stream=0, check=False)
+    a.update(kw)
+    return pa.pa_append_attention(shape, **a)
+
+
+def test_append_attention_checks_both_parts_before_enqueueing():
+    # Each argument set breaks one rule of the append or of the attention; the call must report
+    # it before enqueueing anything (a launch here, without a GPU, would report PA_ERR_HIP).
+    assert _append_attn(_shape(), query=None) == pa.PA_ERR_NULL
+    assert _append_attn(_shape(), q_out=FAKE) == pa.PA_ERR_SHAPE        # q_out == query
+    assert _append_attn(_shape(), value=None) == pa.PA_ERR_SHAPE        # append: key xor value
+    assert _append_attn(_shape(packed_qkv=True)) == pa.PA_ERR_SHAPE     # packed with key/value
+    assert _append_attn(_shape(), key_cache=None) == pa.PA_ERR_NULL
+    assert _append_attn(_shape(), rotary_dim=63, cos_cache=FAKE, sin_cache=FAKE,
+                        rotary_mode=pa.PA_ROTARY_NEOX, rotary_positions=4) == pa.PA_ERR_SHAPE
+    assert _append_attn(_shape(), causal=2) == pa.PA_ERR_SHAPE         # attention rules
+    assert _append_attn(_shape(), num_splits=-2) == pa.PA_ERR_SHAPE
+    assert _append_attn(_shape(), block_table=None) == pa.PA_ERR_NULL
+    assert _append_attn(_shape(), output=None) == pa.PA_ERR_NULL
+    assert _append_attn(_shape(), workspace_bytes=16) == pa.PA_ERR_WORKSPACE
+    assert _append_attn(_shape(), workspace=FAKE + 4) == pa.PA_ERR_WORKSPACE
+    assert _append_attn(_shape(), workspace=None) == pa.PA_ERR_NULL
+    assert _append_attn(_shape(head_size=96)) == pa.PA_ERR_UNSUPPORTED
+    assert _append_attn(_shape(batch=0)) == pa.PA_ERR_SHAPE
+    assert _append_attn(_shape(num_tokens=0), workspace=None) == pa.PA_OK
+
+
 def test_workspace_size_is_zero_for_invalid_shapes():
     assert pa.pa_paged_attention_workspace_size(_shape(batch=0)) == 0
     assert pa.pa_paged_attention_workspace_size(_shape(), -3) == 0

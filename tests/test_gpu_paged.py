@@ -245,15 +245,24 @@ def test_many_sequences_attention(B, num_splits):
     assert_attention_close(out, ref, f"B={B}")
 
 
+@pytest.mark.parametrize("one_call", [False, True], ids=["two_calls", "one_call"])
 @pytest.mark.parametrize("num_splits", [pa.PA_SPLITS_AUTO, 3], ids=lambda s: f"S{s}")
-def test_graph_capture_replays_match_eager(num_splits):
-    """The append and the attention call captured into one HIP graph (the library enqueues
-    kernels only: no allocation, memset or synchronization): every replay, with eager library
-    work between replays, is bit-identical to the eager step."""
+def test_graph_capture_replays_match_eager(num_splits, one_call):
+    """The append and the attention (two calls, or pa_append_attention) captured into one HIP
+    graph (the library enqueues kernels only: no allocation, memset or synchronization): every
+    replay, with eager library work between replays, is bit-identical to the eager step."""
     w = W.paged_workload(160, past=[40, 300, 5, 1000], n_new=[1, 70, 1, 33], num_heads=8,
                          kv_num_heads=2, head_size=128, block_size=16, table="pool",
                          name="graph")
     c = dev.PagedCase(w)
+
+    def step():
+        if one_call:
+            c.append_attention(num_splits)
+        else:
+            c.append()
+            c.attention(num_splits)
+
     c.append()
     ref = c.attention(num_splits).clone()  # eager; also sizes the workspace outside the graph
     torch.cuda.synchronize()
@@ -261,14 +270,12 @@ def test_graph_capture_replays_match_eager(num_splits):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        c.append()
-        c.attention(num_splits)
+        step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        c.append()
-        c.attention(num_splits)
+        step()
     for i in range(3):
         c.output.zero_()
         torch.cuda.synchronize()
@@ -280,6 +287,95 @@ def test_graph_capture_replays_match_eager(num_splits):
         eager = c.attention(num_splits, out=torch.empty_like(ref))
         torch.cuda.synchronize()
         assert_bits_equal(eager, ref, f"eager after replay {i}")
+
+
+# pa_append_attention against the two separate calls on fresh copies of the same workload:
+# caches and output bit for bit, and the output against the oracle.
+APPEND_ATTN = [TINY[1], TINY[3], TINY[4], TINY[5], PREFILL[0], PREFILL[5], PREFILL[7]]
+
+
+@pytest.mark.parametrize("case", APPEND_ATTN, ids=lambda c: str(c["seed"]))
+@pytest.mark.parametrize("num_splits", [pa.PA_SPLITS_AUTO, pa.PA_SPLITS_PAGE_RULE, 3],
+                         ids=lambda s: f"S{s}")
+def test_append_attention_matches_separate_calls(case, num_splits):
+    case = dict(case)
+    w = W.paged_workload(case.pop("seed"), table="pool", slack=0.2, name="append_attn", **case)
+    kc, vc, ref = _oracle(w)
+    sep, out_sep = _run(w, num_splits)
+    c = dev.PagedCase(w)
+    out = c.append_attention(num_splits)
+    torch.cuda.synchronize()
+    assert_bits_equal(c.key_cache, sep.key_cache, "key_cache")
+    assert_bits_equal(c.value_cache, sep.value_cache, "value_cache")
+    assert_bits_equal(out, out_sep, "output")
+    assert_bits_equal(c.key_cache, kc, "key_cache vs oracle")
+    assert_attention_close(out, ref, f"append_attention S={num_splits}")
+
+
+@pytest.mark.parametrize("B", [100, 300])
+def test_append_attention_many_sequences(B):
+    """Past the one-wave planner (100 sequences) and past one planner chunk and the lane-held
+    cumulative lengths of the append (300): the planner workgroup runs with 256 threads."""
+    def past(r):
+        return r.integers(0, 400, size=B)
+
+    def n_new(r):
+        n = np.ones(B, dtype=np.int64)
+        n[::37] = 40
+        n[B // 2] = 0
+        return n
+
+    w = W.paged_workload(170 + B, past=past, n_new=n_new, num_heads=8, kv_num_heads=2,
+                         head_size=64, block_size=16, table="pool", name=f"append_attn{B}")
+    kc, vc, ref = _oracle(w)
+    sep, out_sep = _run(w)
+    c = dev.PagedCase(w)
+    out = c.append_attention()
+    torch.cuda.synchronize()
+    assert_bits_equal(c.key_cache, sep.key_cache, "key_cache")
+    assert_bits_equal(c.value_cache, sep.value_cache, "value_cache")
+    assert_bits_equal(out, out_sep, "output")
+    assert_attention_close(out, ref, f"B={B}")
+
+
+@pytest.mark.parametrize("case", [QROT[0], QROT[2], QROT[4]], ids=lambda c: str(c["seed"]))
+def test_append_attention_rotates_query(case):
+    """With q_out: the rotated rows bit-identical to the oracle's, and the output bit-identical
+    to pa_kv_append_rotate_query followed by attention over q_out."""
+    case = dict(case)
+    sm = case.pop("use_slot_mapping", False)
+    w = W.paged_workload(case.pop("seed"), table="pool", slack=0.2, name="append_attn_q",
+                         use_slot_mapping=sm, **case)
+    qref = oracle.rotate_query(w)
+    sep = dev.PagedCase(w)
+    q_sep = sep.append_rotate_query(use_slot_mapping=sm)
+    shape = pa.paged_shape(w["B"], w["T"], w["H"], w["G"], w["D"], w["NB"], w["bs"], w["MB"],
+                           False)
+    ws, n = sep.workspace_for(pa.PA_SPLITS_AUTO)
+    out_sep = torch.empty_like(sep.output)
+    pa.pa_paged_attention(shape, q_sep, sep.key_cache, sep.value_cache, sep.cu, sep.past,
+                          sep.block_table, w["scale"], w["causal"], pa.PA_SPLITS_AUTO, ws, n,
+                          out_sep)
+    c = dev.PagedCase(w)
+    q_out = torch.empty_like(q_sep)
+    out = c.append_attention(q_out=q_out, use_slot_mapping=sm)
+    torch.cuda.synchronize()
+    assert_bits_equal(q_out, qref, "q_out")
+    assert_bits_equal(c.key_cache, sep.key_cache, "key_cache")
+    assert_bits_equal(c.value_cache, sep.value_cache, "value_cache")
+    assert_bits_equal(out, out_sep, "output")
+
+
+def test_append_attention_gqa_full_size(gqa):
+    """The batch-64 serving decode through the one-call path: caches bit-exact against the
+    oracle, output within the attention bar."""
+    w, kc, vc, ref = gqa
+    c = dev.PagedCase(w)
+    out = c.append_attention(pa.PA_SPLITS_AUTO)
+    torch.cuda.synchronize()
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_bits_equal(c.value_cache, vc, "value_cache")
+    assert_attention_close(out, ref, "append_attention gqa")
 
 
 @pytest.mark.parametrize("causal", [0, 1])
