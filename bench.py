@@ -2,9 +2,10 @@
 """Benchmark: paged GQA decode step on one MI355X.
 
 A step is one pass of the hot path over the batch-64 GQA serving-decode workload (B=64, H=32,
-G=8, D=128, bs=16, past ~ U[512, 8192], seed 2): pa_kv_append of the 64 new K/V rows, then
-pa_paged_attention (device planner, split-KV decode kernel, log-sum-exp combine). Inputs are
-resident in HBM before timing starts.
+G=8, D=128, bs=16, past ~ U[512, 8192], seed 2): one pa_append_attention call, i.e. the append
+of the 64 new K/V rows beside the device planner in one launch, then the split-KV decode kernel
+and the log-sum-exp combine. Inputs are resident in HBM before timing starts. The same step as
+two calls (pa_kv_append, then pa_paged_attention) is timed beside it.
 
 Printed: ONE JSON line. `value` is the step's KV-cache read rate (sum_b L_b * G * D * 2 * 2
 bytes per step / step time) in GB/s; `query_tokens_per_s` sits beside it. `roofline` is the
@@ -98,6 +99,9 @@ def main():
     c = dev.PagedCase(w)
 
     def step():
+        c.append_attention(pa.PA_SPLITS_AUTO)
+
+    def step_two_calls():
         c.append()
         c.attention(pa.PA_SPLITS_AUTO)
 
@@ -105,13 +109,13 @@ def main():
     pa.pa_timing_enable(True)
     ms, wall = timed(step, args.steps, args.warmup, torch)
     pa.pa_timing_enable(False)
-    n_launch = args.steps + args.warmup
-    kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "prefill_combine",
-                                           "combine")}
+    kt = {k: pa.pa_timing_get(k) for k in ("append_plan", "attn_decode", "prefill_combine")}
     pa.pa_timing_reset()
     # the same steps without the library's event records, for the step time itself
     ms_plain, _ = timed(step, args.steps, args.warmup, torch)
-    print(f"# step {ms_plain:.4f} ms (with event hooks {ms:.4f} ms)", file=sys.stderr, flush=True)
+    ms_two, _ = timed(step_two_calls, args.steps, args.warmup, torch)
+    print(f"# step {ms_plain:.4f} ms (with event hooks {ms:.4f} ms; as two calls {ms_two:.4f} ms)",
+          file=sys.stderr, flush=True)
 
     dec_ms = kt["attn_decode"][0] / max(1, kt["attn_decode"][1])
     achieved = kv / (dec_ms * 1e-3) / 1e9
@@ -163,6 +167,7 @@ def main():
                    "past_seqlens": "uniform [512, 8192], seed 2", "kv_bytes_per_step": kv,
                    "num_splits": "auto", "parallelism": "none (1 GPU)"},
         "kernel_us": per_kernel,
+        "two_calls_ms_per_step": round(ms_two, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles("attn_decode"),
@@ -187,6 +192,7 @@ def run_extra(args, torch, np, pa, dev, W):
     kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "prefill_combine",
                                            "combine")}
     pa.pa_timing_reset()
+    ms_one, _ = timed(lambda: c.append_attention(pa.PA_SPLITS_AUTO), steps, 2, torch)
     us = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
     # prefill flops: causal QK^T and PV over the prefill rows, 4*D per (row, head, key)
     L = w["past"].astype(np.int64)
@@ -198,7 +204,8 @@ def run_extra(args, torch, np, pa, dev, W):
             flops += int(keys.sum()) * w["H"] * w["D"] * 4
     app_bytes = w["T"] * w["G"] * w["D"] * 2 * 4 + w["T"] * (w["rotary_dim"] // 2) * 2 * 2
     out["mixed_prefill_decode"] = {
-        "workload": w["name"], "ms_per_step": round(ms, 4), "kernel_us": us,
+        "workload": w["name"], "ms_per_step": round(ms, 4),
+        "one_call_ms_per_step": round(ms_one, 4), "kernel_us": us,
         "kv_bytes": kv, "step_kv_GBps": round(kv / (ms * 1e-3) / 1e9, 1),
         "prefill_TFLOPs": round(flops / (us.get("prefill_combine", 1e9) * 1e-6) / 1e12, 2),
         "prefill_mfma_frac": round(flops / (us.get("prefill_combine", 1e9) * 1e-6) / 1e12
