@@ -6,10 +6,10 @@
 namespace pa {
 namespace {
 
-template <int D>
+template <int D, int R>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int mode) {
-    combine_rows<D>(a, mode, (blockIdx.x * blockDim.x + threadIdx.x) >> 6,
-                    (gridDim.x * blockDim.x) >> 6);
+    combine_rows<D, R>(a, mode, (blockIdx.x * blockDim.x + threadIdx.x) >> 6,
+                       (gridDim.x * blockDim.x) >> 6);
 }
 
 }  // namespace
@@ -21,12 +21,15 @@ pa_status launch_combine(const CombineArgs &a, int max_groups, hipStream_t strea
     if (max_groups <= 0) return PA_OK;
     const long long waves = combine_waves(max_groups, a.lanes, a.D);
     const int grid = (int)((waves + 3) / 4);
-    switch (a.D) {
-        case 64:
-            scope.launch(combine_kernel<64>, dim3(grid), dim3(256), 0, a, mode);
+    const int R = combine_r(a.lanes, a.D);
+    switch (a.D * 4 + R) {
+        case 64 * 4 + 1: scope.launch(combine_kernel<64, 1>, dim3(grid), dim3(256), 0, a, mode); break;
+        case 64 * 4 + 2: scope.launch(combine_kernel<64, 2>, dim3(grid), dim3(256), 0, a, mode); break;
+        case 128 * 4 + 1:
+            scope.launch(combine_kernel<128, 1>, dim3(grid), dim3(256), 0, a, mode);
             break;
-        case 128:
-            scope.launch(combine_kernel<128>, dim3(grid), dim3(256), 0, a, mode);
+        case 128 * 4 + 2:
+            scope.launch(combine_kernel<128, 2>, dim3(grid), dim3(256), 0, a, mode);
             break;
         default:
             return PA_ERR_UNSUPPORTED;

@@ -7,92 +7,121 @@
 // Output row r = k*lanes + lane of group k:
 //   M = max m over units with l > 0, w = exp(m - M), out = sum w o / sum w l (0 if no l > 0).
 //
-// D/4 lanes own one output row (a float4 each), so a wave covers 64*4/D rows; the rows of one
-// unit are adjacent in memory, so a wave's loads for one unit are one contiguous span. Units are
-// merged online, eight per memory round trip (running max, rescaled sums), so a row costs
-// ceil(units / 8) dependent loads. wave / nwaves: this wave's index among the waves that share
-// the work (grid-stride over row blocks). mode: 0 uniform splits, 1 CSR offsets, 2 planner list.
+// D/4 lanes own one output row (a float4 each), so a row block of 64*4/D rows fills a wave; a
+// wave takes R row blocks of a group at once. The rows of one unit are adjacent in memory, so a
+// wave's loads for one unit are one contiguous span (with R = 2 and four rows per unit at
+// D = 128, the unit's whole 2 KB). Units are merged online, 8 / R per memory round trip
+// (running max, rescaled sums). wave / nwaves: this wave's index among the waves that share the
+// work (grid-stride over groups' row-block pairs). mode: 0 uniform splits, 1 CSR offsets,
+// 2 planner list. combine_dispatch picks R from the row count.
 #pragma once
 #include "common.h"
 
 namespace pa {
 
-template <int D>
+template <int D, int R>
 __device__ __forceinline__ void combine_rows(const CombineArgs &a, int mode, int wave, int nwaves) {
     constexpr int LPR = D / 4;      // lanes per row
-    constexpr int RPW = 64 / LPR;   // rows per wave
-    constexpr int NB = 8;           // units loaded per round trip
+    constexpr int RPW = 64 / LPR;   // rows per wave per row block
+    constexpr int NB = 8 / R;       // units loaded per round trip
     const int lane = threadIdx.x & 63;
     const int sub = lane % LPR;     // float4 index inside the row
     const int rw = lane / LPR;      // row inside the wave's row block
     const int n_groups = (mode == 2) ? a.n_items[0] : a.num_groups;
-    const int blocks_per_group = (a.lanes + RPW - 1) / RPW;
+    const int blocks_per_group = (a.lanes + R * RPW - 1) / (R * RPW);
     const long long n_work = (long long)n_groups * blocks_per_group;
 
     for (long long w = wave; w < n_work; w += nwaves) {
         const int k = (int)(w / blocks_per_group);
-        const int lane_row = (int)(w - (long long)k * blocks_per_group) * RPW + rw;
+        const int row0 = (int)(w - (long long)k * blocks_per_group) * R * RPW + rw;
         long long e0, e1, row_group;
-        if (mode == 0) {          // uniform splits
+        if (mode == 0) {
             e0 = (long long)k * a.splits; e1 = e0 + a.splits; row_group = k;
-        } else if (mode == 1) {   // CSR offsets
+        } else if (mode == 1) {
             e0 = a.group_ptr[k]; e1 = a.group_ptr[k + 1]; row_group = k;
-        } else {                  // planner list
+        } else {
             const CombItem it = a.items[k];
             e0 = it.e0; e1 = e0 + it.count; row_group = it.row;
         }
-        const bool active = lane_row < a.lanes;
-        const int lr = active ? lane_row : 0;
-
-        // Online merge, NB units per round trip: every lane of the row loads the units' m and l
-        // (one broadcast line) and its own float4 of o, all before any of them is used.
-        float M = -INFINITY, Ls = 0.f;
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        int lr[R];
+        bool active[R];
+        for (int j = 0; j < R; ++j) {
+            const int r = row0 + j * RPW;
+            active[j] = r < a.lanes;
+            lr[j] = active[j] ? r : 0;
+        }
+        float M[R], Ls[R];
+        float4_t acc[R];
+        for (int j = 0; j < R; ++j) {
+            M[j] = -INFINITY; Ls[j] = 0.f; acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
         for (long long e = e0; e < e1; e += NB) {
-            float mv[NB], lv[NB];
-            float4_t ov[NB];
+            float mv[NB][R], lv[NB][R];
+            float4_t ov[NB][R];
             for (int u = 0; u < NB; ++u) {
                 const long long eu = e + u < e1 ? e + u : e1 - 1;
-                const long long p = eu * a.lanes + lr;
-                mv[u] = a.m[p];
-                lv[u] = e + u < e1 ? a.l[p] : 0.f;
-                ov[u] = gload_nt<float4_t>(a.o + p * D + 4 * sub);
+                for (int j = 0; j < R; ++j) {
+                    const long long p = eu * a.lanes + lr[j];
+                    mv[u][j] = a.m[p];
+                    lv[u][j] = e + u < e1 ? a.l[p] : 0.f;
+                    ov[u][j] = gload_nt<float4_t>(a.o + p * D + 4 * sub);
+                }
             }
-            float bm = -INFINITY;
-            for (int u = 0; u < NB; ++u)
-                if (lv[u] > 0.f) bm = fmaxf(bm, mv[u]);
-            if (bm == -INFINITY) continue;             // no unit of this batch counts
-            const float Mn = fmaxf(M, bm);
-            const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
-            acc *= sc;
-            Ls *= sc;
-            for (int u = 0; u < NB; ++u) {
-                const float wu = lv[u] > 0.f ? __builtin_amdgcn_exp2f((mv[u] - Mn) * kLog2e) : 0.f;
-                acc += wu * ov[u];
-                Ls += wu * lv[u];
+            for (int j = 0; j < R; ++j) {
+                float bm = -INFINITY;
+                for (int u = 0; u < NB; ++u)
+                    if (lv[u][j] > 0.f) bm = fmaxf(bm, mv[u][j]);
+                if (bm == -INFINITY) continue;
+                const float Mn = fmaxf(M[j], bm);
+                const float sc =
+                    (M[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M[j] - Mn) * kLog2e);
+                acc[j] *= sc;
+                Ls[j] *= sc;
+                for (int u = 0; u < NB; ++u) {
+                    const float wu =
+                        lv[u][j] > 0.f ? __builtin_amdgcn_exp2f((mv[u][j] - Mn) * kLog2e) : 0.f;
+                    acc[j] += wu * ov[u][j];
+                    Ls[j] += wu * lv[u][j];
+                }
+                M[j] = Mn;
             }
-            M = Mn;
         }
-        if (!active) continue;
-        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-        acc *= inv;
-        const long long r = row_group * a.lanes + lane_row;
-        if (a.out_f32) {
-            *(float4_t *)((float *)a.out + r * D + 4 * sub) = acc;
-        } else {
-            half4_t h;
-            for (int i = 0; i < 4; ++i) h[i] = (half_t)acc[i];
-            *(half4_t *)((half_t *)a.out + r * D + 4 * sub) = h;
+        for (int j = 0; j < R; ++j) {
+            if (!active[j]) continue;
+            const float inv = Ls[j] > 0.f ? 1.f / Ls[j] : 0.f;
+            float4_t o = acc[j] * inv;
+            const long long r = row_group * a.lanes + row0 + j * RPW;
+            if (a.out_f32) {
+                *(float4_t *)((float *)a.out + r * D + 4 * sub) = o;
+            } else {
+                half4_t h;
+                for (int i = 0; i < 4; ++i) h[i] = (half_t)o[i];
+                *(half4_t *)((half_t *)a.out + r * D + 4 * sub) = h;
+            }
         }
     }
 }
 
 
-// Waves to launch for up to max_groups groups of `lanes` rows of head dim D.
+// Two row blocks per wave when a group has that many rows (fewer, longer contiguous loads);
+// one otherwise, so that no load is spent on rows past the group.
+__host__ __device__ constexpr int combine_r(int lanes, int D) { return lanes >= 2 * (256 / D) ? 2 : 1; }
+
+template <int D>
+__device__ __forceinline__ void combine_dispatch(const CombineArgs &a, int mode, int wave,
+                                                 int nwaves) {
+    if (combine_r(a.lanes, D) == 2) combine_rows<D, 2>(a, mode, wave, nwaves);
+    else combine_rows<D, 1>(a, mode, wave, nwaves);
+}
+
+// Waves to launch for up to max_groups groups of `lanes` rows of head dim D. Capped at 8 (two
+// row blocks per wave) or 12 waves per CU: on the 2 GB block-sparse merge more waves in flight
+// read HBM more slowly (8192 waves: 5.2 TB/s; 2048 waves of two row blocks: 5.6 TB/s).
 inline long long combine_waves(int max_groups, int lanes, int D) {
-    const int rpw = 64 / (D / 4);
-    const long long work = (long long)max_groups * ((lanes + rpw - 1) / rpw);
-    const long long cap = (long long)device_cu_count() * 32;  // waves: 8 per SIMD
+    const int R = combine_r(lanes, D);
+    const int rows = R * (64 / (D / 4));
+    const long long work = (long long)max_groups * ((lanes + rows - 1) / rows);
+    const long long cap = (long long)device_cu_count() * (R == 2 ? 8 : 12);
     return work < cap ? work : cap;
 }
 

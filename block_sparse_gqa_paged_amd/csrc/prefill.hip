@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
 
     if ((int)blockIdx.x < (int)gridDim.x - pre_blocks) {
         constexpr int kWg = kPfThreads / 64;
-        combine_rows<D>(cmb, 2, blockIdx.x * kWg + (threadIdx.x >> 6),
+        combine_dispatch<D>(cmb, 2, blockIdx.x * kWg + (threadIdx.x >> 6),
                         (gridDim.x - pre_blocks) * kWg);
         return;
     }
