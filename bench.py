@@ -12,7 +12,9 @@ bytes per step / step time) in GB/s; `query_tokens_per_s` sits beside it. `roofl
 decode attention kernel alone: algorithmic KV bytes per launch / its mean launch time from HIP
 events recorded by the library on the launch stream, against 8 TB/s. `cpu_baseline` times the
 CPU oracle on the same workload's attention rows. `extra` carries the mixed prefill+decode and
-block-sparse workloads.
+block-sparse workloads. Beside the contract's mean over the timed steps: p10 / p50 / p90 of 100
+individually timed steps, and the box's own 1 GiB device-copy rate (bytes read + written) as a
+second reference next to the 8 TB/s peak.
 """
 import argparse
 import hashlib
@@ -79,6 +81,41 @@ def timed(fn, steps, warmup, torch):
     return s.elapsed_time(e) / steps, wall
 
 
+def step_percentiles(fn, n, warmup, torch, np):
+    """Per-step durations (ms) from an event pair around each of n steps: p10, p50, p90."""
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    t = np.array([s.elapsed_time(e) for s, e in ev])
+    return {f"p{q}": round(float(np.percentile(t, q)), 4) for q in (10, 50, 90)}
+
+
+def box_copy_gbps(torch, nbytes=1 << 30, reps=5):
+    """The box's own device-to-device copy rate (bytes read + bytes written per second)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -114,6 +151,8 @@ def main():
     # the same steps without the library's event records, for the step time itself
     ms_plain, _ = timed(step, args.steps, args.warmup, torch)
     ms_two, _ = timed(step_two_calls, args.steps, args.warmup, torch)
+    pct = step_percentiles(step, 100, 10, torch, np)
+    copy_gbps = box_copy_gbps(torch)
     print(f"# step {ms_plain:.4f} ms (with event hooks {ms:.4f} ms; as two calls {ms_two:.4f} ms)",
           file=sys.stderr, flush=True)
 
@@ -168,10 +207,12 @@ def main():
                    "num_splits": "auto", "parallelism": "none (1 GPU)"},
         "kernel_us": per_kernel,
         "two_calls_ms_per_step": round(ms_two, 4),
+        "step_ms_percentiles_100": pct,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles("attn_decode"),
-                     "kernel": "attn_decode", "kernel_us": round(dec_ms * 1e3, 2)},
+                     "kernel": "attn_decode", "kernel_us": round(dec_ms * 1e3, 2),
+                     "box_copy_GBps_read_plus_write": copy_gbps},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -348,6 +348,32 @@ def block_sparse_forward(seed=4):
                            name="block_sparse_tq4096_hkv8_q4_d128_blk64")
 
 
+def random_partials(seed, *, groups, lanes, head_dim, max_units=9, p_empty=0.1,
+                    uniform_splits=0):
+    """Seeded (o, m, l) partial sets for merge tests. With uniform_splits = S > 0 every group
+    owns S units and group_ptr is None; otherwise group k owns U[0, max_units] units (some groups
+    none) and group_ptr is their CSR offsets. Unit e holds `lanes` partials p = e*lanes + lane:
+    o ~ N(0, 1) [P, head_dim] float32, m ~ U[-20, 20], l ~ U[0.5, 50]; a fraction p_empty of the
+    partials are empty key ranges (o = 0, m = -1e30, l = 0)."""
+    r = np.random.default_rng(seed)
+    if uniform_splits > 0:
+        counts = np.full(groups, uniform_splits, dtype=np.int64)
+        gp = None
+    else:
+        counts = r.integers(0, max_units + 1, size=groups)
+        gp = np.zeros(groups + 1, dtype=np.int32)
+        gp[1:] = np.cumsum(counts)
+    P = int(counts.sum()) * lanes
+    o = r.standard_normal((P, head_dim)).astype(np.float32)
+    m = r.uniform(-20.0, 20.0, size=P).astype(np.float32)
+    l = r.uniform(0.5, 50.0, size=P).astype(np.float32)
+    empty = r.random(P) < p_empty
+    o[empty] = 0.0
+    m[empty] = -1e30
+    l[empty] = 0.0
+    return dict(o=o, m=m, l=l, group_ptr=gp, groups=groups)
+
+
 def kv_bytes(w) -> int:
     """K+V cache bytes a causal decode/prefill pass must read once per sequence: sum_b L_b*G*D*2*2."""
     L = w["past"].astype(np.int64) + np.diff(w["cu"]).astype(np.int64)

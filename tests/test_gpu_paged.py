@@ -496,6 +496,30 @@ def test_combine_uniform_splits(S, out_dtype):
         assert np.allclose(g, ref, rtol=1e-5, atol=1e-6)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("lanes", [1, 3, 5, 7, 12, 33])
+@pytest.mark.parametrize("uniform", [0, 3], ids=["csr", "uniform3"])
+def test_combine_row_blocks(D, lanes, uniform):
+    """Random partial sets over both merge layouts: one row block of 256/D rows per wave, or two
+    when a group has that many rows (lanes >= 8 at D = 64, >= 4 at D = 128), with ragged last
+    blocks, empty groups and empty partials, in CSR and uniform-split form."""
+    rp = W.random_partials(200 + lanes + D + uniform, groups=37, lanes=lanes, head_dim=D,
+                           uniform_splits=uniform)
+    kw = dict(lanes=lanes, head_dim=D)
+    if uniform:
+        kw.update(num_splits=uniform)
+    else:
+        kw.update(group_ptr=rp["group_ptr"])
+    ref = oracle.split_combine(rp["o"], rp["m"], rp["l"], out_dtype=np.float32, **kw)
+    got = dev.combine(rp["o"], rp["m"], rp["l"], out_dtype=pa.PA_F32, **kw).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.allclose(got, ref, rtol=1e-5, atol=1e-6), float(np.abs(got - ref).max())
+    ref16 = oracle.split_combine(rp["o"], rp["m"], rp["l"], out_dtype=np.float16, **kw)
+    got16 = dev.combine(rp["o"], rp["m"], rp["l"], out_dtype=pa.PA_F16, **kw)
+    torch.cuda.synchronize()
+    assert_attention_close(got16, ref16, f"combine fp16 lanes={lanes} D={D}")
+
+
 def test_combine_csr_with_empty_and_sentinel_groups():
     w = W.paged_workload(121, past=[90, 20], n_new=[1, 1], num_heads=4, kv_num_heads=4,
                          head_size=64, block_size=16, name="comb")
