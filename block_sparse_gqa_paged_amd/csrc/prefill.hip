@@ -237,6 +237,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
 
             // S^T: keys 32s + 8*g16 + 4u + i of columns n16 (both column blocks per K read).
             float sc[2][2][2][4];
+            // The score products run at raised wave priority: of the two waves sharing a SIMD,
+            // the one in this phase keeps the matrix unit fed while the other runs its softmax.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
             for (int s = 0; s < 2; ++s)
                 for (int u = 0; u < 2; ++u) {
                     float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -253,6 +257,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
             // Online softmax per column, P in fp16 as the B operand of O^T = V^T . P^T. Keys at or
             // past a column's limit are masked only on tiles that reach some limit; the scale
             // (> 0) is applied after the max, inside the exponent's fma.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
             if (kt + kKT > wave_min)
                 for (int cb = 0; cb < 2; ++cb)
                     for (int s = 0; s < 2; ++s)
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
             // O^T += V^T . P^T: A operand = keys 32s + 8*g16 + 0..7 of dim 16*dt + n16, two
             // transposing reads of 4 keys (lane r of a 16-lane group addresses key kb + r/4,
             // dims 16*dt + 4*(r%4) .. +3); the accumulator holds dims 16*dt + 4*g16 + i of column n16.
-            // The operand of output tile dt + 1 is read while tile dt's products run.
+            // Each operand is read two output tiles ahead of its products.
             const int csub = (n16 & 3) >> 1, hoff = 4 * (n16 & 1);
             auto vop = [&](int s, int dt) {
                 const int k0 = 32 * s + 8 * g16 + (n16 >> 2), k4 = k0 + 4;
@@ -298,15 +304,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
                 const half4_t hi = lds_read_tr(Vb + k4 * D + 8 * (c ^ vmask<KC>(k4)) + hoff);
                 return half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             };
-            half8_t vnext = vop(0, 0);
-            for (int s = 0; s < 2; ++s)
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const half8_t vb = vnext;
-                    if (dt + 1 < NDT) vnext = vop(s, dt + 1);
-                    else if (s == 0) vnext = vop(1, 0);
-                    o[0][dt] = mfma16x16x32(vb, pf[0][s], o[0][dt]);
-                    o[1][dt] = mfma16x16x32(vb, pf[1][s], o[1][dt]);
-                }
+            half8_t va = vop(0, 0), vbn = vop(0, 1);
+            for (int x = 0; x < 2 * NDT; ++x) {
+                const int s = x / NDT, dt = x % NDT;
+                const half8_t vb = va;
+                va = vbn;
+                if (x + 2 < 2 * NDT) vbn = vop((x + 2) / NDT, (x + 2) % NDT);
+                o[0][dt] = mfma16x16x32(vb, pf[0][s], o[0][dt]);
+                o[1][dt] = mfma16x16x32(vb, pf[1][s], o[1][dt]);
+            }
         }
 
         // Column totals; lane (g16, n16) writes dims 16*dt + 4*g16 .. +3 of column n16.
