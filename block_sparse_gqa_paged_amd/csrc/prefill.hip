@@ -163,11 +163,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
     const int n_work = a.n_items[0] * a.G;
     if (n_work == 0) return;
 
-    for (;;) {
-        if (threadIdx.x == 0) s_unit = atomicAdd(a.counter, 1);
-        __syncthreads();
-        const int unit = s_unit;
-        __syncthreads();
+    // Prefill workgroup pb takes unit pb first (the planner lists the longest units first), then
+    // units pre_blocks + k in the order of the counter's tickets k: no atomic round trip and no
+    // barrier before the first unit. Later units start after a barrier, so no wave still reads
+    // the previous unit's LDS stage when the new unit's first copies land in it.
+    const int pb = (int)blockIdx.x - ((int)gridDim.x - pre_blocks);
+    for (int iter = 0;; ++iter) {
+        int unit = pb;
+        if (iter > 0) {
+            if (threadIdx.x == 0) s_unit = pre_blocks + atomicAdd(a.counter, 1);
+            __syncthreads();
+            unit = s_unit;
+            __syncthreads();
+        }
         if (unit >= n_work) break;
         const AttnItem it = a.items[unit / a.G];
         const int g = unit - (unit / a.G) * a.G;
