@@ -43,31 +43,49 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+# Sources that shape each profiled launch (its kernel code, the structs it reads and the host code
+# that sizes its grid). A counter reading stays valid only while these files are unchanged.
+KERNEL_SOURCES = {
+    "attn_decode": ("attention.hip", "plan.h", "common.h", "api.hip"),
+    "prefill_combine": ("prefill.hip", "combine_rows.h", "plan.h", "common.h", "api.hip"),
+    "append_plan": ("kv_append.hip", "plan.h", "common.h", "api.hip"),
+    "kv_append": ("kv_append.hip", "common.h", "api.hip"),
+    "plan": ("attention.hip", "plan.h", "common.h", "api.hip"),
+}
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_gqa_paged_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel):
-    """HBM bytes per launch measured with rocprofv3 counters, if taken on the current kernels."""
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on the current sources
+    of that launch."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
-        return None
     k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    if k is None or k.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return k.get("bytes_per_launch")
 
 
-def timed(fn, steps, warmup, torch):
-    for _ in range(warmup):
+def timed(fn, steps, warmup, torch, warm_ms=0.0):
+    """Mean ms per step of `steps` steps, after at least `warmup` untimed steps and at least
+    `warm_ms` of untimed work."""
+    t_w = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t_w) * 1e3 < warm_ms:
         fn()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     s = torch.cuda.Event(enable_timing=True)
@@ -114,6 +132,9 @@ def box_copy_gbps(torch, nbytes=1 << 30, reps=5):
     del src, dst
     torch.cuda.empty_cache()
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+WARM_MS = 100.0  # untimed work before each secondary workload's timed loop
 
 
 def main():
@@ -222,18 +243,26 @@ def main():
 def run_extra(args, torch, np, pa, dev, W):
     out = {}
     steps = max(3, args.steps // 5)
+    # Untimed work before each timed loop. The compute-bound prefill runs up to 25% slower for
+    # the first few tens of milliseconds after the memory-bound decode loop (130-134 us, then
+    # 106-107 us on the mixed workload), so each secondary loop warms up for 100 ms of its own.
+    wu = max(10, args.warmup)
+
+    def warm(fn):  # untimed, with the library's timing hooks off
+        timed(fn, 1, wu, torch, WARM_MS)
     print("# generating the mixed prefill+decode workload", file=sys.stderr, flush=True)
     w = W.mixed_prefill_decode()
     c = dev.PagedCase(w)
     kv = W.kv_bytes(w)
+    warm(lambda: (c.append(), c.attention(pa.PA_SPLITS_AUTO)))
     pa.pa_timing_reset()
     pa.pa_timing_enable(True)
-    ms, _ = timed(lambda: (c.append(), c.attention(pa.PA_SPLITS_AUTO)), steps, 2, torch)
+    ms, _ = timed(lambda: (c.append(), c.attention(pa.PA_SPLITS_AUTO)), steps, 0, torch)
     pa.pa_timing_enable(False)
     kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "prefill_combine",
                                            "combine")}
     pa.pa_timing_reset()
-    ms_one, _ = timed(lambda: c.append_attention(pa.PA_SPLITS_AUTO), steps, 2, torch)
+    ms_one, _ = timed(lambda: c.append_attention(pa.PA_SPLITS_AUTO), steps, wu, torch, WARM_MS)
     us = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
     # prefill flops: causal QK^T and PV over the prefill rows, 4*D per (row, head, key)
     L = w["past"].astype(np.int64)
@@ -258,9 +287,10 @@ def run_extra(args, torch, np, pa, dev, W):
     }
     # the append with every new query row rotated into q_out in the same launch
     q_out = torch.empty((w["T"], w["H"] * w["D"]), dtype=torch.float16, device="cuda")
+    warm(lambda: c.append_rotate_query(q_out))
     pa.pa_timing_reset()
     pa.pa_timing_enable(True)
-    timed(lambda: c.append_rotate_query(q_out), steps, 2, torch)
+    timed(lambda: c.append_rotate_query(q_out), steps, 0, torch)
     pa.pa_timing_enable(False)
     t_rq = pa.pa_timing_get("kv_append")
     pa.pa_timing_reset()
@@ -276,9 +306,10 @@ def run_extra(args, torch, np, pa, dev, W):
     print("# generating the append stress workload", file=sys.stderr, flush=True)
     w = W.append_stress()
     c = dev.PagedCase(w)
+    warm(c.append)
     pa.pa_timing_reset()
     pa.pa_timing_enable(True)
-    ms, _ = timed(c.append, steps, 2, torch)
+    ms, _ = timed(c.append, steps, 0, torch)
     pa.pa_timing_enable(False)
     t_app = pa.pa_timing_get("kv_append")
     pa.pa_timing_reset()
@@ -296,9 +327,10 @@ def run_extra(args, torch, np, pa, dev, W):
     print("# generating the contiguous-cache append workload", file=sys.stderr, flush=True)
     bw = W.bnsh_append()
     bc = dev.BnshCase(bw)
+    warm(bc.append)
     pa.pa_timing_reset()
     pa.pa_timing_enable(True)
-    timed(bc.append, steps, 2, torch)
+    timed(bc.append, steps, 0, torch)
     pa.pa_timing_enable(False)
     t_b = pa.pa_timing_get("kv_append_bnsh")
     pa.pa_timing_reset()
@@ -316,18 +348,20 @@ def run_extra(args, torch, np, pa, dev, W):
     print("# generating the block-sparse workload", file=sys.stderr, flush=True)
     sw = W.block_sparse_forward()
     s = dev.SparseCase(sw)
+    warm(lambda: (s.forward(), s.combine()))
     pa.pa_timing_reset()
     pa.pa_timing_enable(True)
-    ms, _ = timed(lambda: (s.forward(), s.combine()), steps, 1, torch)
+    ms, _ = timed(lambda: (s.forward(), s.combine()), steps, 0, torch)
     pa.pa_timing_enable(False)
     kt = {k: pa.pa_timing_get(k) for k in ("sparse_forward", "combine")}
     pa.pa_timing_reset()
     us = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
     # the edge list itself, built on the device from the kept-block mask
     eb = dev.EdgeBuilder(sw)
+    warm(eb.build)
     pa.pa_timing_reset()
     pa.pa_timing_enable(True)
-    timed(eb.build, steps, 1, torch)
+    timed(eb.build, steps, 0, torch)
     pa.pa_timing_enable(False)
     t_e = pa.pa_timing_get("build_edges")
     pa.pa_timing_reset()
@@ -335,9 +369,10 @@ def run_extra(args, torch, np, pa, dev, W):
     edge_bytes = sw["block_mask"].size + sw["E"] * 20 + (sw["Tq"] * sw["hkv"] + 1) * 4
     del eb
     # the same edges under the right-aligned causal mask
+    warm(lambda: s.forward(causal=True))
     pa.pa_timing_reset()
     pa.pa_timing_enable(True)
-    timed(lambda: s.forward(causal=True), steps, 1, torch)
+    timed(lambda: s.forward(causal=True), steps, 0, torch)
     pa.pa_timing_enable(False)
     t_c = pa.pa_timing_get("sparse_forward")
     pa.pa_timing_reset()
