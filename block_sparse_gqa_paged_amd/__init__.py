@@ -21,12 +21,16 @@ PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_H
 PA_ROTARY_NONE, PA_ROTARY_NEOX, PA_ROTARY_INTERLEAVED = 0, 1, 2
 PA_F16, PA_F32 = 0, 1
 PA_SPLITS_AUTO, PA_SPLITS_PAGE_RULE = 0, -1
+# pa_check_paged_indices flag bits (include/pa.h)
+PA_CHECK_CU_START, PA_CHECK_CU_ORDER, PA_CHECK_CU_END, PA_CHECK_PAST = 1, 2, 4, 8
+PA_CHECK_TABLE_WIDTH, PA_CHECK_TABLE_ENTRY, PA_CHECK_SLOT = 16, 32, 64
+PA_CHECK_SLOT_TABLE, PA_CHECK_POSITION = 128, 256
 
 EXPORTED = ("pa_kv_append", "pa_kv_append_rotate_query", "pa_paged_attention_workspace_size",
             "pa_paged_attention", "pa_append_attention",
             "pa_split_combine", "pa_sparse_forward_workspace_size", "pa_sparse_forward",
             "pa_sparse_forward_causal", "pa_sparse_build_edges_workspace_size",
-            "pa_sparse_build_edges", "pa_kv_append_bnsh",
+            "pa_sparse_build_edges", "pa_kv_append_bnsh", "pa_check_paged_indices",
             "pa_status_string", "pa_timing_enable", "pa_timing_reset", "pa_timing_get")
 
 
@@ -101,6 +105,8 @@ def lib():
     L.pa_sparse_build_edges.restype = _i32
     L.pa_kv_append_bnsh.argtypes = [C.POINTER(BnshShape)] + [_vp] * 9 + [_i32] * 3 + [_vp]
     L.pa_kv_append_bnsh.restype = _i32
+    L.pa_check_paged_indices.argtypes = [sp] + [_vp] * 4 + [_i32, _vp, _vp]
+    L.pa_check_paged_indices.restype = _i32
     L.pa_status_string.argtypes = [_i32]
     L.pa_status_string.restype = C.c_char_p
     L.pa_timing_enable.argtypes = [_i32]
@@ -253,6 +259,16 @@ def pa_sparse_build_edges(tq, hkv, nblk, block_size, batch, block_mask, q_batch,
         _p(used_kv_lens), int(edge_capacity), _p(edge_meta), _p(group_ptr), _p(workspace),
         int(workspace_bytes), _s(stream))
     return _check(st, "pa_sparse_build_edges", check)
+
+
+def pa_check_paged_indices(shape, cumulative_sequence_length, past_seqlens, block_table,
+                           slot_mapping, flags, rotary_positions=0, stream=None, check=True):
+    """Enqueue the device check of a paged call's index arrays; flags (int32 [1], device) gets
+    one PA_CHECK_* bit per violated rule."""
+    st = lib().pa_check_paged_indices(
+        C.byref(shape), _p(cumulative_sequence_length), _p(past_seqlens), _p(block_table),
+        _p(slot_mapping), int(rotary_positions), _p(flags), _s(stream))
+    return _check(st, "pa_check_paged_indices", check)
 
 
 def pa_kv_append_bnsh(shape, query, key, value, present_key, present_value,

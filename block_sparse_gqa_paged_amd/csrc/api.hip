@@ -542,6 +542,19 @@ pa_status pa_append_attention(const pa_paged_shape *shape, const void *query, co
     return run_attention(call, call.pl.tpi_pre, strm);
 }
 
+pa_status pa_check_paged_indices(const pa_paged_shape *shape,
+                                 const int32_t *cumulative_sequence_length,
+                                 const int32_t *past_seqlens, const int32_t *block_table,
+                                 const int32_t *slot_mapping, int32_t rotary_positions,
+                                 int32_t *flags, void *stream) {
+    if (!shape || !cumulative_sequence_length || !past_seqlens || !flags) return PA_ERR_NULL;
+    const pa_status st = check_shape(shape);
+    if (st != PA_OK) return st;
+    if (rotary_positions < 0) return PA_ERR_SHAPE;
+    return launch_check_paged(*shape, cumulative_sequence_length, past_seqlens, block_table,
+                              slot_mapping, rotary_positions, flags, (hipStream_t)stream);
+}
+
 pa_status pa_split_combine(const float *o_partial, const float *m_partial,
                            const float *l_partial, const int32_t *group_ptr, int32_t num_groups,
                            int32_t lanes, int32_t num_splits, int32_t head_dim, int32_t out_dtype,

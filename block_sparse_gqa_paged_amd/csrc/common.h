@@ -231,6 +231,9 @@ struct EdgeArgs {
 };
 pa_status launch_build_edges(const EdgeArgs &a, hipStream_t stream);
 size_t edge_workspace_bytes(long long rows);
+pa_status launch_check_paged(const pa_paged_shape &s, const int32_t *cu, const int32_t *past,
+                             const int32_t *bt, const int32_t *slot, int32_t rotary_positions,
+                             int32_t *flags, hipStream_t stream);
 size_t sparse_workspace_bytes(int E, int units, long long qrows, int D);
 
 // ---------------------------------------------------------------------------------------------

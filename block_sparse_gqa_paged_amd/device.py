@@ -7,8 +7,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, bnsh_shape, pa_append_attention, pa_kv_append,
-               pa_kv_append_bnsh, pa_kv_append_rotate_query,
+from . import (PA_F16, PA_F32, PA_SPLITS_AUTO, bnsh_shape, pa_append_attention,
+               pa_check_paged_indices, pa_kv_append, pa_kv_append_bnsh, pa_kv_append_rotate_query,
                pa_paged_attention,
                pa_paged_attention_workspace_size, pa_sparse_build_edges,
                pa_sparse_build_edges_workspace_size, pa_sparse_forward, pa_sparse_forward_causal,
@@ -47,6 +47,18 @@ class PagedCase:
         self.sin = to_dev(w["sin"], device)
         self.output = torch.empty((w["T"], w["H"] * w["D"]), dtype=torch.float16, device=device)
         self._ws = {}
+
+    def check_indices(self, use_slot_mapping=True, use_block_table=True, stream=None):
+        """The device check of this workload's index arrays (pa_check_paged_indices); waits for
+        it and returns the PA_CHECK_* flag word (0: every rule holds)."""
+        flags = torch.full((1,), -1, dtype=torch.int32, device=self.device)
+        rot = 0 if self.cos is None else self.cos.shape[0]
+        pa_check_paged_indices(self.shape, self.cu, self.past,
+                               self.block_table if use_block_table else None,
+                               self.slot_mapping if use_slot_mapping else None, flags,
+                               rotary_positions=rot, stream=stream)
+        torch.cuda.synchronize()
+        return int(flags.item())
 
     def append(self, use_slot_mapping=True, stream=None):
         w = self.w

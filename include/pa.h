@@ -11,6 +11,7 @@
  *   pa_sparse_build_edges      the sparse forward's edge list from a kept-block mask
  *   pa_kv_append_bnsh          the append into a contiguous BNSH cache (the append page's own)
  *   pa_append_attention        the append and the attention in one call (the manifest's op)
+ *   pa_check_paged_indices     a debug check of the paged calls' device-resident indices
  *
  * Sources. Argument names and layouts follow three web pages:
  *   [manifest] "com.microsoft.PagedAttention ... manifest.json": the op's inputs, outputs,
@@ -28,7 +29,8 @@
  *   - Host-visible scalars and null pointers are checked before anything is enqueued; a failed
  *     check returns a non-zero pa_status and enqueues nothing. The contents of device-resident
  *     index arrays (cumulative_sequence_length, past_seqlens, block_table, slot_mapping,
- *     edge_meta, block_tables) are the caller's contract and are not checked.
+ *     edge_meta, block_tables) are the caller's contract and are not checked; the paged ones
+ *     can be checked on the device beforehand with pa_check_paged_indices.
  *   - fp16 is IEEE binary16 (`_Float16` / `__half`); element offsets may exceed 2^31.
  *   - The library holds no mutable state except a per-device cache of the compute-unit count and
  *     the optional timing records (pa_timing_*). Calls may come from several host threads.
@@ -375,6 +377,53 @@ pa_status pa_kv_append_bnsh(const pa_bnsh_shape *shape, const void *query, const
                             const int32_t *key_total_sequence_lengths, const void *cos_cache,
                             const void *sin_cache, int32_t rotary_dim, int32_t rotary_mode,
                             int32_t rotary_positions, void *stream);
+
+/*
+ * pa_check_paged_indices - check the device-resident index contents of a paged call (a debug
+ * aid; the other entry points do not check them).
+ *
+ * The arrays are the [manifest] inputs cumulative_sequence_length, past_seqlens, block_table
+ * and slot_mapping, with the sizes its "derive" section fixes from `shape`. The append and the
+ * attention kernels follow these indices without bounds checks; this call verifies every rule
+ * they rely on and ORs one PA_CHECK_* bit per violated rule into flags[0]:
+ *   PA_CHECK_CU_START     cumulative_sequence_length[0] != 0
+ *   PA_CHECK_CU_ORDER     cumulative_sequence_length decreases somewhere
+ *   PA_CHECK_CU_END       cumulative_sequence_length[B] != num_tokens
+ *   PA_CHECK_PAST         a past_seqlens entry is negative
+ *   PA_CHECK_TABLE_WIDTH  a sequence's keys (past + new) need more than max_blocks blocks
+ *   PA_CHECK_TABLE_ENTRY  a block_table entry that covers one of its sequence's keys lies
+ *                         outside [0, num_blocks) (entries past the keys are never read)
+ *   PA_CHECK_SLOT         a slot_mapping entry is >= num_blocks * block_size (negative
+ *                         entries mean "not written" and pass)
+ *   PA_CHECK_SLOT_TABLE   a slot_mapping entry differs from the slot the block table gives
+ *                         the row's position (attention would read another row than the
+ *                         append wrote)
+ *   PA_CHECK_POSITION     with rotary_positions > 0: a new row's position is outside
+ *                         [0, rotary_positions) (its cos/sin row does not exist)
+ * slot_mapping may be NULL (not checked); block_table may be NULL (entries, and slot_mapping
+ * against the table, not checked); rotary_positions = 0 skips the position rule.
+ *   flags  int32 [1] (device), written by the call (cleared first); read it after the stream
+ *          reaches the call. 0 means every rule holds.
+ * Only the index arrays are read, inside their declared sizes; no index is followed, so any
+ * contents are safe to check. Two small launches, no allocation, no host synchronisation.
+ * Errors: PA_ERR_NULL (shape, cumulative_sequence_length, past_seqlens or flags NULL),
+ * PA_ERR_SHAPE or PA_ERR_UNSUPPORTED (the shape rules of pa_kv_append), PA_ERR_SHAPE
+ * (rotary_positions < 0), PA_ERR_HIP.
+ */
+#define PA_CHECK_CU_START 1
+#define PA_CHECK_CU_ORDER 2
+#define PA_CHECK_CU_END 4
+#define PA_CHECK_PAST 8
+#define PA_CHECK_TABLE_WIDTH 16
+#define PA_CHECK_TABLE_ENTRY 32
+#define PA_CHECK_SLOT 64
+#define PA_CHECK_SLOT_TABLE 128
+#define PA_CHECK_POSITION 256
+pa_status pa_check_paged_indices(const pa_paged_shape *shape,
+                                 const int32_t *cumulative_sequence_length,
+                                 const int32_t *past_seqlens, const int32_t *block_table,
+                                 const int32_t *slot_mapping, int32_t rotary_positions,
+                                 int32_t *flags, void *stream);
 
 /* Static description of a status code. */
 const char *pa_status_string(pa_status status);

@@ -286,3 +286,15 @@ def test_bnsh_append_rejects_bad_arguments():
               cos_cache=FAKE, sin_cache=FAKE) == pa.PA_ERR_SHAPE
     assert ap(sh(), present_key=None) == pa.PA_ERR_NULL
     assert ap(sh(seq_len=0), present_key=None) == pa.PA_OK
+
+
+def test_check_paged_indices_rejects_bad_arguments():
+    f = lambda shape, **kw: pa.pa_check_paged_indices(
+        shape, kw.get("cu", FAKE), kw.get("past", FAKE), FAKE, None, kw.get("flags", FAKE),
+        rotary_positions=kw.get("rot", 0), stream=0, check=False)
+    assert f(_shape(), flags=None) == pa.PA_ERR_NULL
+    assert f(_shape(), cu=None) == pa.PA_ERR_NULL
+    assert f(_shape(), past=None) == pa.PA_ERR_NULL
+    assert f(_shape(batch=0)) == pa.PA_ERR_SHAPE
+    assert f(_shape(head_size=96)) == pa.PA_ERR_UNSUPPORTED
+    assert f(_shape(), rot=-1) == pa.PA_ERR_SHAPE
