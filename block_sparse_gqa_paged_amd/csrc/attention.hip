@@ -11,8 +11,10 @@
 //    and a key chunk. The wave serves every query head of the kv group, so each K/V byte of the
 //    chunk is read from HBM once per work item.
 //  * QK^T and PV run on MFMA v_mfma_f32_16x16x32_f16. The score tile is S^T = K . Q^T with
-//    16 keys as rows and 16 (token, head) columns: K rows load straight from the cache as the A
-//    operand (16 contiguous bytes per lane), so no LDS is needed. The tile's C layout already
+//    16 keys as rows and 16 (token, head) columns. K rows are copied whole (256 bytes at D = 128,
+//    4 rows per copy instruction) from the cache into the wave's own LDS tile and read back in
+//    the A-operand layout: loaded straight into that layout, each instruction would fetch 64
+//    bytes of 16 different rows, which reads HBM about 8% slower. The tile's C layout already
 //    gives each lane 8 keys of one column, exactly the k-slots of the P operand of O = P . V.
 //    The V operand wants 8 keys of one dimension per lane; V is loaded as 16-byte row chunks
 //    (fully coalesced, 4 rows per load) and transposed in registers with byte permutes.
@@ -57,73 +59,109 @@ template <int D>
 struct Tile {
     static constexpr int KB = D / 32;  // 32-dim k-blocks of QK^T
     static constexpr int W = D / 16;   // dims per lane of the V layout (D = 16 * W)
-    half8_t k[2][KB];                  // A operand rows: keys kappa(u, n16), dims 32kb+8g16..+7
+    half8_t k[2][KB];                  // A operand rows (from LDS): keys kappa(u, n16), dims 32kb+8g16..+7
     uint32_t v[8][W / 2];              // keys 8*g16 + s, dims W*n16 .. W*n16 + W - 1
 };
 
-// Physical blocks a lane needs for the tile at kt (power-of-two block sizes >= 8): bk for its
-// K row group (keys kt + 8*(n16/4) ..) and bv for its V row group (keys kt + 8*g16 ..). Groups
-// past the last valid key are clamped to it, so no table entry beyond the range is read.
+// Physical block of a lane's V row group at the tile at kt (power-of-two block sizes >= 8):
+// keys kt + 8*g16 .. + 7, one aligned group, so one block. Lane 16j thereby holds the block of
+// group j, which the K copies of rows 8j .. 8j + 7 take by lane read. Groups past the last valid
+// key are clamped to it, so no table entry beyond the range is read.
 struct TileIds {
-    int bk, bv;
+    int bv;
 };
 
 __device__ __forceinline__ TileIds tile_ids(const AttnArgs &a, const int32_t *bt, int kt, int k1,
-                                            int g16, int n16) {
+                                            int g16) {
     const int lastg = (k1 - 1) & ~7;
-    TileIds r;
-    r.bk = bt[min(kt + 8 * (n16 >> 2), lastg) >> a.log2bs];
-    r.bv = bt[min(kt + 8 * g16, lastg) >> a.log2bs];
-    return r;
+    return TileIds{bt[min(kt + 8 * g16, lastg) >> a.log2bs]};
 }
 
-// Issue the 16 loads of the tile at kt. kcg / vcg point at kv head g of cache row 0. A row of
-// key j inside block B sits at B*block_elems + (j mod bs)*key_elems, so each lane forms one
-// 64-bit block base per row group and adds 32-bit in-block offsets. Keys past k1 - 1 load key
-// k1 - 1 instead (their scores are masked), so nothing outside the sequence is read.
+// XOR mask, in 16-byte chunks, of row r of a wave's LDS key tile: LDS chunk position p of row r
+// holds cache chunk p ^ krow_mask(r). The A-operand read takes the 16 rows kappa(u, 0..15) at
+// one chunk; the mask gives those rows distinct positions, so at D = 128 the 16 lanes of a
+// 256-byte read pass hit all 64 banks once.
+template <int KC>
+__device__ __forceinline__ int krow_mask(int r) {
+    return ((r & 3) | ((r >> 1) & 12)) & (KC - 1);
+}
+
+// One 16-byte global -> LDS copy per lane, non-temporal (the cache is read once): lane l writes
+// LDS bytes [16 l, 16 l + 16) of the wave-uniform destination dst.
+__device__ __forceinline__ void dma16_nt(const half_t *src, half_t *dst) {
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1))) *)src,
+        (void __attribute__((address_space(3))) *)dst, 16, 0, 2 /* nt */);
+}
+
+// Issue the copies of the K rows of the tile at kt into this wave's LDS tile kl [32 rows][D]
+// (row r = key kt + r). A copy instruction moves 64 * 16 / (2D) whole rows; keys past k1 - 1
+// copy key k1 - 1 instead (their scores are masked), so nothing outside the sequence is read.
+// A row of key j inside block B sits at B*block_elems + (j mod bs)*key_elems of kcg (kv head g
+// of cache row 0).
+template <int D, bool POW2>
+__device__ __forceinline__ void copy_k(const AttnArgs &a, const int32_t *bt, TileIds ids,
+                                       const half_t *kcg, int kt, int k1, int lane, half_t *kl) {
+    constexpr int KC = D / 8;      // 16-byte chunks per row
+    constexpr int RPI = 64 / KC;   // rows per copy instruction (4 or 8: inside one 8-key group)
+    const int klast = k1 - 1;
+    const uint32_t ke = a.key_elems;
+    const int rr = lane / KC, p = lane % KC;
+    for (int i = 0; i < kTileKeys / RPI; ++i) {
+        const int r = RPI * i + rr;
+        const int key = min(kt + r, klast);
+        const half_t *src;
+        if (POW2) {
+            // rows of group j = RPI*i/8 lie in the block lane 16j looked up for its V rows; the
+            // in-block offset uses a 24-bit multiply (key_elems < 2^24 is checked on the host)
+            const int blk = __builtin_amdgcn_readlane(ids.bv, 16 * ((RPI * i) >> 3));
+            src = kcg + (size_t)blk * a.block_elems + __umul24(key & (a.bs - 1), ke);
+        } else {
+            const int j = key / a.bs;
+            src = kcg + (size_t)bt[j] * a.block_elems + (uint32_t)(key - j * a.bs) * ke;
+        }
+        dma16_nt(src + 8 * (p ^ krow_mask<KC>(r)), kl + RPI * i * D);
+    }
+}
+
+// The A operands of the tile from the wave's LDS tile: row kappa(u, n16), dims 32kb+8g16 .. +7.
+template <int D>
+__device__ __forceinline__ void read_k(Tile<D> &t, const half_t *kl, int g16, int n16) {
+    constexpr int KC = D / 8, KB = Tile<D>::KB;
+    for (int u = 0; u < 2; ++u) {
+        const int r = kappa(u, n16);
+        for (int kb = 0; kb < KB; ++kb)
+            t.k[u][kb] = *(const half8_t *)(kl + r * D + 8 * ((4 * kb + g16) ^ krow_mask<KC>(r)));
+    }
+}
+
+// Issue the 8 V loads of the tile at kt into registers: lane (g16, n16) takes dims W*n16 ..
+// of keys kt + 8*g16 + s (4 whole rows per instruction). vcg points at kv head g of cache row
+// 0. Keys past k1 - 1 load key k1 - 1 instead.
 template <int D, bool POW2, bool NT>
-__device__ __forceinline__ void load_tile(Tile<D> &t, const AttnArgs &a, const int32_t *bt,
-                                          TileIds ids, const half_t *kcg, const half_t *vcg,
-                                          int kt, int k1, int g16, int n16) {
-    constexpr int KB = Tile<D>::KB, W = Tile<D>::W;
+__device__ __forceinline__ void load_v(Tile<D> &t, const AttnArgs &a, const int32_t *bt,
+                                       TileIds ids, const half_t *vcg, int kt, int k1, int g16,
+                                       int n16) {
+    constexpr int W = Tile<D>::W;
     const int kl = k1 - 1;
     const uint32_t ke = a.key_elems;
-    const half_t *pk[2];
     const half_t *pv[8];
     if (POW2) {
         // bs is a power of two >= 8, so each aligned 8-key group lies inside one block.
-        const int lastg = kl & ~7;
-        const int gk = min(kt + 8 * (n16 >> 2), lastg);
-        const int gv = min(kt + 8 * g16, lastg);
-        const int mask = a.bs - 1;
-        // In-block offsets use 24-bit multiplies: key_elems < 2^24 is checked on the host.
-        const half_t *bK = kcg + (size_t)ids.bk * a.block_elems + __umul24(gk & mask, ke);
-        const half_t *bV = vcg + (size_t)ids.bv * a.block_elems + __umul24(gv & mask, ke);
+        const int gv = min(kt + 8 * g16, kl & ~7);
+        const half_t *bV = vcg + (size_t)ids.bv * a.block_elems + __umul24(gv & (a.bs - 1), ke);
         if (kt + kTileKeys <= k1) {
-            const uint32_t r0 = __umul24(n16 & 3, ke);
-            pk[0] = bK + r0;
-            pk[1] = bK + r0 + 4 * ke;
             for (int s = 0; s < 8; ++s) pv[s] = bV + (uint32_t)s * ke;
         } else {
-            for (int u = 0; u < 2; ++u) pk[u] = bK + __umul24(min(kt + kappa(u, n16), kl) - gk, ke);
             for (int s = 0; s < 8; ++s) pv[s] = bV + __umul24(min(kt + 8 * g16 + s, kl) - gv, ke);
         }
     } else {
-        for (int u = 0; u < 2; ++u) {
-            const int key = min(kt + kappa(u, n16), kl);
-            const int j = key / a.bs;
-            pk[u] = kcg + (size_t)bt[j] * a.block_elems + (uint32_t)(key - j * a.bs) * ke;
-        }
         for (int s = 0; s < 8; ++s) {
             const int key = min(kt + 8 * g16 + s, kl);
             const int j = key / a.bs;
             pv[s] = vcg + (size_t)bt[j] * a.block_elems + (uint32_t)(key - j * a.bs) * ke;
         }
     }
-    for (int u = 0; u < 2; ++u)
-        for (int kb = 0; kb < KB; ++kb)
-            t.k[u][kb] = NT ? gload_nt<half8_t>(pk[u] + 8 * g16 + 32 * kb)
-                            : gload<half8_t>(pk[u] + 8 * g16 + 32 * kb);
     for (int s = 0; s < 8; ++s) {
         const half_t *p = pv[s] + W * n16;
         if constexpr (W == 8) {
@@ -224,7 +262,7 @@ __device__ __forceinline__ void tile_softmax_pv(State<D, NCB> &st, const float4_
 // Work of one (item, kv head) unit: one wave.
 template <int D, int NCB, bool POW2, bool NT>
 __device__ __forceinline__ void process_unit(const AttnArgs &a, const AttnItem &it, int g,
-                                             int lane) {
+                                             int lane, half_t *kl) {
     constexpr int KB = D / 32, W = D / 16;
     const int g16 = lane >> 4, n16 = lane & 15;
     const int cu_b = a.cu[it.b];
@@ -252,40 +290,49 @@ __device__ __forceinline__ void process_unit(const AttnArgs &a, const AttnItem &
         }
     }
 
-    // One tile buffer. In each step the tile's scores and V^T operands are formed first,
-    // then the next tile's loads are issued while softmax and PV run. The last tile is
-    // peeled off so the in-loop load is unconditional. The block ids of tile t+2 are
-    // requested before the data loads of tile t+1, so by the time a tile's loads issue its
-    // ids have arrived (loads complete in order).
+    // One tile buffer: K rows in the wave's LDS tile kl, V rows in registers. In each step the
+    // tile's K operands are read from LDS, its scores and V^T operands are formed, then the next
+    // tile's copies and loads are issued while softmax and PV run. The last tile is peeled off
+    // so the in-loop copies are unconditional. The block ids of tile t+2 are requested before
+    // the copies of tile t+1, so they have arrived when those copies issue.
     const int32_t *bt = a.bt + (long long)it.b * a.MB;
     const half_t *kcg = a.kc + (size_t)g * D;
     const half_t *vcg = a.vc + (size_t)g * D;
     if (it.k0 < it.k1) {
         Tile<D> tl;
         int kt = it.k0;
-        TileIds ids2 = {0, 0};
-        if (POW2) ids2 = tile_ids(a, bt, kt, it.k1, g16, n16);
-        load_tile<D, POW2, NT>(tl, a, bt, ids2, kcg, vcg, kt, it.k1, g16, n16);
-        if (POW2 && kt + kTileKeys < it.k1)
-            ids2 = tile_ids(a, bt, kt + kTileKeys, it.k1, g16, n16);
+        TileIds ids2 = {0};
+        if (POW2) ids2 = tile_ids(a, bt, kt, it.k1, g16);
+        copy_k<D, POW2>(a, bt, ids2, kcg, kt, it.k1, lane, kl);
+        load_v<D, POW2, NT>(tl, a, bt, ids2, vcg, kt, it.k1, g16, n16);
+        if (POW2 && kt + kTileKeys < it.k1) ids2 = tile_ids(a, bt, kt + kTileKeys, it.k1, g16);
         for (; kt + kTileKeys < it.k1; kt += kTileKeys) {
+            // the LDS copies are tracked by the vector-memory counter only: wait for all
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+            read_k<D>(tl, kl, g16, n16);
             float4_t s[NCB][2];
             tile_scores<D, NCB>(st, tl, s);
             half8_t vb[W];
             tile_vt<D>(tl, vb);
             const int kn = kt + kTileKeys;
             TileIds ids3 = ids2;
-            if (POW2 && kn + kTileKeys < it.k1)
-                ids3 = tile_ids(a, bt, kn + kTileKeys, it.k1, g16, n16);
-            load_tile<D, POW2, NT>(tl, a, bt, ids2, kcg, vcg, kn, it.k1, g16, n16);
+            if (POW2 && kn + kTileKeys < it.k1) ids3 = tile_ids(a, bt, kn + kTileKeys, it.k1, g16);
+            // the K operand reads are back before the next copies overwrite the tile
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+            copy_k<D, POW2>(a, bt, ids2, kcg, kn, it.k1, lane, kl);
+            load_v<D, POW2, NT>(tl, a, bt, ids2, vcg, kn, it.k1, g16, n16);
             tile_softmax_pv<D, NCB>(st, s, vb, kt, a.scale_log2, g16);
             ids2 = ids3;
         }
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        read_k<D>(tl, kl, g16, n16);
         float4_t s[NCB][2];
         tile_scores<D, NCB>(st, tl, s);
         half8_t vb[W];
         tile_vt<D>(tl, vb);
         tile_softmax_pv<D, NCB>(st, s, vb, kt, a.scale_log2, g16);
+        // the tile's LDS reads are back before another unit's copies reuse it
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     }
 
     // Column totals, then each lane writes rows 4*g16 + j of every column block.
@@ -338,15 +385,17 @@ __device__ __forceinline__ void process_unit(const AttnArgs &a, const AttnItem &
 // workgroups take (item, head group) units from the planner's counter, longest items first.
 template <int D, int NCB, bool POW2, bool NT>
 __global__ __launch_bounds__(NCB == 1 ? 512 : 64) void attn_kernel(AttnArgs a) {
+    extern __shared__ half_t s_ktile[];  // one 32-key K tile per wave: [gw][32][D]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    half_t *kl = s_ktile + wave * (kTileKeys * D);
     const int gblocks = a.G / a.gw;
     if (a.slot_ptr) {
         const int u0 = a.slot_ptr[blockIdx.x] * gblocks, u1 = a.slot_ptr[blockIdx.x + 1] * gblocks;
         for (int unit = u0; unit < u1; ++unit) {
             const AttnItem it = a.items[unit / gblocks];
             const int g = (unit - (unit / gblocks) * gblocks) * a.gw + wave;
-            process_unit<D, NCB, POW2, NT>(a, it, g, lane);
+            process_unit<D, NCB, POW2, NT>(a, it, g, lane, kl);
         }
         return;
     }
@@ -361,17 +410,18 @@ __global__ __launch_bounds__(NCB == 1 ? 512 : 64) void attn_kernel(AttnArgs a) {
         if (unit >= n_work) break;
         const AttnItem it = a.items[unit / gblocks];
         const int g = (unit - (unit / gblocks) * gblocks) * a.gw + wave;
-        process_unit<D, NCB, POW2, NT>(a, it, g, lane);
+        process_unit<D, NCB, POW2, NT>(a, it, g, lane, kl);
     }
 }
 
 template <int D, int NCB, bool NT>
 pa_status launch_d_ncb(const AttnArgs &a, int blocks, LaunchScope &scope) {
     const dim3 g(blocks), blk(64 * a.gw);
+    const uint32_t lds = (uint32_t)(a.gw * kTileKeys * D * sizeof(half_t));  // <= 64 KB
     if (a.log2bs >= 0)
-        scope.launch(attn_kernel<D, NCB, true, NT>, g, blk, 0, a);
+        scope.launch(attn_kernel<D, NCB, true, NT>, g, blk, lds, a);
     else
-        scope.launch(attn_kernel<D, NCB, false, NT>, g, blk, 0, a);
+        scope.launch(attn_kernel<D, NCB, false, NT>, g, blk, lds, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
