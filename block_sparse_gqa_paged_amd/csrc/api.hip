@@ -95,7 +95,7 @@ struct PagedPlan {
     int Q, ncb_dec, tpi_dec, tpi_pre;
     int mode, splits, gw, slots;
     int cap_dec, cap_pre, cap_comb, unit_cap;
-    size_t off_dec, off_pre, off_comb, off_slot, off_o, off_m, off_l, total;
+    size_t off_dec, off_pre, off_comb, off_slot, off_first, off_o, off_m, off_l, total;
 };
 
 pa_status check_shape(const pa_paged_shape *s) {
@@ -161,6 +161,8 @@ bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
     off = align_up(off + sizeof(CombItem) * (size_t)p.cap_comb);
     p.off_slot = off;
     off = align_up(off + sizeof(int32_t) * (size_t)(p.slots + 1));
+    p.off_first = off;
+    off = align_up(off + sizeof(AttnItem) * (size_t)p.slots);
     p.off_o = off;
     off = align_up(off + sizeof(float) * (size_t)p.unit_cap * H * D);
     p.off_m = off;
@@ -399,6 +401,7 @@ pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t
     pl.splits = p.splits;
     pl.slots = p.slots;
     pl.slot_ptr = (int32_t *)(ws + p.off_slot);
+    pl.slot_first = (AttnItem *)(ws + p.off_first);
     pl.min_chunk = kSplitMinKeys;
     pl.unit_cap = p.unit_cap;
     pl.cap_dec = p.cap_dec;
@@ -441,6 +444,7 @@ pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t
     a.tpi = p.tpi_dec;
     if (p.mode == 0) {
         a.slot_ptr = pl.slot_ptr;
+        a.slot_first = pl.slot_first;
         call.blocks = p.slots;
     } else {
         a.slot_ptr = nullptr;

@@ -265,9 +265,7 @@ __device__ __forceinline__ void process_unit(const AttnArgs &a, const AttnItem &
                                              int lane, half_t *kl) {
     constexpr int KB = D / 32, W = D / 16;
     const int g16 = lane >> 4, n16 = lane & 15;
-    const int cu_b = a.cu[it.b];
-    const int n_b = a.cu[it.b + 1] - cu_b;
-    const int past_b = a.past[it.b];
+    const int cu_b = it.cu0, n_b = it.n, past_b = it.past;
     const int ntok = min(a.tpi, n_b - it.t0);
     const int ncols = ntok * a.Q;
 
@@ -392,8 +390,12 @@ __global__ __launch_bounds__(NCB == 1 ? 512 : 64) void attn_kernel(AttnArgs a) {
     const int gblocks = a.G / a.gw;
     if (a.slot_ptr) {
         const int u0 = a.slot_ptr[blockIdx.x] * gblocks, u1 = a.slot_ptr[blockIdx.x + 1] * gblocks;
+        // the share's first item comes from its own copy (requested beside the share bounds),
+        // and each later unit's item is requested while the unit before it runs
+        AttnItem next = a.slot_first[blockIdx.x];
         for (int unit = u0; unit < u1; ++unit) {
-            const AttnItem it = a.items[unit / gblocks];
+            const AttnItem it = next;
+            if (unit + 1 < u1) next = a.items[(unit + 1) / gblocks];
             const int g = (unit - (unit / gblocks) * gblocks) * a.gw + wave;
             process_unit<D, NCB, POW2, NT>(a, it, g, lane, kl);
         }

@@ -101,7 +101,9 @@ struct AttnItem {
     int32_t base;  // first partial unit of the sequence, or -1: write the output directly
     int32_t nsplit;  // chunks the sequence's key range is cut into
     int32_t split;   // this item's chunk
-    int32_t comb;    // combine-list entry of the item's first row, or -1
+    int32_t cu0;     // the sequence's first query row (cumulative_sequence_length[b])
+    int32_t n;       // the sequence's new tokens
+    int32_t past;    // the sequence's past length (past_seqlens[b])
 };
 
 // Combine work entry for one output row group (a query row with >= 2 partial units).
@@ -137,6 +139,7 @@ struct PlanArgs {
     int cap_dec, cap_pre, cap_comb;
     int slots;          // mode 0: decode workgroups, one key-range share each
     int32_t *slot_ptr;  // mode 0: [slots + 1] first item of each share
+    AttnItem *slot_first;  // mode 0: [slots] a copy of the first item of each share
     PlanHeader *hdr;
     AttnItem *dec;
     AttnItem *pre;
@@ -159,6 +162,7 @@ struct AttnArgs {
     const int32_t *n_items;  // device count of items
     int32_t *counter;        // dynamic scheduling counter (zeroed by the planner)
     const int32_t *slot_ptr; // stream-K share table [gridDim.x + 1], or NULL for dynamic
+    const AttnItem *slot_first;  // with slot_ptr: [gridDim.x] first item of each share
     half_t *out;
     float *o_part;
     float *m_part;

@@ -200,7 +200,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
                 AttnItem it;
                 it.b = b; it.t0 = 0;
                 it.base = c >= 2 ? ubase : -1; it.nsplit = c; it.split = sp;
-                it.comb = c >= 2 ? cbase : -1;
+                it.cu0 = cu0; it.n = n; it.past = past;
                 int idx;
                 if (streamk) {
                     idx = carry[0] + ex[0] + sp;
@@ -208,7 +208,10 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
                     const long long t0 = max(TB, j * q), t1 = min(TB + T, (j + 1) * q);
                     it.k0 = (int)(t0 - TB) * kTileKeys;
                     it.k1 = min(L, (int)(t1 - TB) * kTileKeys);
-                    if (t0 == j * q && j < a.slots) a.slot_ptr[j] = idx;
+                    if (t0 == j * q && j < a.slots) {
+                        a.slot_ptr[j] = idx;
+                        a.slot_first[j] = it;
+                    }
                 } else {
                     const bool is_tail = sp >= c - tail;
                     idx = is_tail ? full_total + carry_tail + tlex : carry[0] - carry_tail +
@@ -261,7 +264,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs &a) {
             AttnItem it;
             it.b = b; it.t0 = tile * a.tpi_pre; it.k0 = 0;
             it.k1 = pre_k1(tile, n, past);
-            it.base = -1; it.nsplit = 1; it.split = 0; it.comb = -1;
+            it.base = -1; it.nsplit = 1; it.split = 0;
+            it.cu0 = cu0; it.n = n; it.past = past;
             const int idx = atomicAdd(&sh_bin[pre_bin<TH>(it.k1)], 1);
             if (idx < a.cap_pre) a.pre[idx] = it;
         }

@@ -179,9 +179,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
         if (unit >= n_work) break;
         const AttnItem it = a.items[unit / a.G];
         const int g = unit - (unit / a.G) * a.G;
-        const int cu_b = a.cu[it.b];
-        const int n_b = a.cu[it.b + 1] - cu_b;
-        const int past_b = a.past[it.b];
+        const int cu_b = it.cu0, n_b = it.n, past_b = it.past;
         const int ntok = min(a.tpi, n_b - it.t0);
         const int ncols = ntok * a.Q;
 
