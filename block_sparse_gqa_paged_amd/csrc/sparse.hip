@@ -253,9 +253,12 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
     };
 
     // ---- stage the key block. A task is 4 consecutive keys x 8 dims of K and of V (32 + 32
-    // floats). Pass 1 loads and takes the block-wide max |K| and |V|; pass 2 scales by the
-    // powers of two, splits into fp16 hi/lo and stores K row-major and V transposed. With one
-    // task per thread the pass-1 registers are reused; otherwise pass 2 reloads (from L2).
+    // floats): dims 4q .. 4q+3 and D/2 + 4q .. +3, so that the 16-byte loads of the D/8 lanes of
+    // a key quad read whole contiguous half rows (a load instruction of 16-byte pieces at a
+    // 32-byte stride reads HBM more slowly). Pass 1 loads and takes the block-wide max |K| and
+    // |V|; pass 2 scales by the powers of two, splits into fp16 hi/lo and stores K row-major and
+    // V transposed. With one task per thread the pass-1 registers are reused; otherwise pass 2
+    // reloads (from L2).
     constexpr int TASKS = BSP / 4 * KQ;                       // (key quad, 8-dim chunk) pairs
     constexpr int TPT = (TASKS + kThreads - 1) / kThreads;    // tasks per thread
     float kr[4][8], vr[4][8];
@@ -266,10 +269,10 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
             const int pid = page_of(t);
             for (int x = 0; x < 8; ++x) { kr[r][x] = 0.f; vr[r][x] = 0.f; }
             if (pid >= 0) {
-                const float *pk = row_ptr(a.kp, pid, t) + 8 * q;
-                const float *pv = row_ptr(a.vp, pid, t) + 8 * q;
-                const float4_t k0 = gload<float4_t>(pk), k1 = gload<float4_t>(pk + 4);
-                const float4_t v0 = gload<float4_t>(pv), v1 = gload<float4_t>(pv + 4);
+                const float *pk = row_ptr(a.kp, pid, t) + 4 * q;
+                const float *pv = row_ptr(a.vp, pid, t) + 4 * q;
+                const float4_t k0 = gload<float4_t>(pk), k1 = gload<float4_t>(pk + D / 2);
+                const float4_t v0 = gload<float4_t>(pv), v1 = gload<float4_t>(pv + D / 2);
                 for (int x = 0; x < 4; ++x) {
                     kr[r][x] = k0[x]; kr[r][4 + x] = k1[x];
                     vr[r][x] = v0[x]; vr[r][4 + x] = v1[x];
@@ -312,15 +315,19 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
                 hi[x] = v.hi;
                 lo[x] = v.lo;
             }
-            const int off = t * D + 8 * swz(t, q, KQ);
-            *(half8_t *)(Khi + off) = hi;
-            *(half8_t *)(Klo + off) = lo;
+            // dims 4q .. are chunk q/2, dims D/2 + 4q .. chunk KQ/2 + q/2, at half (q & 1)
+            const int off0 = t * D + 8 * swz(t, q >> 1, KQ) + 4 * (q & 1);
+            const int off1 = t * D + 8 * swz(t, KQ / 2 + (q >> 1), KQ) + 4 * (q & 1);
+            *(half4_t *)(Khi + off0) = half4_t{hi[0], hi[1], hi[2], hi[3]};
+            *(half4_t *)(Klo + off0) = half4_t{lo[0], lo[1], lo[2], lo[3]};
+            *(half4_t *)(Khi + off1) = half4_t{hi[4], hi[5], hi[6], hi[7]};
+            *(half4_t *)(Klo + off1) = half4_t{lo[4], lo[5], lo[6], lo[7]};
         }
         // V^T row d holds, in 16-byte chunk 4c + g of a 32-key block c, the keys
         // 32c + 4g .. +3 and 32c + 16 + 4g .. +3: the k-slots (g, 0..7) of one PV operand.
         const int vq = 4 * (t4 >> 3) + (t4 & 3), vh = 4 * ((t4 >> 2) & 1);
         for (int x = 0; x < 8; ++x) {
-            const int d = 8 * q + x;
+            const int d = x < 4 ? 4 * q + x : D / 2 + 4 * q + (x - 4);
             half4_t hi, lo;
             for (int r = 0; r < 4; ++r) {
                 const HiLo v = split16(ldexpf(vr[r][x], -eV));
