@@ -11,7 +11,8 @@
 // wave takes R row blocks of a group at once. The rows of one unit are adjacent in memory, so a
 // wave's loads for one unit are one contiguous span (with R = 2 and four rows per unit at
 // D = 128, the unit's whole 2 KB). Units are merged online, 8 / R per memory round trip
-// (running max, rescaled sums). wave / nwaves: this wave's index among the waves that share the
+// (running max, rescaled sums), the next round's loads in flight while one is merged.
+// wave / nwaves: this wave's index among the waves that share the
 // work (grid-stride over groups' row-block pairs). mode: 0 uniform splits, 1 CSR offsets,
 // 2 planner list. combine_dispatch picks R from the row count.
 #pragma once
@@ -55,9 +56,11 @@ __device__ __forceinline__ void combine_rows(const CombineArgs &a, int mode, int
         for (int j = 0; j < R; ++j) {
             M[j] = -INFINITY; Ls[j] = 0.f; acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
         }
-        for (long long e = e0; e < e1; e += NB) {
-            float mv[NB][R], lv[NB][R];
-            float4_t ov[NB][R];
+        // Software-pipelined: the loads of round e + NB are issued before round e is merged,
+        // so a wave always has a round of partials in flight.
+        float mv[NB][R], lv[NB][R];
+        float4_t ov[NB][R];
+        auto load_round = [&](long long e) {
             for (int u = 0; u < NB; ++u) {
                 const long long eu = e + u < e1 ? e + u : e1 - 1;
                 for (int j = 0; j < R; ++j) {
@@ -67,10 +70,20 @@ __device__ __forceinline__ void combine_rows(const CombineArgs &a, int mode, int
                     ov[u][j] = gload_nt<float4_t>(a.o + p * D + 4 * sub);
                 }
             }
+        };
+        if (e0 < e1) load_round(e0);
+        for (long long e = e0; e < e1; e += NB) {
+            float cm[NB][R], cl[NB][R];
+            float4_t co[NB][R];
+            for (int u = 0; u < NB; ++u)
+                for (int j = 0; j < R; ++j) {
+                    cm[u][j] = mv[u][j]; cl[u][j] = lv[u][j]; co[u][j] = ov[u][j];
+                }
+            if (e + NB < e1) load_round(e + NB);
             for (int j = 0; j < R; ++j) {
                 float bm = -INFINITY;
                 for (int u = 0; u < NB; ++u)
-                    if (lv[u][j] > 0.f) bm = fmaxf(bm, mv[u][j]);
+                    if (cl[u][j] > 0.f) bm = fmaxf(bm, cm[u][j]);
                 if (bm == -INFINITY) continue;
                 const float Mn = fmaxf(M[j], bm);
                 const float sc =
@@ -79,9 +92,9 @@ __device__ __forceinline__ void combine_rows(const CombineArgs &a, int mode, int
                 Ls[j] *= sc;
                 for (int u = 0; u < NB; ++u) {
                     const float wu =
-                        lv[u][j] > 0.f ? __builtin_amdgcn_exp2f((mv[u][j] - Mn) * kLog2e) : 0.f;
-                    acc[j] += wu * ov[u][j];
-                    Ls[j] += wu * lv[u][j];
+                        cl[u][j] > 0.f ? __builtin_amdgcn_exp2f((cm[u][j] - Mn) * kLog2e) : 0.f;
+                    acc[j] += wu * co[u][j];
+                    Ls[j] += wu * cl[u][j];
                 }
                 M[j] = Mn;
             }
