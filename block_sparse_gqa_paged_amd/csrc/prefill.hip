@@ -321,19 +321,35 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
             }
         }
 
-        // Column totals; lane (g16, n16) writes dims 16*dt + 4*g16 .. +3 of column n16.
+        // Output. Lane (g16, n16) holds dims 16*dt + 4*g16 .. +3 of its two columns; stored
+        // directly, each instruction would write 8 bytes into 16 columns. The wave's 32 columns
+        // go instead through its own part of the LDS stage the last tile did not use (every wave
+        // finished the tile before it at the last barrier; the next unit's first copies land
+        // only after the next unit's barriers), XOR-swizzled by column, and leave as whole
+        // columns: 64*16/(2D) columns per store instruction, a token's Q heads contiguous.
+        constexpr int CPL = D / 8;  // 16-byte chunks per column
+        half_t *ost = (wave < 2 ? Ks[ntl & 1] : Vs[ntl & 1]) + (wave & 1) * 32 * D;
         for (int cb = 0; cb < 2; ++cb) {
             const float lt = col_sum(l[cb]);
-            const int col = 32 * wave + 16 * cb + n16;
-            if (col >= ncols) continue;
-            const int t = col / a.Q, qh = col - t * a.Q;
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            half_t *op = a.out + (long long)(cu_b + it.t0 + t) * a.H * D +
-                         (long long)(g * a.Q + qh) * D + 4 * g16;
+            const int lc = 16 * cb + n16;
             for (int dt = 0; dt < NDT; ++dt) {
                 half4_t r;
                 for (int i = 0; i < 4; ++i) r[i] = (half_t)(o[cb][dt][i] * inv);
-                *(half4_t *)(op + 16 * dt) = r;
+                const int ch = 2 * dt + (g16 >> 1);
+                *(half4_t *)(ost + lc * D + 8 * (ch ^ (lc & (CPL - 1))) + 4 * (g16 & 1)) = r;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 4
+        for (int j = 0; j < CPL / 2; ++j) {
+            const int lc = (64 / CPL) * j + lane / CPL, ch = lane % CPL;
+            const half8_t v = *(const half8_t *)(ost + lc * D + 8 * (ch ^ (lc & (CPL - 1))));
+            const int col = 32 * wave + lc;
+            if (col < ncols) {
+                const int t = col / a.Q, qh = col - t * a.Q;
+                *(half8_t *)(a.out + (long long)(cu_b + it.t0 + t) * a.H * D +
+                             (long long)(g * a.Q + qh) * D + 8 * ch) = v;
             }
         }
     }
