@@ -13,7 +13,7 @@ decode attention kernel alone: algorithmic KV bytes per launch / its mean launch
 events recorded by the library on the launch stream, against 8 TB/s. `cpu_baseline` times the
 CPU oracle on the same workload's attention rows. `extra` carries the mixed prefill+decode and
 block-sparse workloads. Beside the contract's mean over the timed steps: p10 / p50 / p90 of 100
-individually timed steps, and the box's own 1 GiB device-copy rate (bytes read + written) as a
+individually timed steps, and the GPU's own 1 GiB device-copy rate (bytes read + written) as a
 second reference next to the 8 TB/s peak.
 """
 import argparse
@@ -115,8 +115,8 @@ def step_percentiles(fn, n, warmup, torch, np):
     return {f"p{q}": round(float(np.percentile(t, q)), 4) for q in (10, 50, 90)}
 
 
-def box_copy_gbps(torch, nbytes=1 << 30, reps=5):
-    """The box's own device-to-device copy rate (bytes read + bytes written per second)."""
+def device_copy_gbps(torch, nbytes=1 << 30, reps=5):
+    """The GPU's own device-to-device copy rate (bytes read + bytes written per second)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -207,7 +207,7 @@ def main():
     ms_plain, _ = timed(step, args.steps, args.warmup, torch)
     ms_two, _ = timed(step_two_calls, args.steps, args.warmup, torch)
     pct = step_percentiles(step, 100, 10, torch, np)
-    copy_gbps = box_copy_gbps(torch)
+    copy_gbps = device_copy_gbps(torch)
     print(f"# step {ms_plain:.4f} ms (with event hooks {ms:.4f} ms; as two calls {ms_two:.4f} ms)",
           file=sys.stderr, flush=True)
 
@@ -268,7 +268,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles("attn_decode"),
                      "kernel": "attn_decode", "kernel_us": round(dec_ms * 1e3, 2),
-                     "box_copy_GBps_read_plus_write": copy_gbps},
+                     "device_copy_GBps_read_plus_write": copy_gbps},
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
         "extra": extra,
