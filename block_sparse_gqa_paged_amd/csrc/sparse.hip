@@ -257,7 +257,8 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
     // ---- stage the key block. A task is 4 consecutive keys x 8 dims of K and of V (32 + 32
     // floats): dims 4q .. 4q+3 and D/2 + 4q .. +3, so that the 16-byte loads of the D/8 lanes of
     // a key quad read whole contiguous half rows (a load instruction of 16-byte pieces at a
-    // 32-byte stride reads HBM more slowly). Pass 1 loads and takes the block-wide max |K| and
+    // 32-byte stride reads HBM more slowly), non-temporal. Pass 1 loads and takes the block-wide
+    // max |K| and
     // |V|; pass 2 scales by the powers of two, splits into fp16 hi/lo and stores K row-major and
     // V transposed. With one task per thread the pass-1 registers are reused; otherwise pass 2
     // reloads (from L2).
@@ -273,8 +274,8 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
             if (pid >= 0) {
                 const float *pk = row_ptr(a.kp, pid, t) + 4 * q;
                 const float *pv = row_ptr(a.vp, pid, t) + 4 * q;
-                const float4_t k0 = gload<float4_t>(pk), k1 = gload<float4_t>(pk + D / 2);
-                const float4_t v0 = gload<float4_t>(pv), v1 = gload<float4_t>(pv + D / 2);
+                const float4_t k0 = gload_nt<float4_t>(pk), k1 = gload_nt<float4_t>(pk + D / 2);
+                const float4_t v0 = gload_nt<float4_t>(pv), v1 = gload_nt<float4_t>(pv + D / 2);
                 for (int x = 0; x < 4; ++x) {
                     kr[r][x] = k0[x]; kr[r][4 + x] = k1[x];
                     vr[r][x] = v0[x]; vr[r][4 + x] = v1[x];
