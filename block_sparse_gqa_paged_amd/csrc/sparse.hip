@@ -184,7 +184,8 @@ __global__ __launch_bounds__(256) void sp_qsplit(SparseArgs a, SparseWs w, long 
     const int c = (int)(gid - row * LPR);
     const long long r = row < rows ? row : rows - 1;
     const float *src = a.q + r * D + 8 * c;
-    const float4_t x0 = gload<float4_t>(src), x1 = gload<float4_t>(src + 4);
+    // the fp32 query rows are read once here (the planes written below are what the forward reads)
+    const float4_t x0 = gload_nt<float4_t>(src), x1 = gload_nt<float4_t>(src + 4);
     float mx = 0.f;
     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(fabsf(x0[i]), fabsf(x1[i])));
     for (int o = LPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
