@@ -458,8 +458,8 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
         // n16, so a direct store instruction would write 64 bytes into each of 16 rows; at this
         // occupancy that writes HBM about 20% slower than whole 128-byte lines. Each 128-byte
         // line j of 8 rows goes through the wave's 1 KB LDS slab instead and leaves as one
-        // store of 8 whole lines (lane l: row 8h + l/8, dims 32j + 4(l%8) ..). m and l come from
-        // g16 == 0.
+        // store of 8 whole lines (lane l: row 8h + l/8, dims 32j + 4(l%8) ..), non-temporal (the
+        // 2 GB of partials are read back only by the merge). m and l come from g16 == 0.
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next group's query loads (above)
         if (vrow && g16 == 0) {
             const long long p = (long long)e * a.qhead + qh;
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
                     *(float4_t *)(rowp + 16 + 4 * g16) = v1;
                 }
                 const float4_t v = *(const float4_t *)(slab + 4 * lane);
-                if (rvalid) *(float4_t *)(dst + 32 * j) = v;
+                if (rvalid) __builtin_nontemporal_store(v, (float4_t *)(dst + 32 * j));
             }
         }
     }
