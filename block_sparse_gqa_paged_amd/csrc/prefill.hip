@@ -348,8 +348,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
             const int col = 32 * wave + lc;
             if (col < ncols) {
                 const int t = col / a.Q, qh = col - t * a.Q;
-                *(half8_t *)(a.out + (long long)(cu_b + it.t0 + t) * a.H * D +
-                             (long long)(g * a.Q + qh) * D + 8 * ch) = v;
+                half_t *dst = a.out + (long long)(cu_b + it.t0 + t) * a.H * D +
+                              (long long)(g * a.Q + qh) * D + 8 * ch;
+                __builtin_nontemporal_store(v, (half8_t *)dst);  // written once
             }
         }
     }
