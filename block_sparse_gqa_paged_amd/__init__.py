@@ -27,7 +27,7 @@ PA_CHECK_TABLE_WIDTH, PA_CHECK_TABLE_ENTRY, PA_CHECK_SLOT = 16, 32, 64
 PA_CHECK_SLOT_TABLE, PA_CHECK_POSITION = 128, 256
 
 EXPORTED = ("pa_kv_append", "pa_kv_append_rotate_query", "pa_paged_attention_workspace_size",
-            "pa_paged_attention", "pa_append_attention",
+            "pa_paged_attention", "pa_paged_attention_noalloc", "pa_append_attention",
             "pa_split_combine", "pa_sparse_forward_workspace_size", "pa_sparse_forward",
             "pa_sparse_forward_causal", "pa_sparse_build_edges_workspace_size",
             "pa_sparse_build_edges", "pa_kv_append_bnsh", "pa_check_paged_indices",
@@ -85,6 +85,9 @@ def lib():
     L.pa_paged_attention.argtypes = ([sp] + [_vp] * 6 + [C.c_float, _i32, _i32, _vp, C.c_size_t,
                                                          _vp, _vp])
     L.pa_paged_attention.restype = _i32
+    L.pa_paged_attention_noalloc.argtypes = [sp] + [_vp] * 6 + [C.c_float, _i32, _i32, _vp,
+                                                                _vp]
+    L.pa_paged_attention_noalloc.restype = _i32
     L.pa_append_attention.argtypes = ([sp] + [_vp] * 11 + [_i32, _i32, _i32, _vp, C.c_float,
                                       _i32, _i32, _vp, C.c_size_t, _vp, _vp])
     L.pa_append_attention.restype = _i32
@@ -198,6 +201,19 @@ def pa_paged_attention(shape, query, key_cache, value_cache, cumulative_sequence
         int(causal), int(num_splits), _p(workspace), int(workspace_bytes), _p(output),
         _s(stream))
     return _check(st, "pa_paged_attention", check)
+
+
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/pa.h
+
+
+def pa_paged_attention_noalloc(shape, query, key_cache, value_cache, cumulative_sequence_length,
+                               past_seqlens, block_table, scale, causal, num_splits, output,
+                               stream=None, check=True):
+    st = lib().pa_paged_attention_noalloc(
+        C.byref(shape), _p(query), _p(key_cache), _p(value_cache),
+        _p(cumulative_sequence_length), _p(past_seqlens), _p(block_table), float(scale),
+        int(causal), int(num_splits), _p(output), _s(stream))
+    return _check(st, "pa_paged_attention_noalloc", check)
 
 
 def pa_append_attention(shape, query, key, value, key_cache, value_cache,

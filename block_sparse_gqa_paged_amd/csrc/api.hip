@@ -372,13 +372,14 @@ struct AttnCall {
     bool combine;
 };
 
-// q_stride: the query row stride in elements.
+// q_stride: the query row stride in elements. With validate_only the call checks every
+// argument except the workspace pointer (its size against workspace_bytes) and fills nothing.
 pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t q_stride,
                          const void *key_cache, const void *value_cache,
                          const int32_t *cumulative_sequence_length, const int32_t *past_seqlens,
                          const int32_t *block_table, float scale, int32_t causal,
                          int32_t num_splits, void *workspace, size_t workspace_bytes,
-                         void *output, AttnCall &call) {
+                         void *output, AttnCall &call, bool validate_only = false) {
     pa_status st = check_shape(shape);
     if (st != PA_OK) return st;
     if (causal != 0 && causal != 1) return PA_ERR_SHAPE;
@@ -390,6 +391,7 @@ pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t
     PagedPlan p;
     if (!make_plan(shape, num_splits, p)) return PA_ERR_SHAPE;
     if (s.num_tokens == 0) return PA_OK;
+    if (validate_only) return workspace_bytes < p.total ? PA_ERR_WORKSPACE : PA_OK;
     if (!workspace) return PA_ERR_NULL;
     if (workspace_bytes < p.total || ((uintptr_t)workspace % kAlign) != 0)
         return PA_ERR_WORKSPACE;
@@ -519,6 +521,61 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
     hipStream_t strm = (hipStream_t)stream;
     if ((st = launch_plan(call.pl, strm)) != PA_OK) return st;
     return run_attention(call, call.pl.tpi_pre, strm);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Scratch of pa_paged_attention_noalloc: one static array per device, never allocated by a
+// call. Host code must not pass `scratch` itself to a kernel (in host code the name is only a
+// stand-in for the device variable): each device's address comes from hipGetSymbolAddress,
+// looked up once per device with that device current, and is kept in g_scratch_ptr.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, or nullptr when the lookup fails.
+void *scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+}  // namespace
+
+extern "C" {
+
+pa_status pa_paged_attention_noalloc(const pa_paged_shape *shape, const void *query,
+                                     const void *key_cache, const void *value_cache,
+                                     const int32_t *cumulative_sequence_length,
+                                     const int32_t *past_seqlens, const int32_t *block_table,
+                                     float scale, int32_t causal, int32_t num_splits,
+                                     void *output, void *stream) {
+    if (!shape) return PA_ERR_NULL;
+    // every argument, and the shape's scratch size against the array's, is checked before the
+    // address lookup (the one HIP call besides the launches)
+    AttnCall call;
+    const int64_t H = shape->num_heads, G = shape->kv_num_heads, D = shape->head_size;
+    const pa_status st = make_attention(
+        shape, query, shape->packed_qkv ? (H + 2 * G) * D : H * D, key_cache, value_cache,
+        cumulative_sequence_length, past_seqlens, block_table, scale, causal, num_splits,
+        nullptr, PA_NOALLOC_SCRATCH_BYTES, output, call, /*validate_only=*/true);
+    if (st != PA_OK || shape->num_tokens == 0) return st;
+    void *ws = scratch_address();
+    if (!ws) return PA_ERR_HIP;
+    return pa_paged_attention(shape, query, key_cache, value_cache, cumulative_sequence_length,
+                              past_seqlens, block_table, scale, causal, num_splits, ws,
+                              PA_NOALLOC_SCRATCH_BYTES, output, stream);
 }
 
 pa_status pa_append_attention(const pa_paged_shape *shape, const void *query, const void *key,

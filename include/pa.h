@@ -4,6 +4,7 @@
  * A C ABI over device pointers. These operations make up the path:
  *   pa_kv_append        fused rotary + scatter of new K/V rows into cache slots
  *   pa_paged_attention  paged attention (decode and chunked prefill), split-KV when useful
+ *   pa_paged_attention_noalloc  the same with the library's static scratch (no workspace)
  *   pa_split_combine    log-sum-exp merge of (o, m, l) partials
  *   pa_sparse_forward   fp32 block-sparse "edge" forward emitting (o, m, l) partials
  *   pa_kv_append_rotate_query  the append plus the same rotation of the new query rows
@@ -22,8 +23,10 @@
  *              its Params struct, bindings and partial layout.
  *
  * Conventions that hold for every entry point:
- *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library never allocates,
- *     frees or keeps device memory between calls; scratch space comes in as `workspace`.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library never allocates
+ *     or frees device memory; scratch space comes in as `workspace`. The one exception is
+ *     pa_paged_attention_noalloc, whose scratch is a static array that the library's code object
+ *     holds on each device it runs on until the process ends.
  *   - Calls are asynchronous: they validate, enqueue kernels on `stream` (a hipStream_t; NULL is
  *     the null stream) and return. Results are ready when the stream reaches them.
  *   - Host-visible scalars and null pointers are checked before anything is enqueued; a failed
@@ -32,8 +35,9 @@
  *     edge_meta, block_tables) are the caller's contract and are not checked; the paged ones
  *     can be checked on the device beforehand with pa_check_paged_indices.
  *   - fp16 is IEEE binary16 (`_Float16` / `__half`); element offsets may exceed 2^31.
- *   - The library holds no mutable state except a per-device cache of the compute-unit count and
- *     the optional timing records (pa_timing_*). Calls may come from several host threads.
+ *   - The library holds no mutable host state except per-device caches (the compute-unit count,
+ *     the address of pa_paged_attention_noalloc's scratch) and the optional timing records
+ *     (pa_timing_*). Calls may come from several host threads.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -190,6 +194,32 @@ pa_status pa_paged_attention(const pa_paged_shape *shape, const void *query,
                              const int32_t *past_seqlens, const int32_t *block_table, float scale,
                              int32_t causal, int32_t num_splits, void *workspace,
                              size_t workspace_bytes, void *output, void *stream);
+
+/*
+ * pa_paged_attention_noalloc - pa_paged_attention without a caller workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.
+ *
+ * Same arguments, kernels and results (bit for bit) as pa_paged_attention with that call's
+ * workspace replaced by a static device array of PA_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each device. The first call on a device looks the array's address up (with that
+ * device current); no call allocates, frees or clears memory. Every kernel input in the array
+ * is written by the call itself (the planner zeroes its counters), so the previous call's
+ * contents never matter.
+ * Calls that overlap on one device (two streams, or two host threads, with no ordering between
+ * them) share the array and race: order them on one stream, or use pa_paged_attention with
+ * separate workspaces.
+ * Errors: those of pa_paged_attention; PA_ERR_WORKSPACE when
+ * pa_paged_attention_workspace_size(shape, num_splits) exceeds PA_NOALLOC_SCRATCH_BYTES
+ * (checked before any HIP call); PA_ERR_HIP when the address lookup fails.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status pa_paged_attention_noalloc(const pa_paged_shape *shape, const void *query,
+                                     const void *key_cache, const void *value_cache,
+                                     const int32_t *cumulative_sequence_length,
+                                     const int32_t *past_seqlens, const int32_t *block_table,
+                                     float scale, int32_t causal, int32_t num_splits,
+                                     void *output, void *stream);
 
 /*
  * pa_append_attention - the whole op of [manifest]: pass "scatter" and then the attention

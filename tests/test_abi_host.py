@@ -154,6 +154,28 @@ def test_append_attention_checks_both_parts_before_enqueueing():
     assert _append_attn(_shape(num_tokens=0), workspace=None) == pa.PA_OK
 
 
+def test_noalloc_rejects_before_any_hip_call():
+    """pa_paged_attention_noalloc checks its shape against the static array's size before it
+    makes any HIP call: a split count whose partials need more than PA_NOALLOC_SCRATCH_BYTES is
+    PA_ERR_WORKSPACE, and the other argument errors are those of pa_paged_attention."""
+    def na(shape, **kw):
+        a = dict(query=FAKE, key_cache=FAKE, value_cache=FAKE, cumulative_sequence_length=FAKE,
+                 past_seqlens=FAKE, block_table=FAKE, scale=0.0, causal=1,
+                 num_splits=pa.PA_SPLITS_AUTO, output=FAKE, stream=0, check=False)
+        a.update(kw)
+        return pa.pa_paged_attention_noalloc(shape, **a)
+    big = _shape(batch=64, num_tokens=4096, num_heads=32, kv_num_heads=8, head_size=128,
+                 num_blocks=100000, block_size=16, max_blocks=4096)
+    assert pa.pa_paged_attention_workspace_size(big, 16) > pa.PA_NOALLOC_SCRATCH_BYTES
+    assert na(big, num_splits=16) == pa.PA_ERR_WORKSPACE
+    assert na(_shape(), causal=2) == pa.PA_ERR_SHAPE
+    assert na(_shape(), num_splits=-2) == pa.PA_ERR_SHAPE
+    assert na(_shape(head_size=96)) == pa.PA_ERR_UNSUPPORTED
+    assert na(_shape(), block_table=None) == pa.PA_ERR_NULL
+    assert na(_shape(), output=None) == pa.PA_ERR_NULL
+    assert na(_shape(num_tokens=0)) == pa.PA_OK
+
+
 def test_workspace_size_is_zero_for_invalid_shapes():
     assert pa.pa_paged_attention_workspace_size(_shape(batch=0)) == 0
     assert pa.pa_paged_attention_workspace_size(_shape(), -3) == 0
