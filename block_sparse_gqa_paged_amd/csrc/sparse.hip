@@ -11,12 +11,15 @@
 //    a histogram whose atomic returns each edge's rank, a scan, and a plain scatter into a
 //    workspace permutation. One workgroup then stages a key block in LDS once and reuses it for
 //    up to kChunk edges; results per edge do not depend on the grouping or the order.
-//  * fp32 products run as three fp16 MFMAs (v_mfma_f32_16x16x32_f16) on split operands:
-//    x = hi + lo with hi = fp16(x), lo = fp16(x - hi), and a.b ~ hi.hi + hi.lo + lo.hi with fp32
-//    accumulation; the dropped lo.lo term is ~2^-22 of the product. Before the split, K and V
-//    of the block and each query row are scaled by a power of two that brings their largest
-//    magnitude into [0.5, 1), which is exact and keeps every value inside fp16 range; the scale
-//    is folded back into the scores and the output.
+//  * fp32 products run as three fp16 MFMAs (v_mfma_f32_16x16x32_f16) on split operands. Before
+//    the split, each query row, the block's K and each dimension of the block's V are scaled by
+//    a power of two that brings their largest magnitude into [0.5, 1) (exact; folded back into
+//    the scores and, per dimension, into the output). Q and K: x = hi + 2^-11 lo with
+//    hi = fp16(x), lo = fp16((x - hi) * 2^11), so lo stays a normal fp16 number for every x down
+//    to 2^-14 of the scaled maximum and each operand keeps 22 significant bits over that range;
+//    q.k ~ hi.hi + 2^-11 (hi.lo + lo.hi), the two sums in separate fp32 accumulators. V and P:
+//    x = hi + lo with lo = fp16(x - hi) (V per dimension and P <= 1 need no wider range), and
+//    p.v ~ hi.hi + hi.lo + lo.hi. The dropped lo.lo terms are ~2^-22 of each product.
 //  * S^T = K . Q^T has 16 keys as rows and 16 query rows as columns; its accumulator gives each
 //    lane 8 keys of one row across two key tiles, exactly the k-slots of the P operand of
 //    O^T = V^T . P^T, so P never leaves registers, and O^T gives each lane four consecutive
@@ -162,6 +165,14 @@ __device__ __forceinline__ HiLo split16(float x) {
     const half_t hi = (half_t)x;
     return HiLo{hi, (half_t)(x - (float)hi)};
 }
+// The same with the remainder stored times 2^11: x ~ hi + 2^-11 lo, lo normal in fp16 for every
+// |x| >= 2^-14 (the remainder of such an x is >= 2^-25), so small elements of a row or block
+// keep their precision instead of falling into fp16 subnormals.
+constexpr float kLoScale = 2048.f, kLoUnscale = 1.f / 2048.f;
+__device__ __forceinline__ HiLo split16r(float x) {
+    const half_t hi = (half_t)x;
+    return HiLo{hi, (half_t)((x - (float)hi) * kLoScale)};
+}
 
 // Power-of-two factor that brings max |x| = mx into [0.5, 1) (1 for mx == 0).
 __device__ __forceinline__ int pow2_exp(float mx) {
@@ -175,7 +186,8 @@ __device__ __forceinline__ int pow2_exp(float mx) {
 __device__ __forceinline__ int swz(int r, int q, int nq) { return q ^ (r & (min(nq, 16) - 1)); }
 
 // One query row per D/8 lanes: the row times the power of two that brings its largest magnitude
-// into [0.5, 1), split into the fp16 hi/lo planes, and scale_log2 * 2^eQ for its scores.
+// into [0.5, 1), split into the fp16 hi / scaled-lo planes, and scale_log2 * 2^eQ for its
+// scores.
 template <int D>
 __global__ __launch_bounds__(256) void sp_qsplit(SparseArgs a, SparseWs w, long long rows) {
     constexpr int LPR = D / 8;  // lanes per row (divides 64, so a row stays inside one wave)
@@ -192,7 +204,7 @@ __global__ __launch_bounds__(256) void sp_qsplit(SparseArgs a, SparseWs w, long 
     const int e = pow2_exp(mx);
     half8_t hi, lo;
     for (int i = 0; i < 4; ++i) {
-        const HiLo u = split16(ldexpf(x0[i], -e)), v = split16(ldexpf(x1[i], -e));
+        const HiLo u = split16r(ldexpf(x0[i], -e)), v = split16r(ldexpf(x1[i], -e));
         hi[i] = u.hi; lo[i] = u.lo;
         hi[4 + i] = v.hi; lo[4 + i] = v.lo;
     }
@@ -216,9 +228,15 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
     extern __shared__ half_t lds[];
     half_t *Khi = lds, *Klo = lds + BSP * D;
     half_t *Vhi = lds + 2 * BSP * D, *Vlo = lds + 3 * BSP * D;
-    // per wave: 8 rows x 128 bytes of partial output on their way to a whole-line store
-    float *slab = (float *)(lds + 4 * BSP * D) + (threadIdx.x >> 6) * 256;
-    __shared__ float s_max[2][NW];                      // per-wave maxima of |K| and |V|
+    // per wave: 8 rows x 128 bytes of partial output on their way to a whole-line store; while
+    // the block is staged, the same 8 KB hold the per-wave, per-dimension maxima of |V|
+    float *slabs = (float *)(lds + 4 * BSP * D);
+    float *slab = slabs + (threadIdx.x >> 6) * 256;
+    static_assert(NW * D <= NW * 256, "per-wave |V| maxima fit the store slabs");
+    __shared__ float s_kmax[NW];                        // per-wave maxima of |K|
+    __shared__ int s_ev[D];                             // per-dimension exponent of V
+    // 2^s_ev: output scale per dimension, read as float4 (16-byte aligned)
+    __shared__ __attribute__((aligned(16))) float s_vmul[D];
     __shared__ int s_e[kChunk], s_q[kChunk], s_len[kChunk];  // the item's edges
 
     const int item = blockIdx.x;
@@ -259,63 +277,67 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
     // floats): dims 4q .. 4q+3 and D/2 + 4q .. +3, so that the 16-byte loads of the D/8 lanes of
     // a key quad read whole contiguous half rows (a load instruction of 16-byte pieces at a
     // 32-byte stride reads HBM more slowly), non-temporal. Pass 1 loads and takes the block-wide
-    // max |K| and
-    // |V|; pass 2 scales by the powers of two, splits into fp16 hi/lo and stores K row-major and
-    // V transposed. With one task per thread the pass-1 registers are reused; otherwise pass 2
-    // reloads (from L2).
+    // max |K| and the per-dimension max |V|; pass 2 scales by the powers of two, splits into
+    // fp16 planes and stores K row-major and V transposed. One task per thread: the pass-1
+    // registers are reused.
     constexpr int TASKS = BSP / 4 * KQ;                       // (key quad, 8-dim chunk) pairs
-    constexpr int TPT = (TASKS + kThreads - 1) / kThreads;    // tasks per thread
+    static_assert(TASKS <= kThreads && TASKS % 64 == 0, "one task per thread, whole waves");
     float kr[4][8], vr[4][8];
-    auto load_task = [&](int task) {
-        const int t4 = task / KQ, q = task - t4 * KQ;
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * t4 + r;
-            const int pid = page_of(t);
-            for (int x = 0; x < 8; ++x) { kr[r][x] = 0.f; vr[r][x] = 0.f; }
-            if (pid >= 0) {
-                const float *pk = row_ptr(a.kp, pid, t) + 4 * q;
-                const float *pv = row_ptr(a.vp, pid, t) + 4 * q;
-                const float4_t k0 = gload_nt<float4_t>(pk), k1 = gload_nt<float4_t>(pk + D / 2);
-                const float4_t v0 = gload_nt<float4_t>(pv), v1 = gload_nt<float4_t>(pv + D / 2);
-                for (int x = 0; x < 4; ++x) {
-                    kr[r][x] = k0[x]; kr[r][4 + x] = k1[x];
-                    vr[r][x] = v0[x]; vr[r][4 + x] = v1[x];
-                }
+    const int task = threadIdx.x;
+    const bool has_task = task < TASKS;
+    const int t4 = task / KQ, q = task - t4 * KQ;
+    for (int r = 0; r < 4; ++r) {
+        const int t = 4 * t4 + r;
+        const int pid = has_task ? page_of(t) : -1;
+        for (int x = 0; x < 8; ++x) { kr[r][x] = 0.f; vr[r][x] = 0.f; }
+        if (pid >= 0) {
+            const float *pk = row_ptr(a.kp, pid, t) + 4 * q;
+            const float *pv = row_ptr(a.vp, pid, t) + 4 * q;
+            const float4_t k0 = gload_nt<float4_t>(pk), k1 = gload_nt<float4_t>(pk + D / 2);
+            const float4_t v0 = gload_nt<float4_t>(pv), v1 = gload_nt<float4_t>(pv + D / 2);
+            for (int x = 0; x < 4; ++x) {
+                kr[r][x] = k0[x]; kr[r][4 + x] = k1[x];
+                vr[r][x] = v0[x]; vr[r][4 + x] = v1[x];
             }
         }
-    };
-    float mk = 0.f, mv = 0.f;
-    for (int k = 0; k < TPT; ++k) {
-        const int task = threadIdx.x + k * kThreads;
-        if (task >= TASKS) break;
-        load_task(task);
-        for (int r = 0; r < 4; ++r)
-            for (int x = 0; x < 8; ++x) {
-                mk = fmaxf(mk, fabsf(kr[r][x]));
-                mv = fmaxf(mv, fabsf(vr[r][x]));
-            }
     }
-    for (int o = 32; o > 0; o >>= 1) {
-        mk = fmaxf(mk, __shfl_xor(mk, o, 64));
-        mv = fmaxf(mv, __shfl_xor(mv, o, 64));
+    float mk = 0.f, mv[8];
+    for (int x = 0; x < 8; ++x) {
+        mv[x] = 0.f;
+        for (int r = 0; r < 4; ++r) {
+            mk = fmaxf(mk, fabsf(kr[r][x]));
+            mv[x] = fmaxf(mv[x], fabsf(vr[r][x]));
+        }
     }
-    if (lane == 0) { s_max[0][wave] = mk; s_max[1][wave] = mv; }
+    for (int o = 32; o > 0; o >>= 1) mk = fmaxf(mk, __shfl_xor(mk, o, 64));
+    // lanes l, l + KQ, ... hold the same dims (q = lane mod KQ): reduce over them
+    for (int o = KQ; o < 64; o <<= 1)
+        for (int x = 0; x < 8; ++x) mv[x] = fmaxf(mv[x], __shfl_xor(mv[x], o, 64));
+    if (lane == 0) s_kmax[wave] = mk;
+    if (lane < KQ) {
+        float *vw = slabs + wave * D;
+        for (int x = 0; x < 4; ++x) {
+            vw[4 * q + x] = mv[x];
+            vw[D / 2 + 4 * q + x] = mv[4 + x];
+        }
+    }
     __syncthreads();
-    for (int i = 0; i < NW; ++i) {
-        mk = fmaxf(mk, s_max[0][i]);
-        mv = fmaxf(mv, s_max[1][i]);
+    for (int i = 0; i < NW; ++i) mk = fmaxf(mk, s_kmax[i]);
+    const int eK = pow2_exp(mk);
+    if ((int)threadIdx.x < D) {
+        float m = 0.f;
+        for (int i = 0; i < NW; ++i) m = fmaxf(m, slabs[i * D + threadIdx.x]);
+        const int e = pow2_exp(m);
+        s_ev[threadIdx.x] = e;
+        s_vmul[threadIdx.x] = ldexpf(1.f, e);
     }
-    const int eK = pow2_exp(mk), eV = pow2_exp(mv);
-    for (int k = 0; k < TPT; ++k) {
-        const int task = threadIdx.x + k * kThreads;
-        if (task >= TASKS) break;
-        if (TPT > 1) load_task(task);
-        const int t4 = task / KQ, q = task - t4 * KQ;
+    __syncthreads();
+    if (has_task) {
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * t4 + r;
             half8_t hi, lo;
             for (int x = 0; x < 8; ++x) {
-                const HiLo v = split16(ldexpf(kr[r][x], -eK));
+                const HiLo v = split16r(ldexpf(kr[r][x], -eK));
                 hi[x] = v.hi;
                 lo[x] = v.lo;
             }
@@ -332,9 +354,10 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
         const int vq = 4 * (t4 >> 3) + (t4 & 3), vh = 4 * ((t4 >> 2) & 1);
         for (int x = 0; x < 8; ++x) {
             const int d = x < 4 ? 4 * q + x : D / 2 + 4 * q + (x - 4);
+            const int ed = s_ev[d];
             half4_t hi, lo;
             for (int r = 0; r < 4; ++r) {
-                const HiLo v = split16(ldexpf(vr[r][x], -eV));
+                const HiLo v = split16(ldexpf(vr[r][x], -ed));
                 hi[r] = v.hi;
                 lo[r] = v.lo;
             }
@@ -402,19 +425,20 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
         float s[NT][4];
         float mx = -INFINITY;
         for (int j = 0; j < NT; ++j) {
-            float4_t acc = {0.f, 0.f, 0.f, 0.f};
+            // hi.hi in acc, the scaled cross terms hi.lo + lo.hi in acx
+            float4_t acc = {0.f, 0.f, 0.f, 0.f}, acx = {0.f, 0.f, 0.f, 0.f};
             const int t = 16 * j + n16;
             for (int kb = 0; kb < KB; ++kb) {
                 const int off = t * D + 8 * swz(t, 4 * kb + g16, KQ);
                 const half8_t khi = *(const half8_t *)(Khi + off);
                 const half8_t klo = *(const half8_t *)(Klo + off);
-                acc = mfma16x16x32(khi, qlo[kb], acc);
-                acc = mfma16x16x32(klo, qhi[kb], acc);
+                acx = mfma16x16x32(khi, qlo[kb], acx);
+                acx = mfma16x16x32(klo, qhi[kb], acx);
                 acc = mfma16x16x32(khi, qhi[kb], acc);
             }
             for (int i = 0; i < 4; ++i) {
                 const bool ok = (lm[j >> 2] >> (16 * (j & 3) + i)) & 1;
-                s[j][i] = ok ? acc[i] * mult : -INFINITY;
+                s[j][i] = ok ? __builtin_fmaf(acx[i], kLoUnscale, acc[i]) * mult : -INFINITY;
                 mx = fmaxf(mx, s[j][i]);
             }
             // keep the next tile's LDS operand reads from being hoisted over this tile (each
@@ -454,7 +478,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
                 if (dt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // Stores, o scaled back by 2^eV. Lane (g16, n16) holds dims 16dt + 4g16 .. +3 of row
+        // Stores, o scaled back by 2^eV of each dim. Lane (g16, n16) holds dims 16dt + 4g16 .. +3 of row
         // n16, so a direct store instruction would write 64 bytes into each of 16 rows; at this
         // occupancy that writes HBM about 20% slower than whole 128-byte lines. Each 128-byte
         // line j of 8 rows goes through the wave's 1 KB LDS slab instead and leaves as one
@@ -475,11 +499,9 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
             for (int j = 0; j < NDT / 2; ++j) {
                 if ((n16 >> 3) == h) {
                     float *rowp = slab + (n16 & 7) * 32;
-                    float4_t v0, v1;
-                    for (int i = 0; i < 4; ++i) {
-                        v0[i] = ldexpf(o[2 * j][i], eV);
-                        v1[i] = ldexpf(o[2 * j + 1][i], eV);
-                    }
+                    const float4_t m0 = *(const float4_t *)(s_vmul + 32 * j + 4 * g16);
+                    const float4_t m1 = *(const float4_t *)(s_vmul + 32 * j + 16 + 4 * g16);
+                    const float4_t v0 = o[2 * j] * m0, v1 = o[2 * j + 1] * m1;
                     *(float4_t *)(rowp + 4 * g16) = v0;
                     *(float4_t *)(rowp + 16 + 4 * g16) = v1;
                 }
@@ -510,8 +532,9 @@ pa_status launch_sparse(const SparseArgs &a, hipStream_t stream) {
     while (16 * nt < a.block_size) nt *= 2;
     // the K and V hi/lo planes, then one 1 KB store slab per wave
     const size_t lds = (size_t)4 * 16 * nt * a.D * sizeof(half_t) + (kThreads / 64) * 1024;
-    // dynamic LDS plus the kernel's static arrays (edge list, per-wave maxima)
-    if (lds + 2048 > sparse_lds_limit() || (a.D != 64 && a.D != 128)) return PA_ERR_UNSUPPORTED;
+    // dynamic LDS plus the kernel's static arrays (edge list, maxima, per-dimension V scales:
+    // 2.6 KB at D = 128)
+    if (lds + 4096 > sparse_lds_limit() || (a.D != 64 && a.D != 128)) return PA_ERR_UNSUPPORTED;
     const long long qrows = (long long)a.tq * a.hkv * a.qhead;
     LaunchScope scope("sparse_forward", stream, qrows > 0 ? 6 : 5);
     SparseWs w;

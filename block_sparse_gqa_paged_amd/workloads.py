@@ -61,7 +61,7 @@ def paged_workload(seed, *, past, n_new, num_heads, kv_num_heads, head_size, blo
                    table="pool", slack=0.10, max_blocks=None, packed=False,
                    rotary_mode=ROTARY_NONE, rotary_dim=0, rotary_positions=None,
                    theta=10000.0, key_scale=1.0, use_slot_mapping=False, causal=1,
-                   scale=None, poison=False, name="paged"):
+                   scale=None, poison=False, key_step=None, name="paged"):
     """Generic paged workload.
 
     ``past`` and ``n_new`` are either integer sequences (used as given) or callables
@@ -76,6 +76,10 @@ def paged_workload(seed, *, past, n_new, num_heads, kv_num_heads, head_size, blo
                       ceil(L_b / bs) ids of permutation(NB), in batch order; unused entries are -1.
     poison=True writes fp16 NaN into every cache row a sequence does not own below L_b
     (rows at positions >= L_b of owned blocks, and every block no sequence owns).
+    key_step: a list of (position, factor) pairs; every key of a sequence at absolute position
+    >= position (cache rows below past, new rows above it) is multiplied by factor (float32,
+    then fp16), the pairs compounding. It draws nothing: scores that jump by a known amount
+    partway through a sequence.
     """
     rng = np.random.default_rng(seed)
     past = np.asarray(past(rng) if callable(past) else past, dtype=np.int64)
@@ -121,6 +125,27 @@ def paged_workload(seed, *, past, n_new, num_heads, kv_num_heads, head_size, blo
         query = _fill_normal(rng, (T, H * D), np.float16)
         key = _fill_normal(rng, (T, G * D), np.float16, key_scale)
         value = _fill_normal(rng, (T, G * D), np.float16)
+
+    if key_step:
+        for b in range(B):
+            f = np.ones(int(L[b]), dtype=np.float32)
+            for pos0, fac in key_step:
+                f[int(pos0):] *= np.float32(fac)
+            for j in range(int(L[b])):
+                if f[j] == 1.0:
+                    continue
+                if j < past[b]:
+                    blk, off = int(block_table[b, j // bs]), j % bs
+                    key_cache[blk, off] = (key_cache[blk, off].astype(np.float32)
+                                           * f[j]).astype(np.float16)
+                else:
+                    i = int(cu[b]) + j - int(past[b])
+                    if packed:
+                        ks = query[i, H * D:(H + G) * D]
+                        query[i, H * D:(H + G) * D] = (ks.astype(np.float32) * f[j]).astype(
+                            np.float16)
+                    else:
+                        key[i] = (key[i].astype(np.float32) * f[j]).astype(np.float16)
 
     slot_mapping = None
     if use_slot_mapping:
@@ -267,7 +292,8 @@ def bnsh_append(seed=6):
 
 def sparse_workload(seed, *, Tq, hkv, qhead, head_dim, block_size, page_size, batch,
                     key_capacity, window=4, p_random=0.05, unmapped_frac=0.10,
-                    all_blocks=False, softmax_scale=None, name="sparse"):
+                    all_blocks=False, softmax_scale=None, outliers=None, tiny=None,
+                    name="sparse"):
     """Block-sparse edge workload, fp32.
 
     Draw order: used_kv_lens = key_capacity - U{1..63} (clamped to >= 1) per batch; the page
@@ -284,6 +310,14 @@ def sparse_workload(seed, *, Tq, hkv, qhead, head_dim, block_size, page_size, ba
     right-aligned key position (the causal limit when the mask is applied). block_mask
     [Tq, hkv, nblk] (uint8) and q_batch [Tq] are the kept-block mask and each row's batch, the
     inputs an edge-list builder turns into edge_meta and group_ptr.
+
+    Wide-range options, drawn after everything above (the other draws do not change):
+      outliers = (n, k_factor, v_factor): n channels (drawn without replacement) of every key
+        row are multiplied by k_factor and of every value row by v_factor; the same query
+        channels are divided by k_factor, so those channels' score terms keep unit scale while
+        each key row spans the factor's range.
+      tiny = (frac, factor): each (page, head, row) key/value row with probability frac, then
+        each (query row, head) with probability frac, is multiplied by factor.
     """
     rng = np.random.default_rng(seed)
     ppb = block_size // page_size
@@ -317,6 +351,19 @@ def sparse_workload(seed, *, Tq, hkv, qhead, head_dim, block_size, page_size, ba
             k[:, :nused[b]] = rnd[q, :, :nused[b]]
             k[:, max(0, qb - window + 1):qb + 1] = True
             k[:, 0] = True
+    if outliers:
+        n_ch, kf, vf = outliers
+        ch = rng.choice(head_dim, size=int(n_ch), replace=False)
+        k_pages[..., ch] *= np.float32(kf)
+        v_pages[..., ch] *= np.float32(vf)
+        q_buf[..., ch] /= np.float32(kf)
+    if tiny:
+        frac, fac = tiny
+        rows = rng.random(size=k_pages.shape[:3]) < frac
+        k_pages[rows] *= np.float32(fac)
+        v_pages[rows] *= np.float32(fac)
+        qrows = rng.random(size=q_buf.shape[:2]) < frac
+        q_buf[qrows] *= np.float32(fac)
     q_pos = (used[np.arange(Tq) // qpb] - qpb + np.arange(Tq) % qpb).astype(np.int32)
     qi, hi, bi = np.nonzero(keep)          # row-major: already sorted by (q, h, blk)
     bb = qi // qpb

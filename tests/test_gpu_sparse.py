@@ -1,7 +1,7 @@
 """GPU parity of the block-sparse edge forward (pa_sparse_forward) and its merge against the CPU
-oracle: tiny edge lists compared partial by partial, and the full-size workload (Tq 4096, hkv 8,
-qhead 4, D 128, block 64, page 16) compared on every partial of a seeded sample of (q, h)
-groups and on their merged rows.
+oracle: tiny edge lists compared partial by partial, inputs with a wide dynamic range (outlier
+channels, rows near 1e-5), and the full-size workload (Tq 4096, hkv 8, qhead 4, D 128, block 64,
+page 16) compared on every merged row and on every partial of a seeded 1% edge sample.
 """
 import numpy as np
 import pytest
@@ -12,7 +12,8 @@ import block_sparse_gqa_paged_amd as pa  # noqa: E402
 import oracle  # noqa: E402
 from block_sparse_gqa_paged_amd import device as dev  # noqa: E402
 from block_sparse_gqa_paged_amd import workloads as W  # noqa: E402
-from parity import assert_sparse_out_close, assert_sparse_partials_close  # noqa: E402
+from parity import (assert_sparse_out_close, assert_sparse_partials_close,  # noqa: E402
+                    oracle_sparse_full)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +71,58 @@ def test_tiny_causal_partials_and_merge(case):
     assert_sparse_out_close(out, merged, "causal merged")
 
 
+# Wide dynamic range inside key blocks, value dimensions and query rows: outlier channels (keys
+# and values x100 / x1000, the matching query channels scaled down so scores stay O(1)) and rows
+# near 1e-5, at the 1e-4 bar. In an outlier value channel the weighted sum of terms of size ~1000
+# can cancel to a small value; its fp32 rounding is relative to the terms (the page's own loops
+# run in plain fp32 miss 1e-4 * max(1, |o|) by up to 6x there, and stay near 1e-6 of the terms),
+# so o and the merged rows are held to 1e-4 of the magnitude of their terms.
+WIDE = [
+    dict(seed=220, outliers=(3, 1000.0, 1000.0)),
+    dict(seed=221, outliers=(3, 100.0, 100.0), tiny=(0.1, 1e-5)),
+    dict(seed=222, tiny=(0.25, 1e-5)),
+    dict(seed=223, head_dim=64, block_size=32, page_size=8, qhead=2,
+         outliers=(2, 1000.0, 100.0), tiny=(0.1, 1e-5)),
+    dict(seed=224, qhead=8, block_size=128, page_size=32, outliers=(4, 300.0, 1000.0),
+         tiny=(0.05, 1e-5), key_capacity=1024),
+]
+
+
+def _assert_wide(sw):
+    """The inputs really span the range: within key rows (outliers) and between rows (tiny)."""
+    k = np.abs(sw["k_pages"]).reshape(-1, sw["D"])
+    v = np.abs(sw["v_pages"]).reshape(-1, sw["D"])
+    spread = [np.median(x.max(axis=1) / np.maximum(np.median(x, axis=1), 1e-30)) for x in (k, v)]
+    tiny = [(x.max(axis=1) < 1e-3 * np.median(x.max(axis=1))).mean() for x in (k, v)]
+    return spread, tiny
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: str(c["seed"]))
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_wide_dynamic_range(case, causal):
+    case = dict(case)
+    sw = _tiny(case.pop("seed"), **case)
+    spread, tiny = _assert_wide(sw)
+    if "outliers" in case:
+        assert min(spread) > 50, spread        # each row's max far above its typical element
+    if "tiny" in case:
+        assert min(tiny) > 0.02, tiny          # rows near 1e-5 inside the blocks
+    q_pos = sw["q_pos"] if causal else None
+    ref = oracle.sparse_forward(sw, q_pos=q_pos)
+    # the magnitude of the summed terms: the same partials over |V| (the weights do not change)
+    o_terms = oracle.sparse_forward(dict(sw, v_pages=np.abs(sw["v_pages"])), q_pos=q_pos)[0]
+    c = dev.SparseCase(sw)
+    got = c.forward(causal=causal)
+    out = c.combine()
+    torch.cuda.synchronize()
+    assert_sparse_partials_close(got, ref, "wide partials", o_terms=o_terms)
+    kw = dict(lanes=sw["qhead"], head_dim=sw["D"], group_ptr=sw["group_ptr"],
+              out_dtype=np.float32)
+    merged = oracle.split_combine(*ref, **kw)
+    terms = oracle.split_combine(o_terms, ref[1], ref[2], **kw)
+    assert_sparse_out_close(out, merged, "wide merged", terms=terms)
+
+
 def test_sentinels_and_out_of_range_edges():
     sw = _tiny(210)
     em = sw["edge_meta"].copy()
@@ -114,28 +167,22 @@ def full():
     return sw, o.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy(), out.cpu().numpy()
 
 
-def _check_sampled_groups(sw, o, m, l, out, q_pos=None):
-    G = sw["Tq"] * sw["hkv"]
-    groups = np.random.default_rng(7).choice(G, size=96, replace=False)
-    groups.sort()
-    gp = sw["group_ptr"]
-    edges = np.concatenate([np.arange(gp[g], gp[g + 1]) for g in groups])
-    sub_gp = np.concatenate([[0], np.cumsum(gp[groups + 1] - gp[groups])]).astype(np.int32)
-    ro, rm, rl = oracle.sparse_forward(sw, edge_meta=sw["edge_meta"][edges], q_pos=q_pos)
+def _check_full(sw, o, m, l, out, q_pos=None):
+    """Every merged row against the oracle's, and every partial of a seeded 1% edge sample."""
+    rng = np.random.default_rng(7)
+    sample = np.sort(rng.choice(sw["E"], size=max(1, sw["E"] // 100), replace=False))
+    merged, (ro, rm, rl) = oracle_sparse_full(oracle, sw, q_pos=q_pos, sample_edges=sample)
     q = sw["qhead"]
-    prow = (edges[:, None] * q + np.arange(q)[None, :]).reshape(-1)
-    assert_sparse_partials_close((o[prow], m[prow], l[prow]), (ro, rm, rl), "sampled partials")
-    merged = oracle.split_combine(ro, rm, rl, lanes=q, head_dim=sw["D"], group_ptr=sub_gp,
-                                  out_dtype=np.float32)
-    orow = (groups[:, None] * q + np.arange(q)[None, :]).reshape(-1)
-    assert_sparse_out_close(out[orow], merged, "sampled merged rows")
+    prow = (sample[:, None] * q + np.arange(q)[None, :]).reshape(-1)
+    assert_sparse_partials_close((o[prow], m[prow], l[prow]), (ro, rm, rl), "1% edge sample")
+    assert_sparse_out_close(out, merged, "every merged row")
 
 
-def test_full_size_sampled_groups(full):
-    _check_sampled_groups(*full)
+def test_full_size_every_merged_row(full):
+    _check_full(*full)
 
 
-def test_full_size_causal_sampled_groups(full):
+def test_full_size_causal_every_merged_row(full):
     """The same workload under the right-aligned causal mask (its random blocks past a row's
     position become sentinels, the row's own block is cut at the position)."""
     sw = full[0]
@@ -143,8 +190,8 @@ def test_full_size_causal_sampled_groups(full):
     o, m, l = c.forward(causal=True)
     out = c.combine()
     torch.cuda.synchronize()
-    _check_sampled_groups(sw, o.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy(),
-                          out.cpu().numpy(), q_pos=sw["q_pos"])
+    _check_full(sw, o.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy(), out.cpu().numpy(),
+                q_pos=sw["q_pos"])
 
 
 def test_full_size_invariants(full):
