@@ -1,7 +1,7 @@
 """GPU parity of the paged path (pa_kv_append, pa_paged_attention, pa_split_combine) against
 the CPU oracle, on seeded workloads: a tiny family that spans several 32-key tiles with ragged
-tails, the four paged workload shapes at full size (mixed prefill checked on sampled rows), NaN
-in stale cache rows, page permutation, and every split policy.
+tails, the four paged workload shapes at full size (every output row), NaN in stale cache rows,
+page permutation, every split policy, and prefill columns whose running maximum is raised.
 """
 import numpy as np
 import pytest
@@ -12,8 +12,9 @@ import block_sparse_gqa_paged_amd as pa  # noqa: E402
 import oracle  # noqa: E402
 from block_sparse_gqa_paged_amd import device as dev  # noqa: E402
 from block_sparse_gqa_paged_amd import workloads as W  # noqa: E402
-from parity import (assert_attention_close, assert_bits_equal, rows_as_decode,  # noqa: E402
+from parity import (assert_attention_close, assert_bits_equal, oracle_rows,  # noqa: E402
                     ROT_ABS)
+from lazy_softmax import RAISE_CASES, raise_columns  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -97,6 +98,21 @@ def test_prefill_family(case):
     c, out = _run(w)
     assert_bits_equal(c.key_cache, kc, "key_cache")
     assert_attention_close(out, ref, "prefill")
+
+
+# Prefill rows whose scores rise by more than 2^8 after the first 64-key tile: the kernel's
+# lazily raised maximum rescales O and l (the CPU suite shows the raise occurs in most of these
+# columns and that a wrong rescale would exceed the bar).
+@pytest.mark.parametrize("case", RAISE_CASES, ids=lambda c: str(c["seed"]))
+def test_prefill_max_raise(case):
+    case = dict(case)
+    w = W.paged_workload(case.pop("seed"), table="pool", slack=0.2, name="raise", **case)
+    kc, vc, ref = _oracle(w)
+    raised, total = raise_columns(w, kc)
+    assert raised > 0.5 * total, (raised, total)
+    c, out = _run(w)
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_attention_close(out, ref, "prefill with max raises")
 
 
 # Fused query rotation: the key/value append plus q_out, each bit-identical to the oracle.
@@ -468,14 +484,10 @@ def test_mixed_prefill_decode_full_size(mixed):
     kc, vc = oracle.kv_append(w)
     assert_bits_equal(c.key_cache, kc, "key_cache")
     assert_bits_equal(c.value_cache, vc, "value_cache")
-    # attention on sampled rows: every decode row, and rows of each prefill sequence
-    rng = np.random.default_rng(0)
-    pre = np.concatenate([w["cu"][b] + np.unique(np.r_[0, 1, 511, rng.integers(0, 512, 5)])
-                          for b in range(8)])
-    rows = np.concatenate([pre, np.arange(w["cu"][8], w["T"])])
-    sub = rows_as_decode(w, rows)
-    ref = oracle.paged_attention(sub, kc, vc)
-    assert_attention_close(out[rows], ref, "mixed sampled rows")
+    # attention on every row: the 4096 prefill rows and the 56 decode rows, each computed by the
+    # oracle as the equivalent one-token decode, on host threads
+    ref = oracle_rows(oracle, w, kc, vc)
+    assert_attention_close(out, ref, "mixed, every row")
 
 
 # ------------------------------------------------------------------ combine of oracle partials
