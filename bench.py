@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFS = 2500.0
-FP32_MFMA_PEAK_TFS = 157.3
+FLUSH_BYTES = 512 << 20  # written between launches of cache-sized workloads (> the 256 MB MALL)
 
 
 def parse():
@@ -137,6 +137,48 @@ def device_copy_gbps(torch, nbytes=1 << 30, reps=5):
 WARM_MS = 100.0  # untimed work before each secondary workload's timed loop
 
 
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cold_kernel_us(pa, torch, fn, kernel, n, flush):
+    """Mean duration (us) of the library launch `kernel` over n calls of fn, each preceded by a
+    512 MB write that evicts the caches (only the kernel's own hook-timed interval is counted)."""
+    pa.pa_timing_reset()
+    for _ in range(n):
+        flush.zero_()
+        pa.pa_timing_enable(True)
+        fn()
+        pa.pa_timing_enable(False)
+    torch.cuda.synchronize()
+    t = pa.pa_timing_get(kernel)
+    pa.pa_timing_reset()
+    return t[0] / max(1, t[1]) * 1e3
+
+
+def torch_kernel_us(torch, fn, n, flush=None):
+    """Mean duration (us) of fn (torch work on the current stream), from an event pair around
+    each call; with flush, a 512 MB write before each call (outside the timed pair)."""
+    tot = 0.0
+    for _ in range(n):
+        if flush is not None:
+            flush.zero_()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        tot += s.elapsed_time(e)
+    return tot / n * 1e3
+
+
 def oracle_all_cores(oracle, w, kc, vc, ref, kv, np):
     """The same oracle call on every host core: the batch is cut into contiguous groups of
     sequences, one per thread (the oracle runs in C, outside the interpreter lock), each group
@@ -168,7 +210,7 @@ def oracle_all_cores(oracle, w, kc, vc, ref, kv, np):
     assert np.array_equal(joined.view(np.uint16), ref.view(np.uint16)), "partitioned oracle differs"
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"the same rows, {cores} threads over contiguous sequence groups, "
-                      f"{dt:.2f} s"}
+                      f"{dt:.2f} s", "host": host_cpu_model()}
 
 
 def main():
@@ -206,6 +248,10 @@ def main():
     # the same steps without the library's event records, for the step time itself
     ms_plain, _ = timed(step, args.steps, args.warmup, torch)
     ms_two, _ = timed(step_two_calls, args.steps, args.warmup, torch)
+    # the manifest's own split rule (numSplits from MAX_SPLITS / SPLIT_MIN_KEYS /
+    # SPLIT_TARGET_WORKGROUPS: S = 2 here) through the same one-call step
+    ms_page, _ = timed(lambda: c.append_attention(pa.PA_SPLITS_PAGE_RULE), args.steps,
+                       args.warmup, torch)
     pct = step_percentiles(step, 100, 10, torch, np)
     copy_gbps = device_copy_gbps(torch)
     print(f"# step {ms_plain:.4f} ms (with event hooks {ms:.4f} ms; as two calls {ms_two:.4f} ms)",
@@ -227,7 +273,8 @@ def main():
         dt = time.perf_counter() - t0
         cpu = {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"all {w['T']} decode rows x {w['H']} heads of the workload, "
-                         f"attention only, {dt:.1f} s single-threaded"}
+                         f"attention only, {dt:.1f} s single-threaded",
+               "host": host_cpu_model()}
         cpu_all = oracle_all_cores(oracle, w, kc, vc, ref, kv, np)
 
     extra = {}
@@ -263,6 +310,9 @@ def main():
                    "num_splits": "auto", "parallelism": "none (1 GPU)"},
         "kernel_us": per_kernel,
         "two_calls_ms_per_step": round(ms_two, 4),
+        "page_rule_splits_ms_per_step": round(ms_page, 4),
+        "page_rule_splits_pct_of_hbm_peak": round(100.0 * kv / (ms_page * 1e-3) / 1e9
+                                                  / HBM_PEAK_GBS, 2),
         "step_ms_percentiles_100": pct,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -286,6 +336,10 @@ def run_extra(args, torch, np, pa, dev, W):
 
     def warm(fn):  # untimed, with the library's timing hooks off
         timed(fn, 1, wu, torch, WARM_MS)
+    # Workloads smaller than the 256 MB last-level cache are timed cold: a 512 MB write before
+    # each launch evicts their inputs (the write itself is not timed).
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    n_cold = max(5, steps)
     print("# generating the mixed prefill+decode workload", file=sys.stderr, flush=True)
     w = W.mixed_prefill_decode()
     c = dev.PagedCase(w)
@@ -320,21 +374,43 @@ def run_extra(args, torch, np, pa, dev, W):
         "append_pct_hbm": round(100 * app_bytes / (us.get("kv_append", 1e9) * 1e-6) / 1e9
                                 / HBM_PEAK_GBS, 2),
         "append_bytes": app_bytes,
+        "append_cache": "in the step: the previous step's 1.8 GB decode has evicted its inputs",
+    }
+    # What a 35 MB append can reach on this machine: the same append cold (flush before each
+    # launch), a plain device copy moving the same bytes (half read, half written) cold, and the
+    # append of 2 tokens (one workgroup: the launch and its dependent loads, no bandwidth).
+    us_cold = cold_kernel_us(pa, torch, c.append, "kv_append", n_cold, flush)
+    src = torch.empty(app_bytes // 2, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    us_copy = torch_kernel_us(torch, lambda: dst.copy_(src), n_cold, flush)
+    del src, dst
+    w2 = W.paged_workload(7, past=[100], n_new=[2], num_heads=32, kv_num_heads=8,
+                          head_size=128, block_size=32, packed=True, rotary_mode=W.ROTARY_NEOX,
+                          rotary_dim=128, rotary_positions=256, name="append_2_tokens")
+    c2 = dev.PagedCase(w2)
+    warm(c2.append)
+    us_min = cold_kernel_us(pa, torch, c2.append, "kv_append", n_cold, flush)
+    del c2
+    out["append_floor"] = {
+        "workload": w["name"], "append_bytes": app_bytes,
+        "append_cold_us": round(us_cold, 2),
+        "append_cold_pct_hbm": round(100 * app_bytes / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+        "device_copy_same_bytes_cold_us": round(us_copy, 2),
+        "device_copy_same_bytes_pct_hbm": round(100 * app_bytes / (us_copy * 1e-6) / 1e9
+                                                / HBM_PEAK_GBS, 2),
+        "append_2_tokens_us": round(us_min, 2),
+        "us_at_60pct_hbm": round(app_bytes / (0.6 * HBM_PEAK_GBS * 1e9) * 1e6, 2),
     }
     # the append with every new query row rotated into q_out in the same launch
     q_out = torch.empty((w["T"], w["H"] * w["D"]), dtype=torch.float16, device="cuda")
     warm(lambda: c.append_rotate_query(q_out))
-    pa.pa_timing_reset()
-    pa.pa_timing_enable(True)
-    timed(lambda: c.append_rotate_query(q_out), steps, 0, torch)
-    pa.pa_timing_enable(False)
-    t_rq = pa.pa_timing_get("kv_append")
-    pa.pa_timing_reset()
-    us_rq = t_rq[0] / max(1, t_rq[1]) * 1e3
+    us_rq = cold_kernel_us(pa, torch, lambda: c.append_rotate_query(q_out), "kv_append", n_cold,
+                           flush)
     rq_bytes = app_bytes + w["T"] * w["H"] * w["D"] * 2 * 2
     out["mixed_prefill_decode"].update({
         "append_rotate_query_us": round(us_rq, 2), "append_rotate_query_bytes": rq_bytes,
-        "append_rotate_query_GBps": round(rq_bytes / (us_rq * 1e-6) / 1e9, 1)})
+        "append_rotate_query_GBps": round(rq_bytes / (us_rq * 1e-6) / 1e9, 1),
+        "append_rotate_query_cache": "cold (512 MB written before each launch)"})
     del c, q_out
     torch.cuda.empty_cache()
 
@@ -364,19 +440,14 @@ def run_extra(args, torch, np, pa, dev, W):
     bw = W.bnsh_append()
     bc = dev.BnshCase(bw)
     warm(bc.append)
-    pa.pa_timing_reset()
-    pa.pa_timing_enable(True)
-    timed(bc.append, steps, 0, torch)
-    pa.pa_timing_enable(False)
-    t_b = pa.pa_timing_get("kv_append_bnsh")
-    pa.pa_timing_reset()
-    us_b = t_b[0] / max(1, t_b[1]) * 1e3
+    us_b = cold_kernel_us(pa, torch, bc.append, "kv_append_bnsh", n_cold, flush)
     rows = bw["B"] * bw["S"]
     b_bytes = rows * bw["KVH"] * bw["D"] * 2 * 4 + rows * (bw["rotary_dim"] // 2) * 2 * 2
     out["append_bnsh"] = {
         "workload": bw["name"], "append_bytes": b_bytes, "kernel_us": round(us_b, 2),
         "append_GBps": round(b_bytes / (us_b * 1e-6) / 1e9, 1),
         "pct_hbm": round(100 * b_bytes / (us_b * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+        "cache": "cold (512 MB written before each launch)",
     }
     del bc
     torch.cuda.empty_cache()
@@ -395,13 +466,7 @@ def run_extra(args, torch, np, pa, dev, W):
     # the edge list itself, built on the device from the kept-block mask
     eb = dev.EdgeBuilder(sw)
     warm(eb.build)
-    pa.pa_timing_reset()
-    pa.pa_timing_enable(True)
-    timed(eb.build, steps, 0, torch)
-    pa.pa_timing_enable(False)
-    t_e = pa.pa_timing_get("build_edges")
-    pa.pa_timing_reset()
-    us_edges = t_e[0] / max(1, t_e[1]) * 1e3
+    us_edges = cold_kernel_us(pa, torch, eb.build, "build_edges", n_cold, flush)
     edge_bytes = sw["block_mask"].size + sw["E"] * 20 + (sw["Tq"] * sw["hkv"] + 1) * 4
     del eb
     # the same edges under the right-aligned causal mask
@@ -427,19 +492,35 @@ def run_extra(args, torch, np, pa, dev, W):
         ok = (blen > t) & mapped[em[:, 3], em[:, 2] * ppb + t // sw["page_size"]]
         mk += int(ok.sum())
     flops = mk * q * D * 4
+    # the forward's own floor: writing its partials at the rate this device fills a buffer of
+    # the same size
+    wbuf = torch.empty(part_bytes, dtype=torch.uint8, device="cuda")
+    us_fill = torch_kernel_us(torch, lambda: wbuf.fill_(1), n_cold)
+    del wbuf
+    fwd_us = us.get("sparse_forward", 1e9)
     out["block_sparse"] = {
         "workload": sw["name"], "edges": E, "ms_per_step": round(ms, 4), "kernel_us": us,
         "combine_GBps": round(comb_bytes / (us.get("combine", 1e9) * 1e-6) / 1e9, 1),
         "combine_bytes": comb_bytes,
         "combine_pct_hbm": round(100 * comb_bytes / (us.get("combine", 1e9) * 1e-6) / 1e9
                                  / HBM_PEAK_GBS, 2),
-        "forward_TFLOPs": round(flops / (us.get("sparse_forward", 1e9) * 1e-6) / 1e12, 2),
-        "forward_frac_fp32_mfma": round(flops / (us.get("sparse_forward", 1e9) * 1e-6) / 1e12
-                                        / FP32_MFMA_PEAK_TFS, 4),
         "forward_flops": flops,
+        # it runs fp16 matrix instructions: three fp16 products per fp32 product
+        "forward_fp32_TFLOPs": round(flops / (fwd_us * 1e-6) / 1e12, 2),
+        "forward_frac_f16_mfma_algorithmic": round(flops / (fwd_us * 1e-6) / 1e12
+                                                   / MFMA_F16_PEAK_TFS, 4),
+        "forward_frac_f16_mfma_executed": round(3 * flops / (fwd_us * 1e-6) / 1e12
+                                                / MFMA_F16_PEAK_TFS, 4),
+        # its bound: the partial writes (E * qhead * (D + 2) * 4 bytes)
+        "partial_bytes": part_bytes,
+        "partial_write_floor_us": round(us_fill, 2),
+        "forward_vs_write_floor": round(us_fill / fwd_us, 4),
+        "partial_write_frac_hbm_peak": round(part_bytes / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                             4),
         "causal_forward_us": round(us_causal, 2),
         "build_edges_us": round(us_edges, 2), "build_edges_bytes": edge_bytes,
         "build_edges_GBps": round(edge_bytes / (us_edges * 1e-6) / 1e9, 1),
+        "build_edges_cache": "cold (512 MB written before each launch)",
     }
     return out
 

@@ -181,9 +181,15 @@ __device__ __forceinline__ int pow2_exp(float mx) {
     return mx > 0.f ? e : 0;
 }
 
-// XOR swizzle of chunk q in row r (nq chunks per row, a power of two): the 16 rows a 16-lane
-// group reads at one logical chunk land in distinct banks.
-__device__ __forceinline__ int swz(int r, int q, int nq) { return q ^ (r & (min(nq, 16) - 1)); }
+// XOR swizzle of 16-byte chunk q in row r of a plane with nq chunks per row (a power of two). A
+// 16-lane group reads 16 consecutive rows at one logical chunk, and one pass over the LDS banks
+// covers 256 bytes. Rows of 256 bytes or more: the chunk is XORed with r mod 16. Shorter rows
+// (nq < 16: 16 / nq rows share a 256-byte span, rows r and r + 16 / nq start on the same bank):
+// XORed with (r / (16 / nq)) mod nq, so the rows that share a bank offset take distinct chunks.
+__device__ __forceinline__ int swz(int r, int q, int nq) {
+    if (nq >= 16) return q ^ (r & 15);
+    return q ^ ((r / (16 / nq)) & (nq - 1));
+}
 
 // One query row per D/8 lanes: the row times the power of two that brings its largest magnitude
 // into [0.5, 1), split into the fp16 hi / scaled-lo planes, and scale_log2 * 2^eQ for its
@@ -497,15 +503,21 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
             const long long pr = (long long)s_e[rvalid ? ridx : 0] * a.qhead + r % a.qhead;
             float *dst = a.o + pr * D + 4 * (lane & 7);
             for (int j = 0; j < NDT / 2; ++j) {
+                // slab row r (128 bytes) holds its 16-byte chunk c at c ^ ((r >> 1) & 3): the
+                // 8 rows written at one chunk, and the two rows read per 16 lanes, then cover
+                // distinct banks (rows r and r + 2 start on the same bank)
                 if ((n16 >> 3) == h) {
-                    float *rowp = slab + (n16 & 7) * 32;
+                    const int sr = n16 & 7, sx = (sr >> 1) & 3;
+                    float *rowp = slab + sr * 32;
                     const float4_t m0 = *(const float4_t *)(s_vmul + 32 * j + 4 * g16);
                     const float4_t m1 = *(const float4_t *)(s_vmul + 32 * j + 16 + 4 * g16);
                     const float4_t v0 = o[2 * j] * m0, v1 = o[2 * j + 1] * m1;
-                    *(float4_t *)(rowp + 4 * g16) = v0;
-                    *(float4_t *)(rowp + 16 + 4 * g16) = v1;
+                    *(float4_t *)(rowp + 4 * (g16 ^ sx)) = v0;
+                    *(float4_t *)(rowp + 16 + 4 * (g16 ^ sx)) = v1;
                 }
-                const float4_t v = *(const float4_t *)(slab + 4 * lane);
+                const int lr = lane >> 3;
+                const float4_t v =
+                    *(const float4_t *)(slab + lr * 32 + 4 * ((lane & 7) ^ ((lr >> 1) & 3)));
                 if (rvalid) __builtin_nontemporal_store(v, (float4_t *)(dst + 32 * j));
             }
         }
