@@ -93,11 +93,16 @@ constexpr int kWavesPerCu = 8;          // resident decode waves per CU (2 per S
 // pieces, partials and start-up chains: 224 shares on 256 CUs 182.5 -> 179.4 us (208: 180.0,
 // 240: 181.2) on the batch-64 decode.
 constexpr int kDecodeCusNum = 7, kDecodeCusDen = 8;
+// Waves of a decode workgroup that runs beside a prefill workgroup on each CU (the prefill
+// workgroup's shape). Measured on the batch-64 decode: one such workgroup per CU (1024 waves)
+// reads the cache in 190.8 us against 179.4 us for 224 workgroups of 8 waves.
+constexpr int kFusedDecodeWaves = kPrefillCols / 32;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct PagedPlan {
     int Q, ncb_dec, tpi_dec, tpi_pre;
+    bool fused;  // decode and prefill items in one launch (decode_prefill)
     int mode, splits, gw, slots;
     int cap_dec, cap_pre, cap_comb, unit_cap;
     size_t off_dec, off_pre, off_comb, off_slot, off_first, off_o, off_m, off_l, total;
@@ -137,13 +142,23 @@ bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
     p.tpi_dec = 16 * p.ncb_dec / p.Q;
     p.gw = p.ncb_dec == 1 ? std::gcd(G, 8) : 1;
     p.tpi_pre = std::max(1, kPrefillCols / p.Q);  // one prefill workgroup: kPrefillCols columns
+    // Decode and prefill run in one launch when the call surely has prefill items (more tokens
+    // than B decode items hold, so some sequence has more new tokens than a decode item) and the
+    // decode workgroups can take the prefill workgroups' shape (kPrefillCols / 32 waves, one kv
+    // head each): then every CU holds one decode and one prefill workgroup, and the prefill's
+    // matrix work hides under the decode's memory time. Otherwise the decode kernel runs alone
+    // with its own layout and the prefill follows it.
+    p.fused = p.ncb_dec == 1 && G % kFusedDecodeWaves == 0 &&
+              (long long)T > (long long)B * p.tpi_dec;
+    if (p.fused) p.gw = kFusedDecodeWaves;
     if (num_splits == PA_SPLITS_AUTO) {
         p.mode = 0;
         p.splits = 0;
         // one share per resident decode workgroup (gw waves each, kWavesPerCu waves per CU) on
-        // kDecodeCusNum / kDecodeCusDen of the CUs
-        p.slots = std::max(1, device_cu_count() * kDecodeCusNum / kDecodeCusDen * kWavesPerCu /
-                                  p.gw);
+        // kDecodeCusNum / kDecodeCusDen of the CUs; beside the prefill, one per CU
+        p.slots = p.fused ? device_cu_count()
+                          : std::max(1, device_cu_count() * kDecodeCusNum / kDecodeCusDen *
+                                            kWavesPerCu / p.gw);
         p.cap_dec = p.slots + B;   // each share boundary adds at most one piece
         p.unit_cap = p.tpi_dec * p.cap_dec;
     } else {
@@ -368,8 +383,8 @@ struct AttnCall {
     PlanArgs pl;
     AttnArgs a;
     CombineArgs c;
-    int D, ncb_dec, blocks, pblocks, cap_comb;
-    bool combine;
+    int D, ncb_dec, blocks, pblocks, pstatic, cap_comb, comb_groups;
+    bool combine, fused;
 };
 
 // q_stride: the query row stride in elements. With validate_only the call checks every
@@ -458,14 +473,21 @@ pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t
     } else {
         a.slot_ptr = nullptr;
         const long long units = (long long)p.cap_dec * (G / p.gw);
-        call.blocks = (int)std::min(units, (long long)cus * kWavesPerCu / p.gw);
+        call.blocks = (int)std::min(units, p.fused ? (long long)cus
+                                                   : (long long)cus * kWavesPerCu / p.gw);
     }
     call.D = D;
     call.ncb_dec = p.ncb_dec;
+    call.fused = p.fused;
     const long long pre_units = (long long)p.cap_pre * G;
-    // persistent prefill workgroups: as many as fit at once (two waves per SIMD)
+    // persistent prefill workgroups: as many as fit at once (two waves per SIMD); beside the
+    // decode, one per CU takes a first unit statically and one more per CU takes units only
+    // from the counter (it runs when a decode workgroup leaves)
     call.pblocks = (int)std::min(pre_units, (long long)cus * 8 / (kPrefillCols / 32));
+    call.pstatic = p.fused ? (int)std::min(pre_units, (long long)cus) : call.pblocks;
     call.cap_comb = p.cap_comb;
+    // combine entries are rows of decode-like sequences: at most B * tpi_dec
+    call.comb_groups = (int)std::min<long long>(p.cap_comb, (long long)s.batch * p.tpi_dec);
     call.combine = p.unit_cap > 0;
     // The split decode rows are merged by extra workgroups of the prefill launch.
     CombineArgs &c = call.c;
@@ -486,17 +508,27 @@ pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t
 
 // The decode launch, then the prefill launch (which also merges the split decode rows); the
 // planner has run before them on the same stream.
+// Fused: one launch runs the decode and the prefill items side by side, then the split decode
+// rows are merged by a launch of their own.
 pa_status run_attention(const AttnCall &call, int tpi_pre, hipStream_t strm) {
     AttnArgs a = call.a;
+    AttnArgs pre = a;
+    pre.items = call.pl.pre;
+    pre.n_items = &call.pl.hdr->n_pre;
+    pre.counter = &call.pl.hdr->next_pre;
+    pre.slot_ptr = nullptr;
+    pre.slot_first = nullptr;
+    pre.tpi = tpi_pre;
+    pre.gw = 1;
+    if (call.fused) {
+        pa_status st = launch_decode_prefill(a, pre, call.D, call.blocks, call.pstatic,
+                                             call.pblocks, strm);
+        if (st != PA_OK || !call.combine) return st;
+        return launch_combine(call.c, call.comb_groups, strm);
+    }
     pa_status st = launch_attention(a, call.D, call.ncb_dec, call.blocks, "attn_decode", strm);
     if (st != PA_OK) return st;
-    a.items = call.pl.pre;
-    a.n_items = &call.pl.hdr->n_pre;
-    a.counter = &call.pl.hdr->next_pre;
-    a.slot_ptr = nullptr;
-    a.tpi = tpi_pre;
-    a.gw = 1;
-    return launch_prefill(a, call.D, call.pblocks, call.combine ? &call.c : nullptr,
+    return launch_prefill(pre, call.D, call.pblocks, call.combine ? &call.c : nullptr,
                           call.cap_comb, strm);
 }
 

@@ -188,6 +188,11 @@ constexpr int kPrefillCols = 128;  // (token, head) columns per prefill item: 4 
 struct CombineArgs;
 pa_status launch_prefill(const AttnArgs &a, int D, int blocks, const CombineArgs *cmb,
                          int max_groups, hipStream_t stream);
+// Decode items (dec, workgroups of kPrefillCols / 32 waves: dec.gw must equal that) and prefill
+// items (pre) in one launch: dec_blocks decode workgroups first, then pre_blocks prefill
+// workgroups, the first pre_static of which take their first unit statically.
+pa_status launch_decode_prefill(const AttnArgs &dec, const AttnArgs &pre, int D, int dec_blocks,
+                                int pre_static, int pre_blocks, hipStream_t stream);
 
 struct CombineArgs {
     const float *o;

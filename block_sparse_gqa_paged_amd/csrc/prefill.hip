@@ -24,6 +24,7 @@
 //    maximum grows by more than 2^8); the column reductions use row-swap permutes, not LDS.
 //    The two column blocks of a wave share each K and V read.
 #include "combine_rows.h"
+#include "decode_unit.h"
 
 namespace pa {
 namespace {
@@ -135,14 +136,25 @@ __device__ __forceinline__ float col_sum(float x) {
 // (exact in fp16 range) and the final O / l does not depend on which reference maximum was used.
 constexpr float kSlack = 8.f;
 
-// The launch after the decode kernel: the first gridDim.x - pre_blocks workgroups merge the
-// split decode partials (combine role, at most one per CU), the other pre_blocks run the
-// persistent prefill loop. The two roles are independent (prefill rows are written directly),
-// so one launch serves both and the step has one launch fewer. The combine workgroups come
-// first: placed last they would wait for the persistent prefill workgroups to leave.
+// One launch, two roles by workgroup index:
+//  * workgroups [0, gridDim.x - pre_blocks) either merge the split decode partials (combine
+//    role, at most one per CU; the decode kernel ran in the launch before), or, with
+//    dec_blocks > 0, run the decode (decode role: decode_loop over dec with kPfWaves-wave
+//    workgroups, each wave's 32-key K tile in the first LDS stage) beside the prefill;
+//  * the other pre_blocks run the persistent prefill loop; the first static_first of them take
+//    their first unit without the counter.
+// The roles are independent (prefill rows are written directly, and decode and prefill items
+// never share a row), so one launch serves both. The front roles come first in launch order:
+// placed last, the combine would wait for the persistent prefill workgroups to leave, and the
+// decode's static shares must all be resident from the start. With the decode role the grid
+// holds one decode and one prefill workgroup per CU (two 4-wave workgroups fit a CU by LDS and
+// registers), then prefill workgroups that only take units from the counter, which run once
+// decode workgroups leave.
 template <int D>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, CombineArgs cmb,
-                                                                 int pre_blocks) {
+                                                                 int pre_blocks, AttnArgs dec,
+                                                                 int dec_blocks,
+                                                                 int static_first) {
     constexpr int KB = D / 32;           // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;          // 16-dim output tiles
     constexpr int KC = D / 8;
@@ -153,6 +165,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
     __shared__ int s_unit;
 
     if ((int)blockIdx.x < (int)gridDim.x - pre_blocks) {
+        if (dec_blocks > 0) {
+            // decode role: dec.gw == kPfWaves waves, K tiles of 32 keys in the first stage
+            static_assert(kPfWaves * kTileKeys * D <= 2 * kKT * D, "decode K tiles fit Ks");
+            half_t *kl = &Ks[0][0] + (threadIdx.x >> 6) * (kTileKeys * D);
+            if (dec.log2bs >= 0)
+                decode_loop<D, 1, true, true>(dec, blockIdx.x, kl, &s_unit);
+            else
+                decode_loop<D, 1, false, true>(dec, blockIdx.x, kl, &s_unit);
+            return;
+        }
         constexpr int kWg = kPfThreads / 64;
         combine_dispatch<D>(cmb, 2, blockIdx.x * kWg + (threadIdx.x >> 6),
                         (gridDim.x - pre_blocks) * kWg);
@@ -163,15 +185,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
     const int n_work = a.n_items[0] * a.G;
     if (n_work == 0) return;
 
-    // Prefill workgroup pb takes unit pb first (the planner lists the longest units first), then
-    // units pre_blocks + k in the order of the counter's tickets k: no atomic round trip and no
-    // barrier before the first unit. Later units start after a barrier, so no wave still reads
-    // the previous unit's LDS stage when the new unit's first copies land in it.
+    // Prefill workgroup pb < static_first takes unit pb first (the planner lists the longest
+    // units first): no atomic round trip and no barrier before the first unit. Every other unit
+    // is static_first + k for the counter's ticket k; it starts after a barrier, so no wave
+    // still reads the previous unit's LDS stage when the new unit's first copies land in it.
     const int pb = (int)blockIdx.x - ((int)gridDim.x - pre_blocks);
     for (int iter = 0;; ++iter) {
         int unit = pb;
-        if (iter > 0) {
-            if (threadIdx.x == 0) s_unit = pre_blocks + atomicAdd(a.counter, 1);
+        if (iter > 0 || pb >= static_first) {
+            if (threadIdx.x == 0) s_unit = static_first + atomicAdd(a.counter, 1);
             __syncthreads();
             unit = s_unit;
             __syncthreads();
@@ -372,10 +394,31 @@ pa_status launch_prefill(const AttnArgs &a, int D, int blocks, const CombineArgs
     }
     const int grid = blocks + comb_blocks;
     if (grid <= 0) return PA_OK;
+    const AttnArgs none{};
     if (D == 128)
-        scope.launch(prefill_kernel<128>, dim3(grid), dim3(kPfThreads), 0, a, c, blocks);
+        scope.launch(prefill_kernel<128>, dim3(grid), dim3(kPfThreads), 0, a, c, blocks, none, 0,
+                     blocks);
     else if (D == 64)
-        scope.launch(prefill_kernel<64>, dim3(grid), dim3(kPfThreads), 0, a, c, blocks);
+        scope.launch(prefill_kernel<64>, dim3(grid), dim3(kPfThreads), 0, a, c, blocks, none, 0,
+                     blocks);
+    else
+        return PA_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status launch_decode_prefill(const AttnArgs &dec, const AttnArgs &pre, int D, int dec_blocks,
+                                int pre_static, int pre_blocks, hipStream_t stream) {
+    LaunchScope scope("decode_prefill", stream);
+    if (dec.gw != kPfWaves || pre_static > pre_blocks || dec_blocks < 0) return PA_ERR_UNSUPPORTED;
+    const int grid = dec_blocks + pre_blocks;
+    if (grid <= 0) return PA_OK;
+    const CombineArgs c{};
+    if (D == 128)
+        scope.launch(prefill_kernel<128>, dim3(grid), dim3(kPfThreads), 0, pre, c, pre_blocks, dec,
+                     dec_blocks, pre_static);
+    else if (D == 64)
+        scope.launch(prefill_kernel<64>, dim3(grid), dim3(kPfThreads), 0, pre, c, pre_blocks, dec,
+                     dec_blocks, pre_static);
     else
         return PA_ERR_UNSUPPORTED;
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;

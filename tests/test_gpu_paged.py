@@ -263,13 +263,16 @@ def test_many_sequences_attention(B, num_splits):
 
 @pytest.mark.parametrize("one_call", [False, True], ids=["two_calls", "one_call"])
 @pytest.mark.parametrize("num_splits", [pa.PA_SPLITS_AUTO, 3], ids=lambda s: f"S{s}")
-def test_graph_capture_replays_match_eager(num_splits, one_call):
+@pytest.mark.parametrize("kv_heads", [2, 8], ids=["serial", "fused"])
+def test_graph_capture_replays_match_eager(num_splits, one_call, kv_heads):
     """The append and the attention (two calls, or pa_append_attention) captured into one HIP
     graph (the library enqueues kernels only: no allocation, memset or synchronization): every
-    replay, with eager library work between replays, is bit-identical to the eager step."""
-    w = W.paged_workload(160, past=[40, 300, 5, 1000], n_new=[1, 70, 1, 33], num_heads=8,
-                         kv_num_heads=2, head_size=128, block_size=16, table="pool",
-                         name="graph")
+    replay, with eager library work between replays, is bit-identical to the eager step. With 8
+    kv heads the decode and prefill items share one launch (the merge of split rows follows in a
+    launch of its own); with 2 the decode kernel runs alone, then the prefill launch."""
+    w = W.paged_workload(160, past=[40, 300, 5, 1000], n_new=[1, 70, 1, 33],
+                         num_heads=4 * kv_heads, kv_num_heads=kv_heads, head_size=128,
+                         block_size=16, table="pool", name="graph")
     c = dev.PagedCase(w)
 
     def step():
