@@ -24,7 +24,7 @@ PA_SPLITS_AUTO, PA_SPLITS_PAGE_RULE = 0, -1
 # pa_check_paged_indices flag bits (include/pa.h)
 PA_CHECK_CU_START, PA_CHECK_CU_ORDER, PA_CHECK_CU_END, PA_CHECK_PAST = 1, 2, 4, 8
 PA_CHECK_TABLE_WIDTH, PA_CHECK_TABLE_ENTRY, PA_CHECK_SLOT = 16, 32, 64
-PA_CHECK_SLOT_TABLE, PA_CHECK_POSITION = 128, 256
+PA_CHECK_SLOT_TABLE, PA_CHECK_POSITION, PA_CHECK_SLOT_DUP = 128, 256, 512
 
 EXPORTED = ("pa_kv_append", "pa_kv_append_rotate_query", "pa_paged_attention_workspace_size",
             "pa_paged_attention", "pa_paged_attention_noalloc", "pa_append_attention",

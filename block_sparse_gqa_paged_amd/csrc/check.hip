@@ -36,7 +36,8 @@ __device__ __forceinline__ bool seq_len(const CheckArgs &a, int b, long long &n,
 }
 
 // Three sweeps in one grid-stride launch: sequences (offsets, past lengths, table width),
-// block-table entries in use, and new rows (slot_mapping, rotary positions).
+// block-table entries in use, and new rows (slot_mapping, rotary positions). Duplicate slots are
+// a launch of their own (check_slot_dup).
 __global__ __launch_bounds__(256) void check_paged(CheckArgs a) {
     const long long stride = (long long)gridDim.x * blockDim.x;
     const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -88,6 +89,48 @@ __global__ __launch_bounds__(256) void check_paged(CheckArgs a) {
     raise_bits(a.flags, bits);
 }
 
+// The slot new row i writes: its slot_mapping entry, else the slot the block table gives its
+// position (only when the position falls inside the table row); -1 when none.
+__device__ __forceinline__ long long row_slot(const CheckArgs &a, int i) {
+    if (a.slot) return a.slot[i];
+    if (!a.bt) return -1;
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.cu[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const long long pos = (long long)a.past[lo] + (i - a.cu[lo]);
+    if (pos < 0 || pos / a.bs >= a.MB) return -1;
+    return (long long)a.bt[(long long)lo * a.MB + pos / a.bs] * a.bs + pos % a.bs;
+}
+
+// Duplicate written slots: workgroup w takes the w-th pair (k, t), t >= k, of 256-row tiles,
+// stages tile t's slots in LDS and compares each of tile k's rows with them (rows j > i only).
+// Every non-negative slot takes part.
+constexpr int kDupTile = 256;
+__global__ __launch_bounds__(kDupTile) void check_slot_dup(CheckArgs a, int ntiles) {
+    __shared__ long long sj[kDupTile];
+    // pair index -> (k, t): pairs are listed k-major, tile k owning ntiles - k pairs
+    long long w = blockIdx.x;
+    int k = 0;
+    while (w >= ntiles - k) {
+        w -= ntiles - k;
+        ++k;
+    }
+    const int t = k + (int)w;
+    const int i = k * kDupTile + threadIdx.x;
+    const int j0 = t * kDupTile;
+    const int jr = j0 + threadIdx.x;
+    sj[threadIdx.x] = jr < a.T ? row_slot(a, jr) : -1;
+    const long long si = i < a.T ? row_slot(a, i) : -1;
+    __syncthreads();
+    bool dup = false;
+    if (si >= 0)
+        for (int x = 0; x < kDupTile; ++x)
+            dup |= (j0 + x > i) && sj[x] == si;
+    if (__ballot(dup) != 0 && (threadIdx.x & 63) == 0) atomicOr(a.flags, PA_CHECK_SLOT_DUP);
+}
+
 }  // namespace
 
 pa_status launch_check_paged(const pa_paged_shape &s, const int32_t *cu, const int32_t *past,
@@ -109,9 +152,14 @@ pa_status launch_check_paged(const pa_paged_shape &s, const int32_t *cu, const i
         std::max<long long>(std::max<long long>((long long)s.batch * s.max_blocks, s.num_tokens),
                             (long long)s.batch + 1);
     const int grid = (int)std::min<long long>((work + 255) / 256, 1024);
-    LaunchScope scope("check_paged", stream, 2);
+    const long long ntiles = ((long long)s.num_tokens + kDupTile - 1) / kDupTile;
+    const long long pairs = (a.slot || a.bt) ? ntiles * (ntiles + 1) / 2 : 0;
+    if (pairs > (1LL << 31) - 1) return PA_ERR_UNSUPPORTED;
+    LaunchScope scope("check_paged", stream, pairs > 0 ? 3 : 2);
     scope.launch(check_clear, dim3(1), dim3(1), 0, flags);
     scope.launch(check_paged, dim3(grid), dim3(256), 0, a);
+    if (pairs > 0)
+        scope.launch(check_slot_dup, dim3((unsigned)pairs), dim3(kDupTile), 0, a, (int)ntiles);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -430,12 +430,19 @@ pa_status pa_kv_append_bnsh(const pa_bnsh_shape *shape, const void *query, const
  *                         append wrote)
  *   PA_CHECK_POSITION     with rotary_positions > 0: a new row's position is outside
  *                         [0, rotary_positions) (its cos/sin row does not exist)
+ *   PA_CHECK_SLOT_DUP     two new rows would write the same cache slot (their slot_mapping
+ *                         entries, or without slot_mapping the slots the block table gives their
+ *                         positions; negative slots write nothing and do not count): the append
+ *                         would race on that slot
  * slot_mapping may be NULL (not checked); block_table may be NULL (entries, and slot_mapping
  * against the table, not checked); rotary_positions = 0 skips the position rule.
  *   flags  int32 [1] (device), written by the call (cleared first); read it after the stream
  *          reaches the call. 0 means every rule holds.
  * Only the index arrays are read, inside their declared sizes; no index is followed, so any
- * contents are safe to check. Two small launches, no allocation, no host synchronisation.
+ * contents are safe to check. Up to three launches (the duplicate-slot rule compares every pair
+ * of new rows in 256-row tiles), no allocation, no host synchronisation.
+ * Errors (besides these): PA_ERR_UNSUPPORTED when num_tokens needs more than 2^31 - 1 tile
+ * pairs.
  * Errors: PA_ERR_NULL (shape, cumulative_sequence_length, past_seqlens or flags NULL),
  * PA_ERR_SHAPE or PA_ERR_UNSUPPORTED (the shape rules of pa_kv_append), PA_ERR_SHAPE
  * (rotary_positions < 0), PA_ERR_HIP.
@@ -449,6 +456,7 @@ pa_status pa_kv_append_bnsh(const pa_bnsh_shape *shape, const void *query, const
 #define PA_CHECK_SLOT 64
 #define PA_CHECK_SLOT_TABLE 128
 #define PA_CHECK_POSITION 256
+#define PA_CHECK_SLOT_DUP 512
 pa_status pa_check_paged_indices(const pa_paged_shape *shape,
                                  const int32_t *cumulative_sequence_length,
                                  const int32_t *past_seqlens, const int32_t *block_table,

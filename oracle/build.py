@@ -12,14 +12,29 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose=False):
-    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+# AddressSanitizer and UndefinedBehaviorSanitizer build (host code; a CPU check of the oracle):
+# every undefined-behaviour report aborts. A process loading it must preload gcc's libasan.
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+            "-g"]
+
+
+def build(verbose=False, sanitize=False, out=None):
+    """Compile oracle.c into out (default oracle/liboracle.so); sanitize=True adds ASan/UBSan."""
+    lib = out or LIB
+    cmd = (["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+            "-Wall", "-Wextra"] + (SANITIZE if sanitize else []) +
+           ["-o", lib + ".tmp", SRC, "-lm"])
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
+
+
+def asan_runtime():
+    """gcc's AddressSanitizer runtime, to preload into a process that loads the sanitized build."""
+    return subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                          check=True).stdout.strip()
 
 
 if __name__ == "__main__":

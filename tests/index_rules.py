@@ -35,21 +35,26 @@ def expected_flags(cu, past, block_table, slot_mapping, *, T, NB, bs, MB, rotary
                     bits |= pa.PA_CHECK_TABLE_ENTRY
     if bits & (pa.PA_CHECK_CU_START | pa.PA_CHECK_CU_ORDER):
         return bits  # rows have no defined sequence: the remaining rules are not compared
+    written = set()  # slots the new rows write, for the duplicate rule
     for i in range(T):
         b = max(k for k in range(B) if cu[k] <= i)
         pos = past[b] + i - cu[b]
         if rotary_positions > 0 and not (0 <= pos < rotary_positions):
             bits |= pa.PA_CHECK_POSITION
-        if slot_mapping is None:
-            continue
-        s = int(slot_mapping[i])
-        if s < 0:
+        derived = None
+        if block_table is not None and pos >= 0 and pos // bs < MB:
+            derived = int(block_table[b][pos // bs]) * bs + pos % bs
+        s = int(slot_mapping[i]) if slot_mapping is not None else derived
+        if s is not None and s >= 0:
+            if s in written:
+                bits |= pa.PA_CHECK_SLOT_DUP  # two rows write one slot: the append races
+            written.add(s)
+        if slot_mapping is None or s < 0:
             continue
         if s >= NB * bs:
             bits |= pa.PA_CHECK_SLOT
-        elif block_table is not None and pos >= 0 and pos // bs < MB:
-            if int(block_table[b][pos // bs]) * bs + pos % bs != s:
-                bits |= pa.PA_CHECK_SLOT_TABLE
+        elif derived is not None and derived != s:
+            bits |= pa.PA_CHECK_SLOT_TABLE
     return bits
 
 

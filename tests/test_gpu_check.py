@@ -1,7 +1,9 @@
 """GPU tests of pa_check_paged_indices against the plain statement of the index rules
 (tests/index_rules.py): seeded workloads pass every rule, each hand-made violation raises its
 bits, and seeded random corruptions of a rotary workload give the same flag word on both sides.
-The check only reads the index arrays, so corrupted contents are safe to pass to it."""
+The check only reads the index arrays, so corrupted contents are safe to pass to it. Duplicate
+written slots (two rows, one slot: the append would race) are checked within and across 256-row
+tiles."""
 import copy
 
 import numpy as np
@@ -63,7 +65,24 @@ EDITS = [
     ("slot_skip", lambda d: d["slot"].__setitem__(0, -1)),
     ("position", lambda d: d.__setitem__("rotary_positions", 6)),
     ("no_table", lambda d: d.update(bt=None)),
+    ("slot_dup", lambda d: d["slot"].__setitem__(4, 25)),            # rows 0 and 4 share a slot
+    ("slot_dup_derived", lambda d: d.update(slot=None, bt=[[3, 6, -1], [6, 0, -1]])),  # shared block
 ]
+
+
+def test_duplicate_slot_across_tiles():
+    """600 new rows (three 256-row tiles): distinct slots pass; one repeated slot between the
+    first and the last tile raises the duplicate bit, on both sides."""
+    T, bs, NB = 600, 16, 64
+    cu, past = [0, 200, 450, T], [0, 7, 30]
+    slot = list(np.random.default_rng(5).permutation(NB * bs)[:T])
+    kw = dict(T=T, NB=NB, bs=bs, MB=64)
+    assert _device_flags(cu, past, None, slot, **kw) == expected_flags(cu, past, None, slot,
+                                                                     **kw) == 0
+    slot[590] = slot[3]
+    want = expected_flags(cu, past, None, slot, **kw)
+    assert want == pa.PA_CHECK_SLOT_DUP
+    assert _device_flags(cu, past, None, slot, **kw) == want
 
 
 @pytest.mark.parametrize("name,edit", EDITS, ids=[e[0] for e in EDITS])

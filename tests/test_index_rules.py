@@ -54,6 +54,12 @@ def test_hand_made_case_is_valid():
     (lambda d: d["slot_mapping"].__setitem__(4, 7), pa.PA_CHECK_SLOT_TABLE),
     (lambda d: d["slot_mapping"].__setitem__(0, -1), 0),                # not written: allowed
     (lambda d: d.__setitem__("rotary_positions", 6), pa.PA_CHECK_POSITION),
+    # row 4 maps to row 0's slot (and off the slot its position has): two rows, one slot
+    (lambda d: d["slot_mapping"].__setitem__(4, 25),
+     pa.PA_CHECK_SLOT_DUP | pa.PA_CHECK_SLOT_TABLE),
+    # derived slots: both sequences' tables name block 6 where their new rows land
+    (lambda d: d.update(slot_mapping=None, block_table=[[3, 6, -1], [6, 0, -1]]),
+     pa.PA_CHECK_SLOT_DUP),
 ])
 def test_each_violation_raises_its_bit(edit, bit):
     d = copy.deepcopy(_base())
