@@ -102,6 +102,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct PagedPlan {
     int Q, ncb_dec, tpi_dec, tpi_pre;
+    int kv_div, Gv;  // query-head groups per cache head, and groups in all (Gv = G * kv_div)
     bool fused;  // decode and prefill items in one launch (decode_prefill)
     int mode, splits, gw, slots;
     int cap_dec, cap_pre, cap_comb, unit_cap;
@@ -114,8 +115,8 @@ pa_status check_shape(const pa_paged_shape *s) {
         s->num_heads % s->kv_num_heads != 0 || s->head_size <= 0 || s->num_blocks < 1 ||
         s->block_size < 1 || s->max_blocks < 1 || (s->packed_qkv != 0 && s->packed_qkv != 1))
         return PA_ERR_SHAPE;
-    if (s->head_size != 64 && s->head_size != 128) return PA_ERR_UNSUPPORTED;
-    if (s->num_heads / s->kv_num_heads > 64) return PA_ERR_UNSUPPORTED;
+    if (s->head_size != 64 && s->head_size != 128 && s->head_size != 256)
+        return PA_ERR_UNSUPPORTED;
     if ((long long)s->kv_num_heads * s->head_size >= (1LL << 24)) return PA_ERR_UNSUPPORTED;
     // the kernels form in-block row offsets with 24 x 24-bit multiplies: a block's elements
     // must fit in 32 bits
@@ -134,13 +135,25 @@ int page_rule_splits(const pa_paged_shape *s) {
 
 bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
     if (check_shape(s) != PA_OK || num_splits < PA_SPLITS_PAGE_RULE) return false;
-    const int T = s->num_tokens, B = s->batch, G = s->kv_num_heads, H = s->num_heads;
+    const int T = s->num_tokens, B = s->batch, H = s->num_heads;
     const int D = s->head_size;
+    // A kv head with more query heads than the decode waves take (64; 16 at D = 256, where one
+    // column block fills a wave's registers) is served as kv_div groups of at most 16 heads
+    // (the smallest such divisor of H / G_cache), each group reading the same cache head.
+    const int Qc = H / s->kv_num_heads;
+    p.kv_div = 1;
+    if (Qc > (D == 256 ? 16 : 64))
+        for (p.kv_div = 2; Qc % p.kv_div != 0 || Qc / p.kv_div > 16; ++p.kv_div) {}
+    p.Gv = s->kv_num_heads * p.kv_div;
+    const int G = p.Gv;
     p.Q = H / G;
     p.gw = 0;  // set below from the decode kernel's column blocks
     p.ncb_dec = p.Q <= 16 ? 1 : (p.Q <= 32 ? 2 : 4);
     p.tpi_dec = 16 * p.ncb_dec / p.Q;
-    p.gw = p.ncb_dec == 1 ? std::gcd(G, 8) : 1;
+    // decode waves per workgroup (kv heads of an item side by side) and resident per CU: at
+    // D = 256 one wave per SIMD (its tiles need the whole register file)
+    const int dec_waves = D == 256 ? 4 : 8;
+    p.gw = p.ncb_dec == 1 ? std::gcd(G, dec_waves) : 1;
     p.tpi_pre = std::max(1, kPrefillCols / p.Q);  // one prefill workgroup: kPrefillCols columns
     // Decode and prefill run in one launch when the call surely has prefill items (more tokens
     // than B decode items hold, so some sequence has more new tokens than a decode item) and the
@@ -148,7 +161,7 @@ bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
     // head each): then every CU holds one decode and one prefill workgroup, and the prefill's
     // matrix work hides under the decode's memory time. Otherwise the decode kernel runs alone
     // with its own layout and the prefill follows it.
-    p.fused = p.ncb_dec == 1 && G % kFusedDecodeWaves == 0 &&
+    p.fused = p.ncb_dec == 1 && G % kFusedDecodeWaves == 0 && D <= 128 &&
               (long long)T > (long long)B * p.tpi_dec;
     if (p.fused) p.gw = kFusedDecodeWaves;
     if (num_splits == PA_SPLITS_AUTO) {
@@ -158,7 +171,7 @@ bool make_plan(const pa_paged_shape *s, int num_splits, PagedPlan &p) {
         // kDecodeCusNum / kDecodeCusDen of the CUs; beside the prefill, one per CU
         p.slots = p.fused ? device_cu_count()
                           : std::max(1, device_cu_count() * kDecodeCusNum / kDecodeCusDen *
-                                            kWavesPerCu / p.gw);
+                                            (D == 256 ? 4 : kWavesPerCu) / p.gw);
         p.cap_dec = p.slots + B;   // each share boundary adds at most one piece
         p.unit_cap = p.tpi_dec * p.cap_dec;
     } else {
@@ -405,13 +418,14 @@ pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t
         return PA_ERR_NULL;
     PagedPlan p;
     if (!make_plan(shape, num_splits, p)) return PA_ERR_SHAPE;
+    const int Gc = s.kv_num_heads;  // cache heads (the layout); p.Gv groups of p.Q query heads
     if (s.num_tokens == 0) return PA_OK;
     if (validate_only) return workspace_bytes < p.total ? PA_ERR_WORKSPACE : PA_OK;
     if (!workspace) return PA_ERR_NULL;
     if (workspace_bytes < p.total || ((uintptr_t)workspace % kAlign) != 0)
         return PA_ERR_WORKSPACE;
     char *ws = (char *)workspace;
-    const int H = s.num_heads, G = s.kv_num_heads, D = s.head_size;
+    const int H = s.num_heads, G = p.Gv, D = s.head_size;
 
     PlanArgs &pl = call.pl;
     pl.cu = cumulative_sequence_length;
@@ -449,11 +463,12 @@ pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t
     a.m_part = (float *)(ws + p.off_m);
     a.l_part = (float *)(ws + p.off_l);
     a.q_stride = q_stride;
-    a.block_elems = (int64_t)s.block_size * G * D;
-    a.key_elems = (uint32_t)(G * D);
+    a.block_elems = (int64_t)s.block_size * Gc * D;
+    a.key_elems = (uint32_t)(Gc * D);
     a.H = H;
     a.G = G;
     a.Q = p.Q;
+    a.kv_div = p.kv_div;
     a.bs = s.block_size;
     a.MB = s.max_blocks;
     a.log2bs = log2_pow2_ge8(s.block_size);
@@ -473,8 +488,9 @@ pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t
     } else {
         a.slot_ptr = nullptr;
         const long long units = (long long)p.cap_dec * (G / p.gw);
-        call.blocks = (int)std::min(units, p.fused ? (long long)cus
-                                                   : (long long)cus * kWavesPerCu / p.gw);
+        call.blocks = (int)std::min(
+            units, p.fused ? (long long)cus
+                           : (long long)cus * (D == 256 ? 4 : kWavesPerCu) / p.gw);
     }
     call.D = D;
     call.ncb_dec = p.ncb_dec;
@@ -483,7 +499,7 @@ pa_status make_attention(const pa_paged_shape *shape, const void *query, int64_t
     // persistent prefill workgroups: as many as fit at once (two waves per SIMD); beside the
     // decode, one per CU takes a first unit statically and one more per CU takes units only
     // from the counter (it runs when a decode workgroup leaves)
-    call.pblocks = (int)std::min(pre_units, (long long)cus * 8 / (kPrefillCols / 32));
+    call.pblocks = (int)std::min(pre_units, (long long)cus * (D == 256 ? 1 : 2));
     call.pstatic = p.fused ? (int)std::min(pre_units, (long long)cus) : call.pblocks;
     call.cap_comb = p.cap_comb;
     // combine entries are rows of decode-like sequences: at most B * tpi_dec
@@ -663,7 +679,7 @@ pa_status pa_split_combine(const float *o_partial, const float *m_partial,
         (out_dtype != PA_F16 && out_dtype != PA_F32))
         return PA_ERR_SHAPE;
     if (!group_ptr && num_splits < 1) return PA_ERR_SHAPE;
-    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
     if (num_groups == 0) return PA_OK;
     if (!o_partial || !m_partial || !l_partial || !out) return PA_ERR_NULL;
     CombineArgs c;
@@ -688,8 +704,9 @@ static pa_status check_sparse(const pa_sparse_shape *s) {
         s->block_size < 1 || s->page_size < 1 || s->block_size % s->page_size != 0 ||
         s->num_pages < 0 || s->max_pages < 1 || s->batch < 1)
         return PA_ERR_SHAPE;
-    if (s->head_dim != 64 && s->head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (s->block_size > 128 || s->qhead > 16) return PA_ERR_UNSUPPORTED;
+    if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256) return PA_ERR_UNSUPPORTED;
+    // the key block's fp16 planes live in LDS: up to 128 keys, 64 at D = 256
+    if (s->block_size > (s->head_dim == 256 ? 64 : 128)) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
 
@@ -791,7 +808,7 @@ pa_status pa_kv_append_bnsh(const pa_bnsh_shape *shape, const void *query, const
         s.num_heads % s.kv_num_heads != 0 || s.head_size <= 0 || s.max_cache_seq < 1 ||
         (s.packed_qkv != 0 && s.packed_qkv != 1))
         return PA_ERR_SHAPE;
-    if (s.head_size != 64 && s.head_size != 128) return PA_ERR_UNSUPPORTED;
+    if (s.head_size != 64 && s.head_size != 128 && s.head_size != 256) return PA_ERR_UNSUPPORTED;
     if (s.packed_qkv) {
         if (key || value) return PA_ERR_SHAPE;
         if (!query) return PA_ERR_NULL;

@@ -51,9 +51,10 @@ pa_status launch_plan(const PlanArgs &a, hipStream_t stream) {
 // ============================================================================================
 namespace {
 // Persistent decode kernel: decode_loop over workgroups of a.gw waves, each with its own LDS
-// K tile.
+// K tile. At D = 256 a workgroup has at most 4 waves, one per SIMD, so that each can hold its
+// 256-dim query, output and V tiles in registers.
 template <int D, int NCB, bool POW2, bool NT>
-__global__ __launch_bounds__(NCB == 1 ? 512 : 64) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NCB == 1 ? (D == 256 ? 256 : 512) : 64) void attn_kernel(AttnArgs a) {
     extern __shared__ half_t s_ktile[];  // one 32-key K tile per wave: [gw][32][D]
     __shared__ int s_unit;
     decode_loop<D, NCB, POW2, NT>(a, blockIdx.x, s_ktile + (threadIdx.x >> 6) * (kTileKeys * D),
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(NCB == 1 ? 512 : 64) void attn_kernel(AttnArgs a) {
 template <int D, int NCB, bool NT>
 pa_status launch_d_ncb(const AttnArgs &a, int blocks, LaunchScope &scope) {
     const dim3 g(blocks), blk(64 * a.gw);
-    const uint32_t lds = (uint32_t)(a.gw * kTileKeys * D * sizeof(half_t));  // <= 64 KB
+    const uint32_t lds = (uint32_t)(a.gw * kTileKeys * D * sizeof(half_t));  // <= 128 KB
     if (a.log2bs >= 0)
         scope.launch(attn_kernel<D, NCB, true, NT>, g, blk, lds, a);
     else
@@ -73,6 +74,10 @@ pa_status launch_d_ncb(const AttnArgs &a, int blocks, LaunchScope &scope) {
 
 template <int D, bool NT>
 pa_status launch_d(const AttnArgs &a, int ncb, int blocks, LaunchScope &scope) {
+    if constexpr (D == 256) {  // wider kv groups are split into groups of <= 16 query heads
+        if (ncb != 1) return PA_ERR_UNSUPPORTED;
+        return launch_d_ncb<D, 1, NT>(a, blocks, scope);
+    }
     switch (ncb) {
         case 1: return launch_d_ncb<D, 1, NT>(a, blocks, scope);
         case 2: return launch_d_ncb<D, 2, NT>(a, blocks, scope);
@@ -91,6 +96,7 @@ pa_status launch_attention(const AttnArgs &a, int D, int ncb, int blocks, const 
     switch (D) {
         case 64: return launch_d<64, true>(a, ncb, blocks, scope);
         case 128: return launch_d<128, true>(a, ncb, blocks, scope);
+        case 256: return launch_d<256, true>(a, ncb, blocks, scope);
         default: return PA_ERR_UNSUPPORTED;
     }
 }

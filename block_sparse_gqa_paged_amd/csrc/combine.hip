@@ -31,6 +31,12 @@ pa_status launch_combine(const CombineArgs &a, int max_groups, hipStream_t strea
         case 128 * 4 + 2:
             scope.launch(combine_kernel<128, 2>, dim3(grid), dim3(256), 0, a, mode);
             break;
+        case 256 * 4 + 1:
+            scope.launch(combine_kernel<256, 1>, dim3(grid), dim3(256), 0, a, mode);
+            break;
+        case 256 * 4 + 2:
+            scope.launch(combine_kernel<256, 2>, dim3(grid), dim3(256), 0, a, mode);
+            break;
         default:
             return PA_ERR_UNSUPPORTED;
     }

@@ -171,6 +171,10 @@ struct AttnArgs {
     int64_t block_elems;  // elements per cache block: bs * G * D
     uint32_t key_elems;   // elements between consecutive keys of a block: G * D
     int H, G, Q, bs, MB, log2bs;  // log2bs < 0: block size is not a power of two >= 8
+    // G counts kv head groups of Q query heads; kv_div groups share one cache head (group g
+    // reads cache head g / kv_div), so a kv head with more query heads than one wave serves is
+    // split into kv_div groups of Q = H / (G_cache * kv_div) heads each
+    int kv_div;
     int causal;
     int gw;            // waves per workgroup, a divisor of G
     int tpi;           // tokens per item

@@ -26,7 +26,10 @@ template <int D>
 struct Tile {
     static constexpr int KB = D / 32;  // 32-dim k-blocks of QK^T
     static constexpr int W = D / 16;   // dims per lane of the V layout (D = 16 * W)
-    half8_t k[2][KB];                  // A operand rows (from LDS): keys kappa(u, n16), dims 32kb+8g16..+7
+    // K operands held in registers for the whole tile at D <= 128; at D = 256 each k-block's
+    // operands are read from LDS right before its products (the registers go to V and O)
+    static constexpr bool kKRegs = D <= 128;
+    half8_t k[2][kKRegs ? KB : 1];     // A operand rows (from LDS): keys kappa(u, n16), dims 32kb+8g16..+7
     uint32_t v[8][W / 2];              // keys 8*g16 + s, dims W*n16 .. W*n16 + W - 1
 };
 
@@ -94,6 +97,7 @@ __device__ __forceinline__ void copy_k(const AttnArgs &a, const int32_t *bt, Til
 // The A operands of the tile from the wave's LDS tile: row kappa(u, n16), dims 32kb+8g16 .. +7.
 template <int D>
 __device__ __forceinline__ void read_k(Tile<D> &t, const half_t *kl, int g16, int n16) {
+    if constexpr (!Tile<D>::kKRegs) return;  // read per k-block inside tile_scores
     constexpr int KC = D / 8, KB = Tile<D>::KB;
     for (int u = 0; u < 2; ++u) {
         const int r = kappa(u, n16);
@@ -131,7 +135,11 @@ __device__ __forceinline__ void load_v(Tile<D> &t, const AttnArgs &a, const int3
     }
     for (int s = 0; s < 8; ++s) {
         const half_t *p = pv[s] + W * n16;
-        if constexpr (W == 8) {
+        if constexpr (W == 16) {  // 32 bytes of the row: two 16-byte loads
+            const u32x4_t x = NT ? gload_nt<u32x4_t>(p) : gload<u32x4_t>(p);
+            const u32x4_t y = NT ? gload_nt<u32x4_t>(p + 8) : gload<u32x4_t>(p + 8);
+            for (int c = 0; c < 4; ++c) { t.v[s][c] = x[c]; t.v[s][4 + c] = y[c]; }
+        } else if constexpr (W == 8) {
             const u32x4_t x = NT ? gload_nt<u32x4_t>(p) : gload<u32x4_t>(p);
             t.v[s][0] = x[0]; t.v[s][1] = x[1]; t.v[s][2] = x[2]; t.v[s][3] = x[3];
         } else {
@@ -155,13 +163,24 @@ struct State {
 // (g16, n16), the scores of keys 8*g16 + 4u + i (i = 0..3) against column n16.
 template <int D, int NCB>
 __device__ __forceinline__ void tile_scores(const State<D, NCB> &st, const Tile<D> &t,
-                                            float4_t (&s)[NCB][2]) {
-    constexpr int KB = Tile<D>::KB;
+                                            float4_t (&s)[NCB][2], const half_t *kl, int g16,
+                                            int n16) {
+    constexpr int KB = Tile<D>::KB, KC = D / 8;
     for (int cb = 0; cb < NCB; ++cb) {
         float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
         for (int kb = 0; kb < KB; ++kb) {
-            s0 = mfma16x16x32(t.k[0][kb], st.q[cb][kb], s0);
-            s1 = mfma16x16x32(t.k[1][kb], st.q[cb][kb], s1);
+            if constexpr (Tile<D>::kKRegs) {
+                s0 = mfma16x16x32(t.k[0][kb], st.q[cb][kb], s0);
+                s1 = mfma16x16x32(t.k[1][kb], st.q[cb][kb], s1);
+            } else {
+                const int r0 = kappa(0, n16), r1 = kappa(1, n16);
+                const half8_t k0 =
+                    *(const half8_t *)(kl + r0 * D + 8 * ((4 * kb + g16) ^ krow_mask<KC>(r0)));
+                const half8_t k1 =
+                    *(const half8_t *)(kl + r1 * D + 8 * ((4 * kb + g16) ^ krow_mask<KC>(r1)));
+                s0 = mfma16x16x32(k0, st.q[cb][kb], s0);
+                s1 = mfma16x16x32(k1, st.q[cb][kb], s1);
+            }
         }
         s[cb][0] = s0;
         s[cb][1] = s1;
@@ -261,8 +280,8 @@ __device__ __forceinline__ void process_unit(const AttnArgs &a, const AttnItem &
     // so the in-loop copies are unconditional. The block ids of tile t+2 are requested before
     // the copies of tile t+1, so they have arrived when those copies issue.
     const int32_t *bt = a.bt + (long long)it.b * a.MB;
-    const half_t *kcg = a.kc + (size_t)g * D;
-    const half_t *vcg = a.vc + (size_t)g * D;
+    const half_t *kcg = a.kc + (size_t)(g / a.kv_div) * D;  // physical kv head
+    const half_t *vcg = a.vc + (size_t)(g / a.kv_div) * D;
     if (it.k0 < it.k1) {
         Tile<D> tl;
         int kt = it.k0;
@@ -276,7 +295,7 @@ __device__ __forceinline__ void process_unit(const AttnArgs &a, const AttnItem &
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             read_k<D>(tl, kl, g16, n16);
             float4_t s[NCB][2];
-            tile_scores<D, NCB>(st, tl, s);
+            tile_scores<D, NCB>(st, tl, s, kl, g16, n16);
             half8_t vb[W];
             tile_vt<D>(tl, vb);
             const int kn = kt + kTileKeys;
@@ -292,7 +311,7 @@ __device__ __forceinline__ void process_unit(const AttnArgs &a, const AttnItem &
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         read_k<D>(tl, kl, g16, n16);
         float4_t s[NCB][2];
-        tile_scores<D, NCB>(st, tl, s);
+        tile_scores<D, NCB>(st, tl, s, kl, g16, n16);
         half8_t vb[W];
         tile_vt<D>(tl, vb);
         tile_softmax_pv<D, NCB>(st, s, vb, kt, a.scale_log2, g16);
@@ -318,7 +337,15 @@ __device__ __forceinline__ void process_unit(const AttnArgs &a, const AttnItem &
             if (it.base < 0) {
                 const float inv = 1.f / lr[j];
                 half_t *op = a.out + row * (long long)a.H * D + (long long)h * D + W * n16;
-                if constexpr (W == 8) {
+                if constexpr (W == 16) {
+                    half8_t r0, r1;
+                    for (int i = 0; i < 8; ++i) {
+                        r0[i] = (half_t)(st.o[cb][i][j] * inv);
+                        r1[i] = (half_t)(st.o[cb][8 + i][j] * inv);
+                    }
+                    *(half8_t *)op = r0;
+                    *(half8_t *)(op + 8) = r1;
+                } else if constexpr (W == 8) {
                     half8_t r;
                     for (int i = 0; i < W; ++i) r[i] = (half_t)(st.o[cb][i][j] * inv);
                     *(half8_t *)op = r;

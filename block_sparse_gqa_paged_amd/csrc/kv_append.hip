@@ -229,7 +229,7 @@ __device__ __forceinline__ void store_row(const AppendArgs &a, const half_t *ks,
 template <int MODE, bool LANECU, bool QROLE>
 __device__ __forceinline__ void append_pairs(const AppendArgs &a, int gid, int n,
                                              int32_t *s_cu, int32_t *s_past) {
-    const int lhc = a.D == 128 ? 3 : 2;  // log2 of the chunk pairs per row (D is 64 or 128)
+    const int lhc = a.D == 256 ? 4 : (a.D == 128 ? 3 : 2);  // log2 of chunk pairs per row
     const int rows = QROLE ? a.H : a.G;  // head rows per token
     const int gidc = gid < n ? gid : n - 1;
     const int j = gidc & ((1 << lhc) - 1);
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void append_plan_kernel(AppendArgs a, Pla
 // stores run along consecutive cache rows of one head. past(b) is the padded-batch rule.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void bnsh_kernel(BnshArgs a) {
-    const int lhc = a.D == 128 ? 3 : 2;
+    const int lhc = a.D == 256 ? 4 : (a.D == 128 ? 3 : 2);  // log2(D / 16)
     const long long n = (long long)a.B * a.KVH * a.S << lhc;
     const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= n) return;

@@ -29,10 +29,21 @@
 namespace pa {
 namespace {
 
-constexpr int kKT = 64;                       // keys per tile
-constexpr int kPfWaves = kPrefillCols / 32;  // 32 (token, head) columns per wave
-constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfKpw = kKT / kPfWaves;        // keys of a tile each wave copies
+constexpr int kKT = 64;  // keys per tile
+
+// Workgroup geometry by head size: each wave takes CB blocks of 16 (token, head) columns of the
+// item's kPrefillCols (two at D <= 128; one at D = 256, where a second block's query and output
+// registers do not fit), so a workgroup has kPrefillCols / (16 CB) waves; each wave copies KPW
+// keys of every tile. Workgroups per CU follow from the LDS stages (64 KB, or 128 KB at 256).
+template <int D>
+struct PfShape {
+    static constexpr int CB = D == 256 ? 1 : 2;
+    static constexpr int COLS = 16 * CB;
+    static constexpr int WAVES = kPrefillCols / COLS;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int KPW = kKT / WAVES;
+    static constexpr int PER_CU = D == 256 ? 1 : 2;
+};
 
 // Key-row order inside a 32-key group: MFMA row m of 16-key half u holds key pkappa(u, m), so
 // that the S^T accumulator of lane (g16, n16) holds keys 8*g16 + 4u + i: 8*g16 .. 8*g16 + 7.
@@ -50,7 +61,7 @@ __device__ __forceinline__ int kmask(int r) {
 }
 template <int KC>
 __device__ __forceinline__ int vmask(int r) {
-    if (KC == 16) return 2 * ((r & 3) | ((r >> 1) & 4));          // 256-byte rows
+    if (KC >= 16) return 2 * ((r & 3) | ((r >> 1) & 4));          // rows of 256 bytes or more
     return 2 * (((r >> 1) & 1) | ((r >> 2) & 2));                 // 128-byte rows: two per bank line
 }
 
@@ -62,18 +73,19 @@ __device__ __forceinline__ void dma16(const half_t *src, half_t *dst) {
         (void __attribute__((address_space(3))) *)dst, 16, 0, 0);
 }
 
-// Cache block of this wave's keys kt + kPfKpw*wave .. + kPfKpw - 1 when they all lie before k1
-// in one block (block size a multiple of kPfKpw), else -1. Wave-uniform; read one tile ahead of
+// Cache block of this wave's keys kt + KPW*wave .. + KPW - 1 when they all lie before k1
+// in one block (block size a multiple of KPW), else -1. Wave-uniform; read one tile ahead of
 // the copies that use it, so that they do not wait on the table lookup.
+template <int KPW>
 __device__ __forceinline__ int pf_wave_block(const AttnArgs &a, const int32_t *bt, int kt, int k1,
                                              int wave) {
-    const int kw = kt + kPfKpw * wave;
-    if (a.bs % kPfKpw != 0 || kw + kPfKpw - 1 >= k1) return -1;
+    const int kw = kt + KPW * wave;
+    if (a.bs % KPW != 0 || kw + KPW - 1 >= k1) return -1;
     return bt[a.log2bs >= 0 ? (kw >> a.log2bs) : kw / a.bs];
 }
 
 // Issue this wave's share of the copies of the tile at kt into the stage (Kd, Vd): keys
-// kt + kPfKpw*wave .. + kPfKpw - 1 of K and of V; pb is pf_wave_block(kt). A copy instruction
+// kt + KPW*wave .. + KPW - 1 of K and of V; pb is pf_wave_block(kt). A copy instruction
 // moves RPI whole rows (lane l: row l / KC, chunk position l % KC). Keys past k1 - 1 copy key
 // k1 - 1 (masked later), so no table entry or row outside the sequence's range is read.
 template <int D>
@@ -82,13 +94,14 @@ __device__ __forceinline__ void pf_copy(const AttnArgs &a, const int32_t *bt, co
                                         half_t *Vd, int wave, int lane) {
     constexpr int KC = D / 8;          // 16-byte chunks per row
     constexpr int RPI = 64 / KC;       // rows per copy instruction
-    constexpr int IPW = kPfKpw / RPI;  // copy instructions per wave and matrix
+    constexpr int KPW = PfShape<D>::KPW;
+    constexpr int IPW = KPW / RPI;     // copy instructions per wave and matrix
     const int pos = lane % KC, rsub = lane / KC;
     const uint32_t ke = a.key_elems;  // < 2^24 (checked on the host): 24-bit multiplies
-    const int kw = kt + kPfKpw * wave;
+    const int kw = kt + KPW * wave;
     const int jw = a.log2bs >= 0 ? (kw >> a.log2bs) : kw / a.bs;
     for (int t = 0; t < IPW; ++t) {
-        const int r = kPfKpw * wave + t * RPI + rsub;  // row within the tile
+        const int r = KPW * wave + t * RPI + rsub;  // row within the tile
         size_t row;
         if (pb >= 0) {
             row = (size_t)pb * a.block_elems + __umul24(kt + r - jw * a.bs, ke);
@@ -97,7 +110,7 @@ __device__ __forceinline__ void pf_copy(const AttnArgs &a, const int32_t *bt, co
             const int j = a.log2bs >= 0 ? (key >> a.log2bs) : key / a.bs;
             row = (size_t)bt[j] * a.block_elems + __umul24(key - j * a.bs, ke);
         }
-        const int r0 = kPfKpw * wave + t * RPI;    // first row of this instruction
+        const int r0 = KPW * wave + t * RPI;    // first row of this instruction
         dma16(kcg + row + 8 * (pos ^ kmask<KC>(r)), Kd + r0 * D);
         dma16(vcg + row + 8 * (pos ^ vmask<KC>(r)), Vd + r0 * D);
     }
@@ -139,7 +152,7 @@ constexpr float kSlack = 8.f;
 // One launch, two roles by workgroup index:
 //  * workgroups [0, gridDim.x - pre_blocks) either merge the split decode partials (combine
 //    role, at most one per CU; the decode kernel ran in the launch before), or, with
-//    dec_blocks > 0, run the decode (decode role: decode_loop over dec with kPfWaves-wave
+//    dec_blocks > 0, run the decode (decode role: decode_loop over dec with 4-wave
 //    workgroups, each wave's 32-key K tile in the first LDS stage) beside the prefill;
 //  * the other pre_blocks run the persistent prefill loop; the first static_first of them take
 //    their first unit without the counter.
@@ -151,14 +164,17 @@ constexpr float kSlack = 8.f;
 // registers), then prefill workgroups that only take units from the counter, which run once
 // decode workgroups leave.
 template <int D>
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, CombineArgs cmb,
+__global__ __launch_bounds__(PfShape<D>::THREADS, PfShape<D>::PER_CU) void prefill_kernel(
+    AttnArgs a, CombineArgs cmb,
                                                                  int pre_blocks, AttnArgs dec,
                                                                  int dec_blocks,
                                                                  int static_first) {
     constexpr int KB = D / 32;           // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;          // 16-dim output tiles
     constexpr int KC = D / 8;
-    static_assert(kPfKpw * kPfWaves == kKT && kPfKpw % 8 == 0, "each wave copies whole rows");
+    constexpr int CB = PfShape<D>::CB, COLS = PfShape<D>::COLS, WAVES = PfShape<D>::WAVES;
+    constexpr int KPW = PfShape<D>::KPW;
+    static_assert(KPW * WAVES == kKT && KPW % 8 == 0, "each wave copies whole rows");
     // Two stages of row-major K and V tiles (64 KB at D = 128: two workgroups per CU).
     __shared__ __attribute__((aligned(16))) half_t Ks[2][kKT * D];
     __shared__ __attribute__((aligned(16))) half_t Vs[2][kKT * D];
@@ -166,16 +182,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
 
     if ((int)blockIdx.x < (int)gridDim.x - pre_blocks) {
         if (dec_blocks > 0) {
-            // decode role: dec.gw == kPfWaves waves, K tiles of 32 keys in the first stage
-            static_assert(kPfWaves * kTileKeys * D <= 2 * kKT * D, "decode K tiles fit Ks");
-            half_t *kl = &Ks[0][0] + (threadIdx.x >> 6) * (kTileKeys * D);
-            if (dec.log2bs >= 0)
-                decode_loop<D, 1, true, true>(dec, blockIdx.x, kl, &s_unit);
-            else
-                decode_loop<D, 1, false, true>(dec, blockIdx.x, kl, &s_unit);
+            // decode role: dec.gw == WAVES waves, K tiles of 32 keys in the first stage (only
+            // at D <= 128: the host never asks for it at 256)
+            if constexpr (WAVES * kTileKeys <= 2 * kKT) {
+                half_t *kl = &Ks[0][0] + (threadIdx.x >> 6) * (kTileKeys * D);
+                if (dec.log2bs >= 0)
+                    decode_loop<D, 1, true, true>(dec, blockIdx.x, kl, &s_unit);
+                else
+                    decode_loop<D, 1, false, true>(dec, blockIdx.x, kl, &s_unit);
+            }
             return;
         }
-        constexpr int kWg = kPfThreads / 64;
+        constexpr int kWg = WAVES;
         combine_dispatch<D>(cmb, 2, blockIdx.x * kWg + (threadIdx.x >> 6),
                         (gridDim.x - pre_blocks) * kWg);
         return;
@@ -206,13 +224,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
         const int ncols = ntok * a.Q;
 
         // Query operands and key limits of this lane's two columns 32*wave + 16*cb + n16.
-        half8_t q[2][KB];
-        int kend[2];
-        float m[2], l[2];
-        float4_t o[2][NDT];
+        half8_t q[CB][KB];
+        int kend[CB];
+        float m[CB], l[CB];
+        float4_t o[CB][NDT];
         int wave_end = 0, wave_min = 0x7fffffff;  // over the wave's live columns
-        for (int cb = 0; cb < 2; ++cb) {
-            const int col = 32 * wave + 16 * cb + n16;
+        for (int cb = 0; cb < CB; ++cb) {
+            const int col = COLS * wave + 16 * cb + n16;
             m[cb] = -INFINITY;
             l[cb] = 0.f;
             for (int dt = 0; dt < NDT; ++dt) o[cb][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -236,8 +254,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
         }
 
         const int32_t *bt = a.bt + (long long)it.b * a.MB;
-        const half_t *kcg = a.kc + (size_t)g * D;
-        const half_t *vcg = a.vc + (size_t)g * D;
+        const half_t *kcg = a.kc + (size_t)(g / a.kv_div) * D;  // physical kv head
+        const half_t *vcg = a.vc + (size_t)(g / a.kv_div) * D;
         const int k1 = it.k1;
         // Tile ti sits in stage ti & 1. At the top of each tile: wait for this wave's copies
         // (and, on the first tile, the query loads), one barrier (every wave's copies of tile ti
@@ -247,9 +265,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
         const int ntl = (k1 + kKT - 1) / kKT;
         int pbn = -1;  // pf_wave_block of the tile after the one whose copies are in flight
         if (ntl > 0) {
-            pf_copy<D>(a, bt, kcg, vcg, 0, k1, pf_wave_block(a, bt, 0, k1, wave), Ks[0], Vs[0],
+            pf_copy<D>(a, bt, kcg, vcg, 0, k1, pf_wave_block<KPW>(a, bt, 0, k1, wave), Ks[0], Vs[0],
                        wave, lane);
-            if (ntl > 1) pbn = pf_wave_block(a, bt, kKT, k1, wave);
+            if (ntl > 1) pbn = pf_wave_block<KPW>(a, bt, kKT, k1, wave);
         }
         for (int ti = 0; ti < ntl; ++ti) {
             const int kt = ti * kKT;
@@ -259,27 +277,28 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
             if (ti + 1 < ntl) {
                 pf_copy<D>(a, bt, kcg, vcg, kt + kKT, k1, pbn, Ks[(ti + 1) & 1], Vs[(ti + 1) & 1],
                            wave, lane);
-                pbn = ti + 2 < ntl ? pf_wave_block(a, bt, kt + 2 * kKT, k1, wave) : -1;
+                pbn = ti + 2 < ntl ? pf_wave_block<KPW>(a, bt, kt + 2 * kKT, k1, wave) : -1;
             }
             if (kt >= wave_end) continue;  // every column of this wave ends before the tile
 
-            // S^T: keys 32s + 8*g16 + 4u + i of columns n16 (both column blocks per K read).
-            float sc[2][2][2][4];
+            // S^T: keys 32s + 8*g16 + 4u + i of columns n16 (every column block per K read).
+            float sc[CB][2][2][4];
             // The score products run at raised wave priority: of the two waves sharing a SIMD,
             // the one in this phase keeps the matrix unit fed while the other runs its softmax.
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(1);
             for (int s = 0; s < 2; ++s)
                 for (int u = 0; u < 2; ++u) {
-                    float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                    float4_t acc[CB];
+                    for (int cb = 0; cb < CB; ++cb) acc[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
                     const int row = 32 * s + pkappa(u, n16);
                     for (int kb = 0; kb < KB; ++kb) {
                         const half8_t kr = *(const half8_t *)(
                             Kb + row * D + 8 * ((4 * kb + g16) ^ kmask<KC>(row)));
-                        acc[0] = mfma16x16x32(kr, q[0][kb], acc[0]);
-                        acc[1] = mfma16x16x32(kr, q[1][kb], acc[1]);
+                        for (int cb = 0; cb < CB; ++cb)
+                            acc[cb] = mfma16x16x32(kr, q[cb][kb], acc[cb]);
                     }
-                    for (int cb = 0; cb < 2; ++cb)
+                    for (int cb = 0; cb < CB; ++cb)
                         for (int i = 0; i < 4; ++i) sc[cb][s][u][i] = acc[cb][i];
                 }
             // Online softmax per column, P in fp16 as the B operand of O^T = V^T . P^T. Keys at or
@@ -288,14 +307,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(0);
             if (kt + kKT > wave_min)
-                for (int cb = 0; cb < 2; ++cb)
+                for (int cb = 0; cb < CB; ++cb)
                     for (int s = 0; s < 2; ++s)
                         for (int u = 0; u < 2; ++u)
                             for (int i = 0; i < 4; ++i)
                                 if (kt + 32 * s + 8 * g16 + 4 * u + i >= kend[cb])
                                     sc[cb][s][u][i] = -INFINITY;
-            half8_t pf[2][2];
-            for (int cb = 0; cb < 2; ++cb) {
+            half8_t pf[CB][2];
+            for (int cb = 0; cb < CB; ++cb) {
                 float mx = -INFINITY;
                 for (int s = 0; s < 2; ++s)
                     for (int u = 0; u < 2; ++u)
@@ -338,20 +357,23 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
                 const half8_t vb = va;
                 va = vbn;
                 if (x + 2 < 2 * NDT) vbn = vop((x + 2) / NDT, (x + 2) % NDT);
-                o[0][dt] = mfma16x16x32(vb, pf[0][s], o[0][dt]);
-                o[1][dt] = mfma16x16x32(vb, pf[1][s], o[1][dt]);
+                for (int cb = 0; cb < CB; ++cb)
+                    o[cb][dt] = mfma16x16x32(vb, pf[cb][s], o[cb][dt]);
             }
         }
 
-        // Output. Lane (g16, n16) holds dims 16*dt + 4*g16 .. +3 of its two columns; stored
-        // directly, each instruction would write 8 bytes into 16 columns. The wave's 32 columns
-        // go instead through its own part of the LDS stage the last tile did not use (every wave
-        // finished the tile before it at the last barrier; the next unit's first copies land
-        // only after the next unit's barriers), XOR-swizzled by column, and leave as whole
-        // columns: 64*16/(2D) columns per store instruction, a token's Q heads contiguous.
+        // Output. Lane (g16, n16) holds dims 16*dt + 4*g16 .. +3 of its columns; stored
+        // directly, each instruction would write 8 bytes into 16 columns. The wave's COLS
+        // columns go instead through its own part of the LDS stage the last tile did not use
+        // (every wave finished the tile before it at the last barrier; the next unit's first
+        // copies land only after the next unit's barriers; the waves' parts run through that
+        // stage's K then V tile), XOR-swizzled by column, and leave as whole columns:
+        // 64*16/(2D) columns per store instruction, a token's Q heads contiguous.
         constexpr int CPL = D / 8;  // 16-byte chunks per column
-        half_t *ost = (wave < 2 ? Ks[ntl & 1] : Vs[ntl & 1]) + (wave & 1) * 32 * D;
-        for (int cb = 0; cb < 2; ++cb) {
+        static_assert(WAVES * COLS * D <= 2 * kKT * D, "the output columns fit one stage");
+        const int ooff = wave * COLS * D;
+        half_t *ost = ooff < kKT * D ? Ks[ntl & 1] + ooff : Vs[ntl & 1] + (ooff - kKT * D);
+        for (int cb = 0; cb < CB; ++cb) {
             const float lt = col_sum(l[cb]);
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             const int lc = 16 * cb + n16;
@@ -364,10 +386,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(AttnArgs a, Comb
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 4
-        for (int j = 0; j < CPL / 2; ++j) {
+        for (int j = 0; j < COLS * CPL / 64; ++j) {
             const int lc = (64 / CPL) * j + lane / CPL, ch = lane % CPL;
             const half8_t v = *(const half8_t *)(ost + lc * D + 8 * (ch ^ (lc & (CPL - 1))));
-            const int col = 32 * wave + lc;
+            const int col = COLS * wave + lc;
             if (col < ncols) {
                 const int t = col / a.Q, qh = col - t * a.Q;
                 half_t *dst = a.out + (long long)(cu_b + it.t0 + t) * a.H * D +
@@ -389,18 +411,22 @@ pa_status launch_prefill(const AttnArgs &a, int D, int blocks, const CombineArgs
         c = *cmb;
         // At most one combine workgroup per CU: max_groups is a bound (every row split); the
         // waves loop when more rows are split than they cover in one pass.
+        const int waves = D == 256 ? PfShape<256>::WAVES : PfShape<128>::WAVES;
         comb_blocks = (int)std::min<long long>(
-            (combine_waves(max_groups, c.lanes, D) + kPfWaves - 1) / kPfWaves, device_cu_count());
+            (combine_waves(max_groups, c.lanes, D) + waves - 1) / waves, device_cu_count());
     }
     const int grid = blocks + comb_blocks;
     if (grid <= 0) return PA_OK;
     const AttnArgs none{};
-    if (D == 128)
-        scope.launch(prefill_kernel<128>, dim3(grid), dim3(kPfThreads), 0, a, c, blocks, none, 0,
-                     blocks);
+    if (D == 256)
+        scope.launch(prefill_kernel<256>, dim3(grid), dim3(PfShape<256>::THREADS), 0, a, c,
+                     blocks, none, 0, blocks);
+    else if (D == 128)
+        scope.launch(prefill_kernel<128>, dim3(grid), dim3(PfShape<128>::THREADS), 0, a, c,
+                     blocks, none, 0, blocks);
     else if (D == 64)
-        scope.launch(prefill_kernel<64>, dim3(grid), dim3(kPfThreads), 0, a, c, blocks, none, 0,
-                     blocks);
+        scope.launch(prefill_kernel<64>, dim3(grid), dim3(PfShape<64>::THREADS), 0, a, c, blocks,
+                     none, 0, blocks);
     else
         return PA_ERR_UNSUPPORTED;
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -409,16 +435,18 @@ pa_status launch_prefill(const AttnArgs &a, int D, int blocks, const CombineArgs
 pa_status launch_decode_prefill(const AttnArgs &dec, const AttnArgs &pre, int D, int dec_blocks,
                                 int pre_static, int pre_blocks, hipStream_t stream) {
     LaunchScope scope("decode_prefill", stream);
-    if (dec.gw != kPfWaves || pre_static > pre_blocks || dec_blocks < 0) return PA_ERR_UNSUPPORTED;
+    if ((D != 64 && D != 128) || dec.gw != PfShape<128>::WAVES || pre_static > pre_blocks ||
+        dec_blocks < 0)
+        return PA_ERR_UNSUPPORTED;
     const int grid = dec_blocks + pre_blocks;
     if (grid <= 0) return PA_OK;
     const CombineArgs c{};
     if (D == 128)
-        scope.launch(prefill_kernel<128>, dim3(grid), dim3(kPfThreads), 0, pre, c, pre_blocks, dec,
-                     dec_blocks, pre_static);
+        scope.launch(prefill_kernel<128>, dim3(grid), dim3(PfShape<128>::THREADS), 0, pre, c,
+                     pre_blocks, dec, dec_blocks, pre_static);
     else if (D == 64)
-        scope.launch(prefill_kernel<64>, dim3(grid), dim3(kPfThreads), 0, pre, c, pre_blocks, dec,
-                     dec_blocks, pre_static);
+        scope.launch(prefill_kernel<64>, dim3(grid), dim3(PfShape<64>::THREADS), 0, pre, c,
+                     pre_blocks, dec, dec_blocks, pre_static);
     else
         return PA_ERR_UNSUPPORTED;
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;

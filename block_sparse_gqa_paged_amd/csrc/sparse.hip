@@ -221,7 +221,8 @@ __global__ __launch_bounds__(256) void sp_qsplit(SparseArgs a, SparseWs w, long 
 }
 
 template <int D, int NT>
-__global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(SparseArgs a, SparseWs w) {
+__global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void sp_main(
+    SparseArgs a, SparseWs w) {
     constexpr int BSP = 16 * NT;             // padded keys per block (NT even)
     constexpr int KB = D / 32;               // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;              // 16-dim output tiles
@@ -380,45 +381,51 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
     }
     __syncthreads();
 
-    // ---- edge groups: 16 query rows (16 / qhead edges) per wave at a time. Lane (g16, n16)
-    // serves query row n16 throughout.
+    // ---- edge groups. The item's rows are its (edge, q-head lane) pairs, row r = edge
+    // r / qhead, lane r mod qhead; a wave takes 16 consecutive rows at a time (16 / qhead whole
+    // edges when qhead divides 16). Lane (g16, n16) serves row n16 of the group.
     const int g16 = lane >> 4, n16 = lane & 15;
-    const int epg = 16 / a.qhead;
-    const int rows = epg * a.qhead;
+    const int nrows = nE * a.qhead;
     const int hq = a.hkv * a.qhead;
-    const int el = n16 / a.qhead, qh = n16 - el * a.qhead;
-    // The next group's query operands are loaded at the start of this group, and the one wait
-    // for them sits right before this group's stores. A wait for a load while stores are
-    // outstanding has to drain the stores too (loads and stores share the counter and may
-    // complete out of order), so without this the next group's first use of its query would
-    // wait for this group's partial stores to reach memory.
+    // With D <= 128 the next group's query operands are loaded at the start of this group, and
+    // the one wait for them sits right before this group's stores. A wait for a load while
+    // stores are outstanding has to drain the stores too (loads and stores share the counter
+    // and may complete out of order), so without this the next group's first use of its query
+    // would wait for this group's partial stores to reach memory. At D = 256 the second set of
+    // query registers does not fit: each group loads its own rows at its start.
+    constexpr bool kPrefetchQ = D <= 128;
     half8_t nqhi[KB], nqlo[KB];
     float nqmul = 0.f;
     auto load_q = [&](int grp) {
-        const int idx = grp * epg + el;
-        const int ix = (n16 < rows && idx < nE) ? idx : 0;
-        const long long qrow = (long long)s_q[ix] * hq + h * a.qhead + qh;
+        const int r = 16 * grp + n16;
+        const int ix = r < nrows ? r / a.qhead : 0;
+        const long long qrow = (long long)s_q[ix] * hq + h * a.qhead + (r % a.qhead);
         for (int kb = 0; kb < KB; ++kb) {
             nqhi[kb] = gload<half8_t>(w.qhi + qrow * D + 32 * kb + 8 * g16);
             nqlo[kb] = gload<half8_t>(w.qlo + qrow * D + 32 * kb + 8 * g16);
         }
         nqmul = gload<float>(w.qmul + qrow);
     };
-    if (wave * epg < nE) load_q(wave);
+    if (kPrefetchQ && 16 * wave < nrows) load_q(wave);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    for (int grp = wave; grp * epg < nE; grp += NW) {
-        const int idx = grp * epg + el;
-        const bool vrow = n16 < rows && idx < nE;
-        const int ix = vrow ? idx : 0;  // rows without an edge read edge 0's query, then drop it
+    for (int grp = wave; 16 * grp < nrows; grp += NW) {
+        const int row = 16 * grp + n16;
+        const bool vrow = row < nrows;
+        const int ix = vrow ? row / a.qhead : 0;  // rows past the item read edge 0, then drop it
+        const int qh = row % a.qhead;
         const int e = s_e[ix];
         const int len = vrow ? s_len[ix] : 0;
+        if (!kPrefetchQ) {
+            load_q(grp);
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        }
         half8_t qhi[KB], qlo[KB];
         for (int kb = 0; kb < KB; ++kb) {
             qhi[kb] = nqhi[kb];
             qlo[kb] = nqlo[kb];
         }
         const float mult = ldexpf(nqmul, eK);
-        if ((grp + NW) * epg < nE) load_q(grp + NW);
+        if (kPrefetchQ && 16 * (grp + NW) < nrows) load_q(grp + NW);
         // keys this lane scores (16j + 4g16 + i) that are mapped and below the edge's length
         uint64_t lm[MW];
         for (int hw = 0; hw < MW; ++hw) {
@@ -497,10 +504,10 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512) ? 4 : 2) void sp_main(Spa
             a.l[p] = ls;
         }
         for (int h = 0; h < 2; ++h) {
-            const int r = 8 * h + (lane >> 3);  // the group row this lane stores
-            const int ridx = grp * epg + r / a.qhead;
-            const bool rvalid = r < rows && ridx < nE;
-            const long long pr = (long long)s_e[rvalid ? ridx : 0] * a.qhead + r % a.qhead;
+            const int r = 16 * grp + 8 * h + (lane >> 3);  // the item row this lane stores
+            const bool rvalid = r < nrows;
+            const long long pr =
+                (long long)s_e[rvalid ? r / a.qhead : 0] * a.qhead + r % a.qhead;
             float *dst = a.o + pr * D + 4 * (lane & 7);
             for (int j = 0; j < NDT / 2; ++j) {
                 // slab row r (128 bytes) holds its 16-byte chunk c at c ^ ((r >> 1) & 3): the
@@ -546,7 +553,10 @@ pa_status launch_sparse(const SparseArgs &a, hipStream_t stream) {
     const size_t lds = (size_t)4 * 16 * nt * a.D * sizeof(half_t) + (kThreads / 64) * 1024;
     // dynamic LDS plus the kernel's static arrays (edge list, maxima, per-dimension V scales:
     // 2.6 KB at D = 128)
-    if (lds + 4096 > sparse_lds_limit() || (a.D != 64 && a.D != 128)) return PA_ERR_UNSUPPORTED;
+    // (at D = 256 the planes of a 128-key block exceed the LDS: blocks of up to 64 keys)
+    if (lds + 4096 > sparse_lds_limit() || (a.D != 64 && a.D != 128 && a.D != 256) ||
+        (a.D == 256 && nt > 4))
+        return PA_ERR_UNSUPPORTED;
     const long long qrows = (long long)a.tq * a.hkv * a.qhead;
     LaunchScope scope("sparse_forward", stream, qrows > 0 ? 6 : 5);
     SparseWs w;
@@ -554,7 +564,8 @@ pa_status launch_sparse(const SparseArgs &a, hipStream_t stream) {
     if (qrows > 0) {
         const long long thr = qrows * (a.D / 8);
         const unsigned grid = (unsigned)((thr + 255) / 256);
-        if (a.D == 128) scope.launch(sp_qsplit<128>, dim3(grid), dim3(256), 0, a, w, qrows);
+        if (a.D == 256) scope.launch(sp_qsplit<256>, dim3(grid), dim3(256), 0, a, w, qrows);
+        else if (a.D == 128) scope.launch(sp_qsplit<128>, dim3(grid), dim3(256), 0, a, w, qrows);
         else scope.launch(sp_qsplit<64>, dim3(grid), dim3(256), 0, a, w, qrows);
     }
     scope.launch(sp_zero, dim3((a.units + 255) / 256), dim3(256), 0, w.counts, a.units);
@@ -564,7 +575,10 @@ pa_status launch_sparse(const SparseArgs &a, hipStream_t stream) {
     scope.launch(sp_scatter, dim3(eg), dim3(256), 0, a, w);
 #define PA_SP_LAUNCH(DD, NN) \
     scope.launch(sp_main<DD, NN>, dim3(w.max_items), dim3(kThreads), (uint32_t)lds, a, w)
-    if (a.D == 128) {
+    if (a.D == 256) {
+        if (nt == 2) PA_SP_LAUNCH(256, 2);
+        else PA_SP_LAUNCH(256, 4);
+    } else if (a.D == 128) {
         if (nt == 2) PA_SP_LAUNCH(128, 2);
         else if (nt == 4) PA_SP_LAUNCH(128, 4);
         else PA_SP_LAUNCH(128, 8);

@@ -78,7 +78,7 @@ typedef struct pa_paged_shape {
     int32_t num_tokens;   /* T  >= 0: rows of query (all sequences' new tokens, concatenated) */
     int32_t num_heads;    /* H  > 0                                                           */
     int32_t kv_num_heads; /* G  > 0, H % G == 0; query head h reads kv head h / (H / G)        */
-    int32_t head_size;    /* D  in {64, 128}                                                  */
+    int32_t head_size;    /* D  in {64, 128, 256}                                             */
     int32_t num_blocks;   /* NB >= 1: dim0 of key_cache and value_cache                       */
     int32_t block_size;   /* bs >= 1: tokens per cache block                                  */
     int32_t max_blocks;   /* MB >= 1: block_table row length                                  */
@@ -115,7 +115,7 @@ typedef struct pa_paged_shape {
  *
  * Rotary arithmetic: two float32 products (each rounded), one float32 add or subtract, then
  * round-to-nearest-even to fp16; the first member of a pair subtracts its partner's sine term.
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (D not 64/128, H/G > 64, G*D >= 2^24,
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (D not 64/128/256, G*D >= 2^24,
  * bs*G*D >= 2^32: the shape limits every paged entry shares), PA_ERR_HIP.
  */
 pa_status pa_kv_append(const pa_paged_shape *shape, const void *query, const void *key,
@@ -181,10 +181,11 @@ size_t pa_paged_attention_workspace_size(const pa_paged_shape *shape, int32_t nu
  *   workspace, workspace_bytes  device scratch of at least
  *            pa_paged_attention_workspace_size(shape, num_splits) bytes, 256-byte aligned
  *   output   fp16 [T, H*D]
- * Rows of a sequence with n_b * (H/G) <= 16 (<= 32 or 64 for H/G above 16 or 32) are
- * decode-like and split-KV eligible; longer sequences run on the chunked-prefill path as items
- * of 128 (token, head) columns (128 / (H/G) tokens of one kv head group), each covering its
- * causal key range in one pass.
+ * Rows of a sequence with n_b * Qg <= 16 (<= 32 or 64 for Qg above 16 or 32) are decode-like
+ * and split-KV eligible; longer sequences run on the chunked-prefill path as items of 128
+ * (token, head) columns (128 / Qg tokens of one head group), each covering its causal key range
+ * in one pass. Qg = H/G, except that a kv head with more than 64 query heads (more than 16 at
+ * D = 256) is served as several groups of at most Qg = 16 heads that read the same cache head.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (the shape limits of pa_kv_append),
  * PA_ERR_WORKSPACE, PA_ERR_HIP.
  */
@@ -264,8 +265,8 @@ pa_status pa_append_attention(const pa_paged_shape *shape, const void *query, co
  *   out[r][d] = sum w o_p[d] / sum w l_p, or 0 when no unit has l_p > 0.
  *   out_dtype PA_F16 (round to nearest even) or PA_F32; out is [num_groups*lanes, head_dim].
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_groups < 0, lanes < 1, head_dim not a positive
- * multiple of 4, num_splits < 1 without group_ptr), PA_ERR_UNSUPPORTED (head_dim not 64 or
- * 128), PA_ERR_HIP.
+ * multiple of 4, num_splits < 1 without group_ptr), PA_ERR_UNSUPPORTED (head_dim not 64, 128
+ * or 256), PA_ERR_HIP.
  */
 pa_status pa_split_combine(const float *o_partial, const float *m_partial,
                            const float *l_partial, const int32_t *group_ptr, int32_t num_groups,
@@ -282,8 +283,9 @@ typedef struct pa_sparse_shape {
     int32_t tq;         /* rows of q_buf                                              */
     int32_t hkv;        /* kv heads                                                   */
     int32_t qhead;      /* query heads per kv head (the q-head lanes of an edge)      */
-    int32_t head_dim;   /* D in {64, 128}                                             */
-    int32_t block_size; /* keys per sparse block, multiple of page_size, <= 128       */
+    int32_t head_dim;   /* D in {64, 128, 256}                                        */
+    int32_t block_size; /* keys per sparse block, multiple of page_size, <= 128 (<= 64
+                           at D = 256)                                                */
     int32_t page_size;  /* keys per page                                              */
     int32_t num_pages;  /* dim0 of k_pages / v_pages                                  */
     int32_t max_pages;  /* block_tables row length                                    */
@@ -312,8 +314,8 @@ size_t pa_sparse_forward_workspace_size(const pa_sparse_shape *shape);
  *   workspace  at least pa_sparse_forward_workspace_size(shape) bytes, 256-byte aligned
  * Edges may come in any order; the kernel groups them by (batch, h, blk) so each block of keys
  * is read once per group. Merge the partials with pa_split_combine.
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (causal != 0, D not 64/128,
- * block_size > 128), PA_ERR_WORKSPACE, PA_ERR_HIP.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (causal != 0, D not 64/128/256,
+ * block_size > 128, or > 64 at D = 256), PA_ERR_WORKSPACE, PA_ERR_HIP.
  */
 pa_status pa_sparse_forward(const pa_sparse_shape *shape, const float *q_buf,
                             const float *k_pages, const float *v_pages,
@@ -380,7 +382,7 @@ typedef struct pa_bnsh_shape {
     int32_t seq_len;        /* S: new tokens per sequence (padded), >= 0                 */
     int32_t num_heads;      /* H (packed rows carry H query heads first)                 */
     int32_t kv_num_heads;   /* KVH, H % KVH == 0                                         */
-    int32_t head_size;      /* D in {64, 128}                                            */
+    int32_t head_size;      /* D in {64, 128, 256}                                       */
     int32_t max_cache_seq;  /* positions per (batch, kv head) in the cache               */
     int32_t packed_qkv;     /* 1: query rows are [Q|K|V], key/value == NULL              */
 } pa_bnsh_shape;
@@ -399,7 +401,7 @@ typedef struct pa_bnsh_shape {
  *   cos_cache, sin_cache, rotary_dim, rotary_mode, rotary_positions: as pa_kv_append
  * A row whose position is >= max_cache_seq (or >= rotary_positions with rotary on) is not
  * written (the page leaves the bound to its caller).
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (D not 64/128), PA_ERR_HIP.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (D not 64/128/256), PA_ERR_HIP.
  */
 pa_status pa_kv_append_bnsh(const pa_bnsh_shape *shape, const void *query, const void *key,
                             const void *value, void *present_key, void *present_value,

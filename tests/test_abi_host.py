@@ -52,7 +52,7 @@ def _append(shape, **kw):
     (dict(num_blocks=0), pa.PA_ERR_SHAPE),
     (dict(num_tokens=-1), pa.PA_ERR_SHAPE),
     (dict(head_size=96), pa.PA_ERR_UNSUPPORTED),
-    (dict(num_heads=128, kv_num_heads=1), pa.PA_ERR_UNSUPPORTED),  # qPerKv > 64
+    (dict(head_size=512), pa.PA_ERR_UNSUPPORTED),
     # a block's elements must fit in 32 bits (24-bit in-block offset products)
     (dict(num_heads=64, kv_num_heads=64, head_size=128, block_size=1 << 19),
      pa.PA_ERR_UNSUPPORTED),
@@ -115,7 +115,7 @@ def test_attention_rejects_bad_arguments():
     assert _attn(_shape(), num_splits=-2) == pa.PA_ERR_SHAPE
     assert _attn(_shape(), block_table=None) == pa.PA_ERR_NULL
     assert _attn(_shape(), output=None) == pa.PA_ERR_NULL
-    assert _attn(_shape(head_size=256)) == pa.PA_ERR_UNSUPPORTED
+    assert _attn(_shape(head_size=512)) == pa.PA_ERR_UNSUPPORTED
     assert _attn(_shape(), workspace_bytes=16) == pa.PA_ERR_WORKSPACE
     n = pa.pa_paged_attention_workspace_size(_shape())
     assert _attn(_shape(), workspace=FAKE + 4, workspace_bytes=n) == pa.PA_ERR_WORKSPACE
@@ -235,7 +235,8 @@ def test_sparse_rejects_bad_arguments():
     assert fwd(sh(), causal=1) == pa.PA_ERR_UNSUPPORTED     # right-aligned causal unimplemented
     assert fwd(sh(block_size=60)) == pa.PA_ERR_SHAPE          # not a multiple of page_size
     assert fwd(sh(block_size=256)) == pa.PA_ERR_UNSUPPORTED
-    assert fwd(sh(qhead=32)) == pa.PA_ERR_UNSUPPORTED
+    assert fwd(sh(head_dim=256, block_size=128)) == pa.PA_ERR_UNSUPPORTED  # planes beyond LDS
+    assert fwd(sh(qhead=32), workspace_bytes=8) == pa.PA_ERR_WORKSPACE   # any qhead: checked on
     assert fwd(sh(head_dim=80)) == pa.PA_ERR_UNSUPPORTED
     assert fwd(sh(), edge_meta=None) == pa.PA_ERR_NULL
     assert fwd(sh(), workspace_bytes=8) == pa.PA_ERR_WORKSPACE

@@ -100,6 +100,49 @@ def test_prefill_family(case):
     assert_attention_close(out, ref, "prefill")
 
 
+# Head size 256 and query-head groups above 64 (a kv head with Q > 64, or Q > 16 at D = 256, is
+# served as groups of at most 16 query heads that read the same cache head).
+WIDE_SHAPES = [
+    dict(seed=190, past=[37, 300, 1000], n_new=[1, 1, 1], num_heads=8, kv_num_heads=2,
+         head_size=256, block_size=16),                               # decode, Q = 4
+    dict(seed=191, past=[0, 150], n_new=[70, 9], num_heads=8, kv_num_heads=8, head_size=256,
+         block_size=32),                                              # prefill, Q = 1
+    dict(seed=192, past=[100, 12], n_new=[3, 40], num_heads=16, kv_num_heads=2, head_size=256,
+         block_size=16, packed=True, rotary_mode=W.ROTARY_NEOX, rotary_dim=256,
+         rotary_positions=256),                                       # packed, NeoX on all dims
+    dict(seed=193, past=[45, 7], n_new=[2, 33], num_heads=32, kv_num_heads=1, head_size=256,
+         block_size=8, rotary_mode=W.ROTARY_INTERLEAVED, rotary_dim=64,
+         rotary_positions=128),                                       # Q = 32 -> 2 groups of 16
+    dict(seed=194, past=[50], n_new=[20], num_heads=4, kv_num_heads=4, head_size=256,
+         block_size=24, causal=0),                                    # bs not a power of two
+    dict(seed=195, past=[130, 600], n_new=[1, 1], num_heads=128, kv_num_heads=1,
+         head_size=128, block_size=16),                               # decode, Q = 128
+    dict(seed=196, past=[40, 0], n_new=[3, 9], num_heads=128, kv_num_heads=1, head_size=64,
+         block_size=16),                                              # prefill, Q = 128
+    dict(seed=197, past=[70], n_new=[5], num_heads=256, kv_num_heads=2, head_size=128,
+         block_size=32, causal=0),                                    # Q = 128, two kv heads
+    dict(seed=198, past=[20, 200], n_new=[1, 1], num_heads=96, kv_num_heads=1, head_size=64,
+         block_size=16),                                              # Q = 96 -> 6 groups of 16
+]
+
+
+@pytest.mark.parametrize("case", WIDE_SHAPES, ids=lambda c: str(c["seed"]))
+@pytest.mark.parametrize("num_splits", [pa.PA_SPLITS_AUTO, pa.PA_SPLITS_PAGE_RULE, 3],
+                         ids=lambda s: f"S{s}")
+def test_wide_shapes(case, num_splits):
+    case = dict(case)
+    w = W.paged_workload(case.pop("seed"), table="pool", slack=0.2, name="wide", **case)
+    kc, vc, ref = _oracle(w)
+    c, out = _run(w, num_splits)
+    assert_bits_equal(c.key_cache, kc, "key_cache")
+    assert_bits_equal(c.value_cache, vc, "value_cache")
+    assert_attention_close(out, ref, f"wide S={num_splits}")
+    c1 = dev.PagedCase(w)
+    out1 = c1.append_attention(num_splits)
+    torch.cuda.synchronize()
+    assert_bits_equal(out1, out, "one-call step")
+
+
 # Prefill rows whose scores rise by more than 2^8 after the first 64-key tile: the kernel's
 # lazily raised maximum rescales O and l (the CPU suite shows the raise occurs in most of these
 # columns and that a wrong rescale would exceed the bar).
@@ -136,6 +179,9 @@ QROT = [
          rotary_positions=64),                                        # element-wise, interleaved
     dict(seed=136, past=[12, 0], n_new=[3, 5], num_heads=8, kv_num_heads=2, head_size=128,
          block_size=16, packed=True),                                 # no rotary: copies
+    dict(seed=138, past=[5, 17], n_new=[6, 2], num_heads=8, kv_num_heads=2, head_size=256,
+         block_size=16, packed=True, rotary_mode=W.ROTARY_NEOX, rotary_dim=256,
+         rotary_positions=64),                                        # D = 256
 ]
 
 
@@ -201,6 +247,8 @@ BNSH = [
     dict(seed=145, batch=2, seq_len=9, num_heads=4, kv_num_heads=2, head_size=64, max_seq=40,
          key_total=[20, 35], rotary_mode=W.ROTARY_INTERLEAVED, rotary_dim=36,
          rotary_positions=30),                                       # rows past the table
+    dict(seed=146, batch=2, seq_len=7, num_heads=8, kv_num_heads=4, head_size=256, max_seq=32,
+         key_total=[12, 30], rotary_mode=W.ROTARY_NEOX),              # D = 256
 ]
 
 
@@ -511,7 +559,7 @@ def test_combine_uniform_splits(S, out_dtype):
         assert np.allclose(g, ref, rtol=1e-5, atol=1e-6)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("lanes", [1, 3, 5, 7, 12, 33])
 @pytest.mark.parametrize("uniform", [0, 3], ids=["csr", "uniform3"])
 def test_combine_row_blocks(D, lanes, uniform):

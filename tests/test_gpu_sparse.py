@@ -37,6 +37,12 @@ TINY = [
     dict(seed=206, Tq=600, hkv=1, qhead=2, key_capacity=256, window=3, p_random=0.5),
     # one edge per 16-row group
     dict(seed=207, qhead=16, hkv=1, head_dim=64, block_size=32, page_size=8),
+    # head dim 256 (blocks of up to 64 keys)
+    dict(seed=208, head_dim=256, block_size=64, page_size=16),
+    dict(seed=209, head_dim=256, block_size=32, page_size=8, qhead=2),
+    # q-head lanes beyond one 16-row group: an edge's rows span groups
+    dict(seed=212, qhead=32, hkv=1, head_dim=64, block_size=32, page_size=8),
+    dict(seed=213, qhead=24, hkv=2, head_dim=128),
 ]
 
 
@@ -85,6 +91,7 @@ WIDE = [
          outliers=(2, 1000.0, 100.0), tiny=(0.1, 1e-5)),
     dict(seed=224, qhead=8, block_size=128, page_size=32, outliers=(4, 300.0, 1000.0),
          tiny=(0.05, 1e-5), key_capacity=1024),
+    dict(seed=225, head_dim=256, outliers=(3, 1000.0, 1000.0), tiny=(0.1, 1e-5)),
 ]
 
 
