@@ -46,8 +46,11 @@ def parse():
 # Sources that shape each profiled launch (its kernel code, the structs it reads and the host code
 # that sizes its grid). A counter reading stays valid only while these files are unchanged.
 KERNEL_SOURCES = {
-    "attn_decode": ("attention.hip", "plan.h", "common.h", "api.hip"),
-    "prefill_combine": ("prefill.hip", "combine_rows.h", "plan.h", "common.h", "api.hip"),
+    "attn_decode": ("attention.hip", "decode_unit.h", "plan.h", "common.h", "api.hip"),
+    "prefill_combine": ("prefill.hip", "decode_unit.h", "combine_rows.h", "plan.h", "common.h",
+                        "api.hip"),
+    "decode_prefill": ("prefill.hip", "decode_unit.h", "combine_rows.h", "plan.h", "common.h",
+                       "api.hip"),
     "append_plan": ("kv_append.hip", "plan.h", "common.h", "api.hip"),
     "kv_append": ("kv_append.hip", "common.h", "api.hip"),
     "plan": ("attention.hip", "plan.h", "common.h", "api.hip"),
@@ -350,7 +353,7 @@ def run_extra(args, torch, np, pa, dev, W):
     ms, _ = timed(lambda: (c.append(), c.attention(pa.PA_SPLITS_AUTO)), steps, 0, torch)
     pa.pa_timing_enable(False)
     kt = {k: pa.pa_timing_get(k) for k in ("kv_append", "plan", "attn_decode", "prefill_combine",
-                                           "combine")}
+                                           "decode_prefill", "combine")}
     pa.pa_timing_reset()
     ms_one, _ = timed(lambda: c.append_attention(pa.PA_SPLITS_AUTO), steps, wu, torch, WARM_MS)
     us = {k: round(v[0] / max(1, v[1]) * 1e3, 2) for k, v in kt.items() if v[1]}
@@ -362,14 +365,29 @@ def run_extra(args, torch, np, pa, dev, W):
         if n[b] > 1:
             keys = L[b] + np.arange(1, n[b] + 1)
             flops += int(keys.sum()) * w["H"] * w["D"] * 4
+    # The decode and prefill items of this call share one launch; the prefill alone is timed on
+    # the same 8 prefill sequences without the decode rows (the same prefill items, the whole
+    # machine to themselves).
+    wp = W.mixed_prefill_decode(n_decode=0)
+    cp = dev.PagedCase(wp)
+    warm(lambda: (cp.append(), cp.attention(pa.PA_SPLITS_AUTO)))
+    pa.pa_timing_reset()
+    pa.pa_timing_enable(True)
+    timed(lambda: cp.attention(pa.PA_SPLITS_AUTO), steps, 0, torch)
+    pa.pa_timing_enable(False)
+    t_pre = pa.pa_timing_get("decode_prefill")
+    pa.pa_timing_reset()
+    us_pre = t_pre[0] / max(1, t_pre[1]) * 1e3
+    del cp
     app_bytes = w["T"] * w["G"] * w["D"] * 2 * 4 + w["T"] * (w["rotary_dim"] // 2) * 2 * 2
     out["mixed_prefill_decode"] = {
         "workload": w["name"], "ms_per_step": round(ms, 4),
         "one_call_ms_per_step": round(ms_one, 4), "kernel_us": us,
         "kv_bytes": kv, "step_kv_GBps": round(kv / (ms * 1e-3) / 1e9, 1),
-        "prefill_TFLOPs": round(flops / (us.get("prefill_combine", 1e9) * 1e-6) / 1e12, 2),
-        "prefill_mfma_frac": round(flops / (us.get("prefill_combine", 1e9) * 1e-6) / 1e12
-                                   / MFMA_F16_PEAK_TFS, 4),
+        "prefill_alone_us": round(us_pre, 2),
+        "prefill_TFLOPs": round(flops / (us_pre * 1e-6) / 1e12, 2),
+        "prefill_mfma_frac": round(flops / (us_pre * 1e-6) / 1e12 / MFMA_F16_PEAK_TFS, 4),
+        "prefill_flops": flops,
         "append_GBps": round(app_bytes / (us.get("kv_append", 1e9) * 1e-6) / 1e9, 1),
         "append_pct_hbm": round(100 * app_bytes / (us.get("kv_append", 1e9) * 1e-6) / 1e9
                                 / HBM_PEAK_GBS, 2),

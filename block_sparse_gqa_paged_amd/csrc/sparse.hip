@@ -26,8 +26,10 @@
 //    dims of one query row for its stores. K (row-major) and V (transposed, keys ordered so
 //    that one 16-byte read is one operand) live in LDS as fp16 hi/lo planes with XOR-swizzled
 //    chunks.
-//  * The query rows are scaled and split once, in a pass of their own, into workspace planes;
-//    an edge reads its rows ready for the MFMA, and the item's edge list sits in LDS.
+//  * Each group of 16 (edge, lane) rows loads its fp32 query rows and scales and splits them in
+//    registers (a row's exponent from the maximum over the 4 lanes that hold it); the item's
+//    edge list sits in LDS. A separate pass writing split query planes would move the same bytes
+//    per row plus its own 200 MB and launch.
 //
 // Edges whose batch, head, block or query index lie outside the shapes write the sentinel.
 // With q_pos (the causal entry), an edge sees only keys at positions <= q_pos[q_idx]: its length
@@ -42,17 +44,15 @@ constexpr int kThreads = 512;  // 8 waves
 
 struct SparseWs {
     int32_t *counts, *rank, *offs, *ioffs, *nitems, *item_unit, *perm;
-    float *qmul;        // per query row: scale_log2 * 2^eQ
-    half_t *qhi, *qlo;  // query rows times 2^-eQ, split into fp16 planes [tq * hq, D]
     int max_items;
 };
 
 size_t al(size_t x) { return (x + 63) / 64 * 64; }  // in int32 words (256 bytes)
 
 // Workspace layout in int32 words; returns the total.
-size_t layout(SparseWs *w, int32_t *ws, int E, int units, long long qrows, int D) {
+size_t layout(SparseWs *w, int32_t *ws, int E, int units) {
     const size_t max_items = (size_t)(E + kChunk - 1) / kChunk + units;
-    size_t off = 0, o[10];
+    size_t off = 0, o[7];
     o[0] = off; off = al(off + units);             // counts
     o[1] = off; off = al(off + E);                 // rank
     o[2] = off; off = al(off + units + 1);         // offs
@@ -60,15 +60,9 @@ size_t layout(SparseWs *w, int32_t *ws, int E, int units, long long qrows, int D
     o[4] = off; off = al(off + 1);                 // nitems
     o[5] = off; off = al(off + max_items);         // item_unit
     o[6] = off; off = al(off + E);                 // perm
-    o[7] = off; off = al(off + qrows);             // qmul
-    o[8] = off; off = al(off + qrows * D / 2);     // qhi
-    o[9] = off; off = al(off + qrows * D / 2);     // qlo
     if (w) {
         w->counts = ws + o[0]; w->rank = ws + o[1]; w->offs = ws + o[2]; w->ioffs = ws + o[3];
         w->nitems = ws + o[4]; w->item_unit = ws + o[5]; w->perm = ws + o[6];
-        w->qmul = (float *)(ws + o[7]);
-        w->qhi = (half_t *)(ws + o[8]);
-        w->qlo = (half_t *)(ws + o[9]);
         w->max_items = (int)max_items;
     }
     return off;
@@ -110,42 +104,44 @@ __global__ void sp_hist(SparseArgs a, SparseWs w) {
     }
 }
 
-// One workgroup: exclusive scans of edge counts and of work-item counts, and the item map.
+// One workgroup: exclusive scans of edge counts and of work-item counts, and the item map. Each
+// thread takes a contiguous run of units: it sums its run, one workgroup-wide scan of the run
+// sums gives the run's offsets, and the thread then writes its units' offsets and item entries.
 __global__ __launch_bounds__(1024) void sp_scan(SparseArgs a, SparseWs w) {
     __shared__ int sh[2][16];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    int carry_e = 0, carry_i = 0;
-    for (int base = 0; base < a.units; base += 1024) {
-        const int u = base + tid;
-        const int c = u < a.units ? w.counts[u] : 0;
-        const int ni = (c + kChunk - 1) / kChunk;
-        int xe = c, xi = ni;
-        for (int o = 1; o < 64; o <<= 1) {
-            const int ye = __shfl_up(xe, o, 64), yi = __shfl_up(xi, o, 64);
-            if (lane >= o) { xe += ye; xi += yi; }
-        }
-        __syncthreads();
-        if (lane == 63) { sh[0][wid] = xe; sh[1][wid] = xi; }
-        __syncthreads();
-        int be = 0, bi = 0, te = 0, ti = 0;
-        for (int i = 0; i < 16; ++i) {
-            if (i < wid) { be += sh[0][i]; bi += sh[1][i]; }
-            te += sh[0][i]; ti += sh[1][i];
-        }
-        if (u < a.units) {
-            const int oe = carry_e + be + xe - c;
-            const int oi = carry_i + bi + xi - ni;
-            w.offs[u] = oe;
-            w.ioffs[u] = oi;
-            for (int k = 0; k < ni; ++k) w.item_unit[oi + k] = u;
-        }
-        carry_e += te;
-        carry_i += ti;
+    const int per = (a.units + 1023) / 1024;
+    const int u0 = min(a.units, tid * per), u1 = min(a.units, u0 + per);
+    int se = 0, si = 0;
+    for (int u = u0; u < u1; ++u) {
+        const int c = w.counts[u];
+        se += c;
+        si += (c + kChunk - 1) / kChunk;
+    }
+    int xe = se, xi = si;  // inclusive scans within the wave
+    for (int o = 1; o < 64; o <<= 1) {
+        const int ye = __shfl_up(xe, o, 64), yi = __shfl_up(xi, o, 64);
+        if (lane >= o) { xe += ye; xi += yi; }
+    }
+    if (lane == 63) { sh[0][wid] = xe; sh[1][wid] = xi; }
+    __syncthreads();
+    int oe = xe - se, oi = xi - si, te = 0, ti = 0;
+    for (int i = 0; i < 16; ++i) {
+        if (i < wid) { oe += sh[0][i]; oi += sh[1][i]; }
+        te += sh[0][i]; ti += sh[1][i];
+    }
+    for (int u = u0; u < u1; ++u) {
+        const int c = w.counts[u], ni = (c + kChunk - 1) / kChunk;
+        w.offs[u] = oe;
+        w.ioffs[u] = oi;
+        for (int k = 0; k < ni; ++k) w.item_unit[oi + k] = u;
+        oe += c;
+        oi += ni;
     }
     if (tid == 0) {
-        w.offs[a.units] = carry_e;
-        w.ioffs[a.units] = carry_i;
-        w.nitems[0] = carry_i;
+        w.offs[a.units] = te;
+        w.ioffs[a.units] = ti;
+        w.nitems[0] = ti;
     }
 }
 
@@ -189,35 +185,6 @@ __device__ __forceinline__ int pow2_exp(float mx) {
 __device__ __forceinline__ int swz(int r, int q, int nq) {
     if (nq >= 16) return q ^ (r & 15);
     return q ^ ((r / (16 / nq)) & (nq - 1));
-}
-
-// One query row per D/8 lanes: the row times the power of two that brings its largest magnitude
-// into [0.5, 1), split into the fp16 hi / scaled-lo planes, and scale_log2 * 2^eQ for its
-// scores.
-template <int D>
-__global__ __launch_bounds__(256) void sp_qsplit(SparseArgs a, SparseWs w, long long rows) {
-    constexpr int LPR = D / 8;  // lanes per row (divides 64, so a row stays inside one wave)
-    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long row = gid / LPR;
-    const int c = (int)(gid - row * LPR);
-    const long long r = row < rows ? row : rows - 1;
-    const float *src = a.q + r * D + 8 * c;
-    // the fp32 query rows are read once here (the planes written below are what the forward reads)
-    const float4_t x0 = gload_nt<float4_t>(src), x1 = gload_nt<float4_t>(src + 4);
-    float mx = 0.f;
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(fabsf(x0[i]), fabsf(x1[i])));
-    for (int o = LPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    const int e = pow2_exp(mx);
-    half8_t hi, lo;
-    for (int i = 0; i < 4; ++i) {
-        const HiLo u = split16r(ldexpf(x0[i], -e)), v = split16r(ldexpf(x1[i], -e));
-        hi[i] = u.hi; lo[i] = u.lo;
-        hi[4 + i] = v.hi; lo[4 + i] = v.lo;
-    }
-    if (row >= rows) return;
-    *(half8_t *)(w.qhi + r * D + 8 * c) = hi;
-    *(half8_t *)(w.qlo + r * D + 8 * c) = lo;
-    if (c == 0) w.qmul[r] = ldexpf(a.scale_log2, e);
 }
 
 template <int D, int NT>
@@ -394,17 +361,16 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     // would wait for this group's partial stores to reach memory. At D = 256 the second set of
     // query registers does not fit: each group loads its own rows at its start.
     constexpr bool kPrefetchQ = D <= 128;
-    half8_t nqhi[KB], nqlo[KB];
-    float nqmul = 0.f;
+    float4_t nq[KB][2];  // fp32 dims 32kb + 8g16 .. +7 of the lane's row
     auto load_q = [&](int grp) {
         const int r = 16 * grp + n16;
         const int ix = r < nrows ? r / a.qhead : 0;
         const long long qrow = (long long)s_q[ix] * hq + h * a.qhead + (r % a.qhead);
+        const float *src = a.q + qrow * D + 8 * g16;
         for (int kb = 0; kb < KB; ++kb) {
-            nqhi[kb] = gload<half8_t>(w.qhi + qrow * D + 32 * kb + 8 * g16);
-            nqlo[kb] = gload<half8_t>(w.qlo + qrow * D + 32 * kb + 8 * g16);
+            nq[kb][0] = gload<float4_t>(src + 32 * kb);
+            nq[kb][1] = gload<float4_t>(src + 32 * kb + 4);
         }
-        nqmul = gload<float>(w.qmul + qrow);
     };
     if (kPrefetchQ && 16 * wave < nrows) load_q(wave);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -419,12 +385,24 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
             load_q(grp);
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         }
+        // the row's largest magnitude (its D dims lie in the 4 lanes g16 = 0..3 of column n16),
+        // the power of two eQ that brings it into [0.5, 1), and the row scaled and split
+        float qmx = 0.f;
+        for (int kb = 0; kb < KB; ++kb)
+            for (int c = 0; c < 2; ++c)
+                for (int i = 0; i < 4; ++i) qmx = fmaxf(qmx, fabsf(nq[kb][c][i]));
+        qmx = wave_max_xor(qmx, 16);
+        qmx = wave_max_xor(qmx, 32);
+        const int eQ = pow2_exp(qmx);
         half8_t qhi[KB], qlo[KB];
-        for (int kb = 0; kb < KB; ++kb) {
-            qhi[kb] = nqhi[kb];
-            qlo[kb] = nqlo[kb];
-        }
-        const float mult = ldexpf(nqmul, eK);
+        for (int kb = 0; kb < KB; ++kb)
+            for (int c = 0; c < 2; ++c)
+                for (int i = 0; i < 4; ++i) {
+                    const HiLo v = split16r(ldexpf(nq[kb][c][i], -eQ));
+                    qhi[kb][4 * c + i] = v.hi;
+                    qlo[kb][4 * c + i] = v.lo;
+                }
+        const float mult = ldexpf(a.scale_log2, eQ + eK);
         if (kPrefetchQ && 16 * (grp + NW) < nrows) load_q(grp + NW);
         // keys this lane scores (16j + 4g16 + i) that are mapped and below the edge's length
         uint64_t lm[MW];
@@ -543,7 +521,9 @@ size_t sparse_lds_limit() {
 }
 
 size_t sparse_workspace_bytes(int E, int units, long long qrows, int D) {
-    return layout(nullptr, nullptr, E, units, qrows, D) * 4;
+    (void)qrows;  // the query rows are split in registers: no per-row workspace
+    (void)D;
+    return layout(nullptr, nullptr, E, units) * 4;
 }
 
 pa_status launch_sparse(const SparseArgs &a, hipStream_t stream) {
@@ -557,17 +537,9 @@ pa_status launch_sparse(const SparseArgs &a, hipStream_t stream) {
     if (lds + 4096 > sparse_lds_limit() || (a.D != 64 && a.D != 128 && a.D != 256) ||
         (a.D == 256 && nt > 4))
         return PA_ERR_UNSUPPORTED;
-    const long long qrows = (long long)a.tq * a.hkv * a.qhead;
-    LaunchScope scope("sparse_forward", stream, qrows > 0 ? 6 : 5);
+    LaunchScope scope("sparse_forward", stream, 5);
     SparseWs w;
-    layout(&w, a.ws, a.E, a.units, qrows, a.D);
-    if (qrows > 0) {
-        const long long thr = qrows * (a.D / 8);
-        const unsigned grid = (unsigned)((thr + 255) / 256);
-        if (a.D == 256) scope.launch(sp_qsplit<256>, dim3(grid), dim3(256), 0, a, w, qrows);
-        else if (a.D == 128) scope.launch(sp_qsplit<128>, dim3(grid), dim3(256), 0, a, w, qrows);
-        else scope.launch(sp_qsplit<64>, dim3(grid), dim3(256), 0, a, w, qrows);
-    }
+    layout(&w, a.ws, a.E, a.units);
     scope.launch(sp_zero, dim3((a.units + 255) / 256), dim3(256), 0, w.counts, a.units);
     const int eg = (a.E + 255) / 256;
     scope.launch(sp_hist, dim3(eg), dim3(256), 0, a, w);
