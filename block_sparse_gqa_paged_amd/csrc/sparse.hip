@@ -8,9 +8,11 @@
 //
 // MI355X design:
 //  * Edges are grouped by their (batch, h, blk) key block with a counting sort on the device:
-//    a histogram whose atomic returns each edge's rank, a scan, and a plain scatter into a
-//    workspace permutation. One workgroup then stages a key block in LDS once and reuses it for
-//    up to kChunk edges; results per edge do not depend on the grouping or the order.
+//    a histogram whose atomic returns each edge's rank, a scan that also writes one record per
+//    work item, and a scatter of packed edge records (id, query, final key count) into sorted
+//    order. One workgroup then stages a key block in LDS once and reuses it for up to kChunk
+//    edges; results per edge do not depend on the grouping or the order. A work item starts
+//    with three dependent loads (its record; its edge records and block table entries; K and V).
 //  * fp32 products run as three fp16 MFMAs (v_mfma_f32_16x16x32_f16) on split operands. Before
 //    the split, each query row, the block's K and each dimension of the block's V are scaled by
 //    a power of two that brings their largest magnitude into [0.5, 1) (exact; folded back into
@@ -42,8 +44,12 @@ namespace {
 constexpr int kChunk = 128;    // edges per work item
 constexpr int kThreads = 512;  // 8 waves
 
+// Work-item record: its key block (unit), first edge in the sorted order, and edge count.
+// Sorted edge record: edge id, query index and the edge's key count (clamped to the block,
+// cut to the query's causal limit). Each is one 16-byte load for the forward kernel.
 struct SparseWs {
-    int32_t *counts, *rank, *offs, *ioffs, *nitems, *item_unit, *perm;
+    int32_t *counts, *rank, *offs, *nitems;
+    int4_t *items, *edges;
     int max_items;
 };
 
@@ -52,17 +58,16 @@ size_t al(size_t x) { return (x + 63) / 64 * 64; }  // in int32 words (256 bytes
 // Workspace layout in int32 words; returns the total.
 size_t layout(SparseWs *w, int32_t *ws, int E, int units) {
     const size_t max_items = (size_t)(E + kChunk - 1) / kChunk + units;
-    size_t off = 0, o[7];
+    size_t off = 0, o[6];
     o[0] = off; off = al(off + units);             // counts
     o[1] = off; off = al(off + E);                 // rank
     o[2] = off; off = al(off + units + 1);         // offs
-    o[3] = off; off = al(off + units + 1);         // ioffs
-    o[4] = off; off = al(off + 1);                 // nitems
-    o[5] = off; off = al(off + max_items);         // item_unit
-    o[6] = off; off = al(off + E);                 // perm
+    o[3] = off; off = al(off + 1);                 // nitems
+    o[4] = off; off = al(off + 4 * max_items);     // items
+    o[5] = off; off = al(off + 4 * (size_t)E);     // edges (sorted)
     if (w) {
-        w->counts = ws + o[0]; w->rank = ws + o[1]; w->offs = ws + o[2]; w->ioffs = ws + o[3];
-        w->nitems = ws + o[4]; w->item_unit = ws + o[5]; w->perm = ws + o[6];
+        w->counts = ws + o[0]; w->rank = ws + o[1]; w->offs = ws + o[2]; w->nitems = ws + o[3];
+        w->items = (int4_t *)(ws + o[4]); w->edges = (int4_t *)(ws + o[5]);
         w->max_items = (int)max_items;
     }
     return off;
@@ -104,9 +109,9 @@ __global__ void sp_hist(SparseArgs a, SparseWs w) {
     }
 }
 
-// One workgroup: exclusive scans of edge counts and of work-item counts, and the item map. Each
-// thread takes a contiguous run of units: it sums its run, one workgroup-wide scan of the run
-// sums gives the run's offsets, and the thread then writes its units' offsets and item entries.
+// One workgroup: exclusive scans of edge counts and of work-item counts, and the item records.
+// Each thread takes a contiguous run of units: it sums its run, one workgroup-wide scan of the
+// run sums gives the run's offsets, and the thread then writes its units' offsets and items.
 __global__ __launch_bounds__(1024) void sp_scan(SparseArgs a, SparseWs w) {
     __shared__ int sh[2][16];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -133,14 +138,13 @@ __global__ __launch_bounds__(1024) void sp_scan(SparseArgs a, SparseWs w) {
     for (int u = u0; u < u1; ++u) {
         const int c = w.counts[u], ni = (c + kChunk - 1) / kChunk;
         w.offs[u] = oe;
-        w.ioffs[u] = oi;
-        for (int k = 0; k < ni; ++k) w.item_unit[oi + k] = u;
+        for (int k = 0; k < ni; ++k)
+            w.items[oi + k] = int4_t{u, oe + k * kChunk, min(kChunk, c - k * kChunk), 0};
         oe += c;
         oi += ni;
     }
     if (tid == 0) {
         w.offs[a.units] = te;
-        w.ioffs[a.units] = ti;
         w.nitems[0] = ti;
     }
 }
@@ -150,7 +154,9 @@ __global__ void sp_scatter(SparseArgs a, SparseWs w) {
     if (e >= a.E) return;
     int q, h, blk, b, len, unit;
     if (!decode_edge(a, e, q, h, blk, b, len, unit)) return;
-    w.perm[w.offs[unit] + w.rank[e]] = e;
+    // causal: keys at positions after the query row's are cut off (a prefix stays)
+    if (a.q_pos) len = min(len, a.q_pos[q] - blk * a.block_size + 1);
+    w.edges[w.offs[unit] + w.rank[e]] = int4_t{e, q, len, 0};
 }
 
 // Split a float (already scaled into [-1, 1]) into fp16 hi and lo parts: x ~ hi + lo.
@@ -187,202 +193,62 @@ __device__ __forceinline__ int swz(int r, int q, int nq) {
     return q ^ ((r / (16 / nq)) & (nq - 1));
 }
 
-template <int D, int NT>
-__global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void sp_main(
-    SparseArgs a, SparseWs w) {
+// Query operands of group grp: lane (g16, n16) loads fp32 dims 32kb + 8g16 .. +7 of item row
+// 16 grp + n16 (a row past the item reads edge 0's query and is dropped later).
+template <int D>
+__device__ __forceinline__ void load_q(const SparseArgs &a, const int4_t *er, int grp, int nrows,
+                                       int h, int lane, float4_t (&nq)[D / 32][2]) {
+    const int g16 = lane >> 4, n16 = lane & 15;
+    const int r = 16 * grp + n16;
+    const int ix = r < nrows ? r / a.qhead : 0;
+    const long long qrow = (long long)er[ix][1] * (a.hkv * a.qhead) + h * a.qhead + (r % a.qhead);
+    const float *src = a.q + qrow * D + 8 * g16;
+    for (int kb = 0; kb < D / 32; ++kb) {
+        nq[kb][0] = gload<float4_t>(src + 32 * kb);
+        nq[kb][1] = gload<float4_t>(src + 32 * kb + 4);
+    }
+}
+
+// The edge groups of one staged key block. The item's rows are its (edge, q-head lane) pairs,
+// row r = edge r / qhead, lane r mod qhead; a wave takes 16 consecutive rows at a time (groups
+// wave, wave + NW, ...; 16 / qhead whole edges when qhead divides 16). Lane (g16, n16) serves
+// row n16 of the group. K (row-major) and V (transposed) are the block's fp16 hi/lo planes, er
+// the item's edge records, mmask the mapped-key bits, eK the block's K exponent and s_vmul the
+// per-dimension V scales; lane and wave are the thread's (a caller may pass values the compiler
+// cannot see through, to keep the per-lane offsets from being hoisted out of its loop).
+//
+// On entry nq holds the query operands of the wave's first group when kPrefetch (loaded and
+// waited for by the caller). Each group waits for all of the wave's outstanding memory
+// operations right before its stores.
+template <int D, int NT, int NW, bool kPrefetch>
+__device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *Khi,
+                                            const half_t *Klo, const half_t *Vhi,
+                                            const half_t *Vlo, float *slab, const float *s_vmul,
+                                            const int4_t *er, int nrows, int h, int eK,
+                                            const uint64_t (&mmask)[(16 * NT + 63) / 64],
+                                            int lane, int wave, float4_t (&nq)[D / 32][2]) {
     constexpr int BSP = 16 * NT;             // padded keys per block (NT even)
     constexpr int KB = D / 32;               // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;              // 16-dim output tiles
     constexpr int KK = NT / 2;               // 32-key k-blocks of PV
     constexpr int KQ = D / 8;                // 16-byte chunks per K row (8 halfs)
     constexpr int VC = BSP / 8;              // 16-byte chunks per V^T row (8 halfs)
-    constexpr int NW = kThreads / 64;        // waves
     constexpr int MW = (BSP + 63) / 64;      // 64-bit key-mask words
-    static_assert(kChunk <= kThreads, "one thread per staged edge");
-    extern __shared__ half_t lds[];
-    half_t *Khi = lds, *Klo = lds + BSP * D;
-    half_t *Vhi = lds + 2 * BSP * D, *Vlo = lds + 3 * BSP * D;
-    // per wave: 8 rows x 128 bytes of partial output on their way to a whole-line store; while
-    // the block is staged, the same 8 KB hold the per-wave, per-dimension maxima of |V|
-    float *slabs = (float *)(lds + 4 * BSP * D);
-    float *slab = slabs + (threadIdx.x >> 6) * 256;
-    static_assert(NW * D <= NW * 256, "per-wave |V| maxima fit the store slabs");
-    __shared__ float s_kmax[NW];                        // per-wave maxima of |K|
-    __shared__ int s_ev[D];                             // per-dimension exponent of V
-    // 2^s_ev: output scale per dimension, read as float4 (16-byte aligned)
-    __shared__ __attribute__((aligned(16))) float s_vmul[D];
-    __shared__ int s_e[kChunk], s_q[kChunk], s_len[kChunk];  // the item's edges
-
-    const int item = blockIdx.x;
-    if (item >= w.nitems[0]) return;
-    const int u = w.item_unit[item];
-    const int c = item - w.ioffs[u];
-    const int ebeg = w.offs[u] + c * kChunk;
-    const int nE = min(kChunk, w.offs[u + 1] - ebeg);
-    const int blk = u % a.nblk;
-    const int bh = u / a.nblk;
-    const int h = bh % a.hkv;
-    const int b = bh / a.hkv;
-    const int32_t *btrow = a.bt + (long long)b * a.max_pages;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
-    // the item's edges: id, query index and clamped length
-    if ((int)threadIdx.x < nE) {
-        const int e = w.perm[ebeg + threadIdx.x];
-        s_e[threadIdx.x] = e;
-        s_q[threadIdx.x] = a.edge_meta[5LL * e];
-        int len = min(a.edge_meta[5LL * e + 4], a.block_size);
-        // causal: keys at positions after the query row's are cut off (a prefix stays)
-        if (a.q_pos) len = min(len, a.q_pos[s_q[threadIdx.x]] - blk * a.block_size + 1);
-        s_len[threadIdx.x] = len;
-    }
-
-    auto page_of = [&](int t) {
-        const int slot = blk * a.ppb + t / a.page_size;
-        int pid = -1;
-        if (t < a.block_size && slot < a.max_pages) pid = btrow[slot];
-        return (pid >= 0 && pid < a.num_pages) ? pid : -1;
-    };
-    auto row_ptr = [&](const float *base, int pid, int t) {
-        return base + (((long long)pid * a.hkv + h) * a.page_size + t % a.page_size) * D;
-    };
-
-    // ---- stage the key block. A task is 4 consecutive keys x 8 dims of K and of V (32 + 32
-    // floats): dims 4q .. 4q+3 and D/2 + 4q .. +3, so that the 16-byte loads of the D/8 lanes of
-    // a key quad read whole contiguous half rows (a load instruction of 16-byte pieces at a
-    // 32-byte stride reads HBM more slowly), non-temporal. Pass 1 loads and takes the block-wide
-    // max |K| and the per-dimension max |V|; pass 2 scales by the powers of two, splits into
-    // fp16 planes and stores K row-major and V transposed. One task per thread: the pass-1
-    // registers are reused.
-    constexpr int TASKS = BSP / 4 * KQ;                       // (key quad, 8-dim chunk) pairs
-    static_assert(TASKS <= kThreads && TASKS % 64 == 0, "one task per thread, whole waves");
-    float kr[4][8], vr[4][8];
-    const int task = threadIdx.x;
-    const bool has_task = task < TASKS;
-    const int t4 = task / KQ, q = task - t4 * KQ;
-    for (int r = 0; r < 4; ++r) {
-        const int t = 4 * t4 + r;
-        const int pid = has_task ? page_of(t) : -1;
-        for (int x = 0; x < 8; ++x) { kr[r][x] = 0.f; vr[r][x] = 0.f; }
-        if (pid >= 0) {
-            const float *pk = row_ptr(a.kp, pid, t) + 4 * q;
-            const float *pv = row_ptr(a.vp, pid, t) + 4 * q;
-            const float4_t k0 = gload_nt<float4_t>(pk), k1 = gload_nt<float4_t>(pk + D / 2);
-            const float4_t v0 = gload_nt<float4_t>(pv), v1 = gload_nt<float4_t>(pv + D / 2);
-            for (int x = 0; x < 4; ++x) {
-                kr[r][x] = k0[x]; kr[r][4 + x] = k1[x];
-                vr[r][x] = v0[x]; vr[r][4 + x] = v1[x];
-            }
-        }
-    }
-    float mk = 0.f, mv[8];
-    for (int x = 0; x < 8; ++x) {
-        mv[x] = 0.f;
-        for (int r = 0; r < 4; ++r) {
-            mk = fmaxf(mk, fabsf(kr[r][x]));
-            mv[x] = fmaxf(mv[x], fabsf(vr[r][x]));
-        }
-    }
-    for (int o = 32; o > 0; o >>= 1) mk = fmaxf(mk, __shfl_xor(mk, o, 64));
-    // lanes l, l + KQ, ... hold the same dims (q = lane mod KQ): reduce over them
-    for (int o = KQ; o < 64; o <<= 1)
-        for (int x = 0; x < 8; ++x) mv[x] = fmaxf(mv[x], __shfl_xor(mv[x], o, 64));
-    if (lane == 0) s_kmax[wave] = mk;
-    if (lane < KQ) {
-        float *vw = slabs + wave * D;
-        for (int x = 0; x < 4; ++x) {
-            vw[4 * q + x] = mv[x];
-            vw[D / 2 + 4 * q + x] = mv[4 + x];
-        }
-    }
-    __syncthreads();
-    for (int i = 0; i < NW; ++i) mk = fmaxf(mk, s_kmax[i]);
-    const int eK = pow2_exp(mk);
-    if ((int)threadIdx.x < D) {
-        float m = 0.f;
-        for (int i = 0; i < NW; ++i) m = fmaxf(m, slabs[i * D + threadIdx.x]);
-        const int e = pow2_exp(m);
-        s_ev[threadIdx.x] = e;
-        s_vmul[threadIdx.x] = ldexpf(1.f, e);
-    }
-    __syncthreads();
-    if (has_task) {
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * t4 + r;
-            half8_t hi, lo;
-            for (int x = 0; x < 8; ++x) {
-                const HiLo v = split16r(ldexpf(kr[r][x], -eK));
-                hi[x] = v.hi;
-                lo[x] = v.lo;
-            }
-            // dims 4q .. are chunk q/2, dims D/2 + 4q .. chunk KQ/2 + q/2, at half (q & 1)
-            const int off0 = t * D + 8 * swz(t, q >> 1, KQ) + 4 * (q & 1);
-            const int off1 = t * D + 8 * swz(t, KQ / 2 + (q >> 1), KQ) + 4 * (q & 1);
-            *(half4_t *)(Khi + off0) = half4_t{hi[0], hi[1], hi[2], hi[3]};
-            *(half4_t *)(Klo + off0) = half4_t{lo[0], lo[1], lo[2], lo[3]};
-            *(half4_t *)(Khi + off1) = half4_t{hi[4], hi[5], hi[6], hi[7]};
-            *(half4_t *)(Klo + off1) = half4_t{lo[4], lo[5], lo[6], lo[7]};
-        }
-        // V^T row d holds, in 16-byte chunk 4c + g of a 32-key block c, the keys
-        // 32c + 4g .. +3 and 32c + 16 + 4g .. +3: the k-slots (g, 0..7) of one PV operand.
-        const int vq = 4 * (t4 >> 3) + (t4 & 3), vh = 4 * ((t4 >> 2) & 1);
-        for (int x = 0; x < 8; ++x) {
-            const int d = x < 4 ? 4 * q + x : D / 2 + 4 * q + (x - 4);
-            const int ed = s_ev[d];
-            half4_t hi, lo;
-            for (int r = 0; r < 4; ++r) {
-                const HiLo v = split16(ldexpf(vr[r][x], -ed));
-                hi[r] = v.hi;
-                lo[r] = v.lo;
-            }
-            const int off = d * BSP + 8 * swz(d, vq, VC) + vh;
-            *(half4_t *)(Vhi + off) = hi;
-            *(half4_t *)(Vlo + off) = lo;
-        }
-    }
-    // mapped-key masks (wave-uniform): bit t set when key t sits on a mapped page
-    uint64_t mmask[MW];
-    for (int hw = 0; hw < MW; ++hw) {
-        const int t = 64 * hw + lane;
-        mmask[hw] = __ballot(t < BSP && page_of(t) >= 0);
-    }
-    __syncthreads();
-
-    // ---- edge groups. The item's rows are its (edge, q-head lane) pairs, row r = edge
-    // r / qhead, lane r mod qhead; a wave takes 16 consecutive rows at a time (16 / qhead whole
-    // edges when qhead divides 16). Lane (g16, n16) serves row n16 of the group.
-    const int g16 = lane >> 4, n16 = lane & 15;
-    const int nrows = nE * a.qhead;
-    const int hq = a.hkv * a.qhead;
-    // With D <= 128 the next group's query operands are loaded at the start of this group, and
-    // the one wait for them sits right before this group's stores. A wait for a load while
-    // stores are outstanding has to drain the stores too (loads and stores share the counter
-    // and may complete out of order), so without this the next group's first use of its query
-    // would wait for this group's partial stores to reach memory. At D = 256 the second set of
-    // query registers does not fit: each group loads its own rows at its start.
-    constexpr bool kPrefetchQ = D <= 128;
-    float4_t nq[KB][2];  // fp32 dims 32kb + 8g16 .. +7 of the lane's row
-    auto load_q = [&](int grp) {
-        const int r = 16 * grp + n16;
-        const int ix = r < nrows ? r / a.qhead : 0;
-        const long long qrow = (long long)s_q[ix] * hq + h * a.qhead + (r % a.qhead);
-        const float *src = a.q + qrow * D + 8 * g16;
-        for (int kb = 0; kb < KB; ++kb) {
-            nq[kb][0] = gload<float4_t>(src + 32 * kb);
-            nq[kb][1] = gload<float4_t>(src + 32 * kb + 4);
-        }
-    };
-    if (kPrefetchQ && 16 * wave < nrows) load_q(wave);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     for (int grp = wave; 16 * grp < nrows; grp += NW) {
+        // the lane index through an empty asm statement, once per group: the ~32 per-lane LDS
+        // operand offsets are then recomputed in each group rather than held in registers
+        // across the loop (which would leave the group's own values short of registers)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int g16 = ln >> 4, n16 = ln & 15;
         const int row = 16 * grp + n16;
         const bool vrow = row < nrows;
         const int ix = vrow ? row / a.qhead : 0;  // rows past the item read edge 0, then drop it
         const int qh = row % a.qhead;
-        const int e = s_e[ix];
-        const int len = vrow ? s_len[ix] : 0;
-        if (!kPrefetchQ) {
-            load_q(grp);
+        const int e = er[ix][0];
+        const int len = vrow ? er[ix][2] : 0;
+        if (!kPrefetch) {
+            load_q<D>(a, er, grp, nrows, h, ln, nq);
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         }
         // the row's largest magnitude (its D dims lie in the 4 lanes g16 = 0..3 of column n16),
@@ -403,7 +269,13 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
                     qlo[kb][4 * c + i] = v.lo;
                 }
         const float mult = ldexpf(a.scale_log2, eQ + eK);
-        if (kPrefetchQ && 16 * (grp + NW) < nrows) load_q(grp + NW);
+        // The next group's query operands are loaded here, and the one wait for them sits right
+        // before this group's stores. A wait for a load while stores are outstanding has to
+        // drain the stores too (loads and stores share the counter and may complete out of
+        // order), so loading later would make the next group's first use of its query wait
+        // for this group's partial stores to reach memory.
+        if (kPrefetch && 16 * (grp + NW) < nrows)
+            load_q<D>(a, er, grp + NW, nrows, h, ln, nq);
         // keys this lane scores (16j + 4g16 + i) that are mapped and below the edge's length
         uint64_t lm[MW];
         for (int hw = 0; hw < MW; ++hw) {
@@ -482,11 +354,11 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
             a.l[p] = ls;
         }
         for (int h = 0; h < 2; ++h) {
-            const int r = 16 * grp + 8 * h + (lane >> 3);  // the item row this lane stores
+            const int r = 16 * grp + 8 * h + (ln >> 3);  // the item row this lane stores
             const bool rvalid = r < nrows;
             const long long pr =
-                (long long)s_e[rvalid ? r / a.qhead : 0] * a.qhead + r % a.qhead;
-            float *dst = a.o + pr * D + 4 * (lane & 7);
+                (long long)er[rvalid ? r / a.qhead : 0][0] * a.qhead + r % a.qhead;
+            float *dst = a.o + pr * D + 4 * (ln & 7);
             for (int j = 0; j < NDT / 2; ++j) {
                 // slab row r (128 bytes) holds its 16-byte chunk c at c ^ ((r >> 1) & 3): the
                 // 8 rows written at one chunk, and the two rows read per 16 lanes, then cover
@@ -500,13 +372,189 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
                     *(float4_t *)(rowp + 4 * (g16 ^ sx)) = v0;
                     *(float4_t *)(rowp + 16 + 4 * (g16 ^ sx)) = v1;
                 }
-                const int lr = lane >> 3;
+                const int lr = ln >> 3;
                 const float4_t v =
-                    *(const float4_t *)(slab + lr * 32 + 4 * ((lane & 7) ^ ((lr >> 1) & 3)));
+                    *(const float4_t *)(slab + lr * 32 + 4 * ((ln & 7) ^ ((lr >> 1) & 3)));
                 if (rvalid) __builtin_nontemporal_store(v, (float4_t *)(dst + 32 * j));
             }
         }
     }
+}
+
+// Block-table page of key t of the block at (b, blk), or -1 (past the block, past the table row,
+// or an unmapped or out-of-range entry).
+__device__ __forceinline__ int block_page(const SparseArgs &a, const int32_t *btrow, int blk,
+                                          int t) {
+    const int slot = blk * a.ppb + t / a.page_size;
+    int pid = -1;
+    if (t < a.block_size && slot < a.max_pages) pid = btrow[slot];
+    return (pid >= 0 && pid < a.num_pages) ? pid : -1;
+}
+
+// Workgroup per work item: stages its key block from HBM into the fp16 planes, then runs the
+// edge groups. For the shapes whose planes and raw rows do not both fit in LDS (D = 256, or
+// 128-key blocks at D = 128).
+template <int D, int NT>
+__global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void sp_main(
+    SparseArgs a, SparseWs w) {
+    constexpr int BSP = 16 * NT;             // padded keys per block (NT even)
+    constexpr int KQ = D / 8;                // 16-byte chunks per K row (8 halfs)
+    constexpr int VC = BSP / 8;              // 16-byte chunks per V^T row (8 halfs)
+    constexpr int NW = kThreads / 64;        // waves
+    constexpr int MW = (BSP + 63) / 64;      // 64-bit key-mask words
+    static_assert(kChunk <= kThreads, "one thread per staged edge");
+    extern __shared__ half_t lds[];
+    half_t *Khi = lds, *Klo = lds + BSP * D;
+    half_t *Vhi = lds + 2 * BSP * D, *Vlo = lds + 3 * BSP * D;
+    // per wave: 8 rows x 128 bytes of partial output on their way to a whole-line store; while
+    // the block is staged, the same 8 KB hold the per-wave, per-dimension maxima of |V|
+    float *slabs = (float *)(lds + 4 * BSP * D);
+    float *slab = slabs + (threadIdx.x >> 6) * 256;
+    static_assert(NW * D <= NW * 256, "per-wave |V| maxima fit the store slabs");
+    __shared__ float s_kmax[NW];                        // per-wave maxima of |K|
+    __shared__ int s_ev[D];                             // per-dimension exponent of V
+    // 2^s_ev: output scale per dimension, read as float4 (16-byte aligned)
+    __shared__ __attribute__((aligned(16))) float s_vmul[D];
+    __shared__ __attribute__((aligned(16))) int4_t s_er[kChunk];  // the item's edge records
+
+    // The item's record is read together with the item count (item < max_items: inside the
+    // workspace; a record past the count holds no defined value and is not used).
+    const int item = blockIdx.x;
+    const int nitems = w.nitems[0];
+    const int4_t rec = w.items[item];
+    if (item >= nitems) return;
+    const int u = rec[0], ebeg = rec[1], nE = rec[2];
+    const int blk = u % a.nblk;
+    const int bh = u / a.nblk;
+    const int h = bh % a.hkv;
+    const int b = bh / a.hkv;
+    const int32_t *btrow = a.bt + (long long)b * a.max_pages;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    // The item's sorted edge records (id, query index, key count) are loaded first, beside the
+    // block table entries; the K and V loads follow as soon as the page ids arrive, and the edge
+    // records go to LDS after them (loads return in order: this waits for the records only).
+    const bool has_edge = (int)threadIdx.x < nE;
+    int4_t erec = {0, 0, 0, 0};
+    if (has_edge) erec = w.edges[ebeg + threadIdx.x];
+
+    auto row_ptr = [&](const float *base, int pid, int t) {
+        return base + (((long long)pid * a.hkv + h) * a.page_size + t % a.page_size) * D;
+    };
+
+    // ---- stage the key block. A task is 4 consecutive keys x 8 dims of K and of V (32 + 32
+    // floats): dims 4q .. 4q+3 and D/2 + 4q .. +3, so that the 16-byte loads of the D/8 lanes of
+    // a key quad read whole contiguous half rows (a load instruction of 16-byte pieces at a
+    // 32-byte stride reads HBM more slowly), non-temporal. Pass 1 loads and takes the block-wide
+    // max |K| and the per-dimension max |V|; pass 2 scales by the powers of two, splits into
+    // fp16 planes and stores K row-major and V transposed. One task per thread: the pass-1
+    // registers are reused.
+    constexpr int TASKS = BSP / 4 * KQ;                       // (key quad, 8-dim chunk) pairs
+    static_assert(TASKS <= kThreads && TASKS % 64 == 0, "one task per thread, whole waves");
+    float kr[4][8], vr[4][8];
+    const int task = threadIdx.x;
+    const bool has_task = task < TASKS;
+    const int t4 = task / KQ, q = task - t4 * KQ;
+    int pids[4];
+    for (int r = 0; r < 4; ++r) pids[r] = has_task ? block_page(a, btrow, blk, 4 * t4 + r) : -1;
+    // mapped-key masks (wave-uniform): bit t set when key t sits on a mapped page
+    uint64_t mmask[MW];
+    for (int hw = 0; hw < MW; ++hw) {
+        const int t = 64 * hw + lane;
+        mmask[hw] = __ballot(t < BSP && block_page(a, btrow, blk, t) >= 0);
+    }
+    for (int r = 0; r < 4; ++r) {
+        const int t = 4 * t4 + r;
+        const int pid = pids[r];
+        for (int x = 0; x < 8; ++x) { kr[r][x] = 0.f; vr[r][x] = 0.f; }
+        if (pid >= 0) {
+            const float *pk = row_ptr(a.kp, pid, t) + 4 * q;
+            const float *pv = row_ptr(a.vp, pid, t) + 4 * q;
+            const float4_t k0 = gload_nt<float4_t>(pk), k1 = gload_nt<float4_t>(pk + D / 2);
+            const float4_t v0 = gload_nt<float4_t>(pv), v1 = gload_nt<float4_t>(pv + D / 2);
+            for (int x = 0; x < 4; ++x) {
+                kr[r][x] = k0[x]; kr[r][4 + x] = k1[x];
+                vr[r][x] = v0[x]; vr[r][4 + x] = v1[x];
+            }
+        }
+    }
+    if (has_edge) s_er[threadIdx.x] = erec;
+    float mk = 0.f, mv[8];
+    for (int x = 0; x < 8; ++x) {
+        mv[x] = 0.f;
+        for (int r = 0; r < 4; ++r) {
+            mk = fmaxf(mk, fabsf(kr[r][x]));
+            mv[x] = fmaxf(mv[x], fabsf(vr[r][x]));
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) mk = fmaxf(mk, __shfl_xor(mk, o, 64));
+    // lanes l, l + KQ, ... hold the same dims (q = lane mod KQ): reduce over them
+    for (int o = KQ; o < 64; o <<= 1)
+        for (int x = 0; x < 8; ++x) mv[x] = fmaxf(mv[x], __shfl_xor(mv[x], o, 64));
+    if (lane == 0) s_kmax[wave] = mk;
+    if (lane < KQ) {
+        float *vw = slabs + wave * D;
+        for (int x = 0; x < 4; ++x) {
+            vw[4 * q + x] = mv[x];
+            vw[D / 2 + 4 * q + x] = mv[4 + x];
+        }
+    }
+    __syncthreads();
+    for (int i = 0; i < NW; ++i) mk = fmaxf(mk, s_kmax[i]);
+    const int eK = pow2_exp(mk);
+    if ((int)threadIdx.x < D) {
+        float m = 0.f;
+        for (int i = 0; i < NW; ++i) m = fmaxf(m, slabs[i * D + threadIdx.x]);
+        const int e = pow2_exp(m);
+        s_ev[threadIdx.x] = e;
+        s_vmul[threadIdx.x] = ldexpf(1.f, e);
+    }
+    __syncthreads();
+    if (has_task) {
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * t4 + r;
+            half8_t hi, lo;
+            for (int x = 0; x < 8; ++x) {
+                const HiLo v = split16r(ldexpf(kr[r][x], -eK));
+                hi[x] = v.hi;
+                lo[x] = v.lo;
+            }
+            // dims 4q .. are chunk q/2, dims D/2 + 4q .. chunk KQ/2 + q/2, at half (q & 1)
+            const int off0 = t * D + 8 * swz(t, q >> 1, KQ) + 4 * (q & 1);
+            const int off1 = t * D + 8 * swz(t, KQ / 2 + (q >> 1), KQ) + 4 * (q & 1);
+            *(half4_t *)(Khi + off0) = half4_t{hi[0], hi[1], hi[2], hi[3]};
+            *(half4_t *)(Klo + off0) = half4_t{lo[0], lo[1], lo[2], lo[3]};
+            *(half4_t *)(Khi + off1) = half4_t{hi[4], hi[5], hi[6], hi[7]};
+            *(half4_t *)(Klo + off1) = half4_t{lo[4], lo[5], lo[6], lo[7]};
+        }
+        // V^T row d holds, in 16-byte chunk 4c + g of a 32-key block c, the keys
+        // 32c + 4g .. +3 and 32c + 16 + 4g .. +3: the k-slots (g, 0..7) of one PV operand.
+        const int vq = 4 * (t4 >> 3) + (t4 & 3), vh = 4 * ((t4 >> 2) & 1);
+        for (int x = 0; x < 8; ++x) {
+            const int d = x < 4 ? 4 * q + x : D / 2 + 4 * q + (x - 4);
+            const int ed = s_ev[d];
+            half4_t hi, lo;
+            for (int r = 0; r < 4; ++r) {
+                const HiLo v = split16(ldexpf(vr[r][x], -ed));
+                hi[r] = v.hi;
+                lo[r] = v.lo;
+            }
+            const int off = d * BSP + 8 * swz(d, vq, VC) + vh;
+            *(half4_t *)(Vhi + off) = hi;
+            *(half4_t *)(Vlo + off) = lo;
+        }
+    }
+    __syncthreads();
+
+    // With D <= 128 each group's query operands are loaded one group ahead (the first here). At
+    // D = 256 the second set of query registers does not fit: each group loads its own rows.
+    constexpr bool kPrefetchQ = D <= 128;
+    const int nrows = nE * a.qhead;
+    float4_t nq[D / 32][2];
+    if (kPrefetchQ && 16 * wave < nrows) load_q<D>(a, s_er, wave, nrows, h, lane, nq);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    edge_groups<D, NT, NW, kPrefetchQ>(a, Khi, Klo, Vhi, Vlo, slab, s_vmul, s_er, nrows, h, eK,
+                                       mmask, lane, wave, nq);
 }
 
 }  // namespace
@@ -529,14 +577,13 @@ size_t sparse_workspace_bytes(int E, int units, long long qrows, int D) {
 pa_status launch_sparse(const SparseArgs &a, hipStream_t stream) {
     int nt = 2;
     while (16 * nt < a.block_size) nt *= 2;
-    // the K and V hi/lo planes, then one 1 KB store slab per wave
-    const size_t lds = (size_t)4 * 16 * nt * a.D * sizeof(half_t) + (kThreads / 64) * 1024;
-    // dynamic LDS plus the kernel's static arrays (edge list, maxima, per-dimension V scales:
-    // 2.6 KB at D = 128)
-    // (at D = 256 the planes of a 128-key block exceed the LDS: blocks of up to 64 keys)
-    if (lds + 4096 > sparse_lds_limit() || (a.D != 64 && a.D != 128 && a.D != 256) ||
-        (a.D == 256 && nt > 4))
+    if ((a.D != 64 && a.D != 128 && a.D != 256) || (a.D == 256 && nt > 4))
         return PA_ERR_UNSUPPORTED;
+    // the K and V hi/lo planes, then one 1 KB store slab per wave, as dynamic LDS, plus the
+    // kernel's static arrays (edge records, maxima, per-dimension V scales: 3.6 KB at D = 128).
+    // At D = 256 the planes of a 128-key block exceed the LDS: blocks of up to 64 keys.
+    const size_t lds = (size_t)4 * 16 * nt * a.D * sizeof(half_t) + (kThreads / 64) * 1024;
+    if (lds + 4096 > sparse_lds_limit()) return PA_ERR_UNSUPPORTED;
     LaunchScope scope("sparse_forward", stream, 5);
     SparseWs w;
     layout(&w, a.ws, a.E, a.units);
