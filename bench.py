@@ -284,13 +284,18 @@ def main():
     if not args.no_extra:
         extra = run_extra(args, torch, np, pa, dev, W)
     if args.copy_calibration:
-        # a plain device copy of known size, for scaling HBM counter readings
-        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        # kernels of known traffic, for scaling HBM counter readings: a plain device copy, and
+        # as an independent check a reduction that only reads and a fill that only writes
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        total = float(src.sum().item())
+        dst.fill_(2.0)
+        torch.cuda.synchronize()
         extra["copy_calibration_bytes_each_way"] = src.numel() * 4
+        extra["read_calibration_sum"] = total
 
     line = {
         "metric": "paged-attn decode KV GB/s (% of HBM peak) and query tokens/s, 1 MI355X",
