@@ -16,12 +16,13 @@
 //  * fp32 products run as three fp16 MFMAs (v_mfma_f32_16x16x32_f16) on split operands. Before
 //    the split, each query row, the block's K and each dimension of the block's V are scaled by
 //    a power of two that brings their largest magnitude into [0.5, 1) (exact; folded back into
-//    the scores and, per dimension, into the output). Q and K: x = hi + 2^-11 lo with
-//    hi = fp16(x), lo = fp16((x - hi) * 2^11), so lo stays a normal fp16 number for every x down
-//    to 2^-14 of the scaled maximum and each operand keeps 22 significant bits over that range;
-//    q.k ~ hi.hi + 2^-11 (hi.lo + lo.hi), the two sums in separate fp32 accumulators. V and P:
-//    x = hi + lo with lo = fp16(x - hi) (V per dimension and P <= 1 need no wider range), and
-//    p.v ~ hi.hi + hi.lo + lo.hi. The dropped lo.lo terms are ~2^-22 of each product.
+//    the scores and, per dimension, into the output). Q and K are scaled by another 2^11 and
+//    split as x = hi + lo, hi = fp16(x), lo = fp16(x - hi): lo stays a normal fp16 number for
+//    elements down to 2^-14 of the maximum, so each operand keeps 22 significant bits over that
+//    range; 2^22 q.k ~ hi.hi + (hi.lo + lo.hi), the two sums in separate fp32 accumulators that
+//    are added once per score. V and P: x = hi + lo with lo = fp16(x - hi) (V per dimension and
+//    P <= 1 need no wider range), and p.v ~ hi.hi + hi.lo + lo.hi. The dropped lo.lo terms are
+//    ~2^-22 of each product.
 //  * S^T = K . Q^T has 16 keys as rows and 16 query rows as columns; its accumulator gives each
 //    lane 8 keys of one row across two key tiles, exactly the k-slots of the P operand of
 //    O^T = V^T . P^T, so P never leaves registers, and O^T gives each lane four consecutive
@@ -159,21 +160,42 @@ __global__ void sp_scatter(SparseArgs a, SparseWs w) {
     w.edges[w.offs[unit] + w.rank[e]] = int4_t{e, q, len, 0};
 }
 
-// Split a float (already scaled into [-1, 1]) into fp16 hi and lo parts: x ~ hi + lo.
-struct HiLo {
-    half_t hi, lo;
-};
-__device__ __forceinline__ HiLo split16(float x) {
-    const half_t hi = (half_t)x;
-    return HiLo{hi, (half_t)(x - (float)hi)};
+// Split two floats x0 f, x1 f (f a power of two, the results in fp16 range) into fp16 hi and lo
+// parts, x f ~ hi + lo: one packed conversion gives both hi parts, and each lo = x f - hi is one
+// mixed-precision fused multiply-add that reads hi as fp16 and writes fp16.
+typedef float float2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split16x2(float x0, float x1, float f, half2_t &hi, half2_t &lo) {
+    hi = __builtin_convertvector(float2_t{x0 * f, x1 * f}, half2_t);
+    lo[0] = (half_t)__builtin_fmaf(x0, f, -(float)hi[0]);
+    lo[1] = (half_t)__builtin_fmaf(x1, f, -(float)hi[1]);
 }
-// The same with the remainder stored times 2^11: x ~ hi + 2^-11 lo, lo normal in fp16 for every
-// |x| >= 2^-14 (the remainder of such an x is >= 2^-25), so small elements of a row or block
-// keep their precision instead of falling into fp16 subnormals.
-constexpr float kLoScale = 2048.f, kLoUnscale = 1.f / 2048.f;
-__device__ __forceinline__ HiLo split16r(float x) {
-    const half_t hi = (half_t)x;
-    return HiLo{hi, (half_t)((x - (float)hi) * kLoScale)};
+// The same unscaled; one is 1.f hidden from the compiler (with a literal 1 the multiply-adds
+// would be rewritten as widen-and-subtract).
+__device__ __forceinline__ void split16x2u(float x0, float x1, float one, half2_t &hi,
+                                           half2_t &lo) {
+    hi = __builtin_convertvector(float2_t{x0, x1}, half2_t);
+    lo[0] = (half_t)__builtin_fmaf(x0, one, -(float)hi[0]);
+    lo[1] = (half_t)__builtin_fmaf(x1, one, -(float)hi[1]);
+}
+// Q and K are split after scaling into [-2^11, 2^11) (kOpExp): there hi keeps 11 significant
+// bits for every |x| >= 2^-14 and lo = fp16(x - hi), at most half an ulp of hi, stays a normal
+// fp16 number for every |x| >= 2^-3, i.e. for elements down to 2^-14 of the row or block maximum,
+// with no separate scaling of the remainder.
+constexpr int kOpExp = 11;
+
+// Item row r -> (edge within the item, q-head lane), r = ix * d + qh, with inv = 1 / d. Rows
+// number at most 128 d + 15, so the quotient is at most 143 and its float estimate is off by
+// less than 1e-4: truncation is the quotient or one away from it, and one step either way
+// corrects it (a few instructions instead of an integer division by the runtime d).
+struct RowIx {
+    int ix, qh;
+};
+__device__ __forceinline__ RowIx row_split(int r, int d, float inv) {
+    int q = (int)((float)r * inv);
+    int rem = r - q * d;
+    if (rem < 0) { --q; rem += d; }
+    if (rem >= d) { ++q; rem -= d; }
+    return RowIx{q, rem};
 }
 
 // Power-of-two factor that brings max |x| = mx into [0.5, 1) (1 for mx == 0).
@@ -197,11 +219,11 @@ __device__ __forceinline__ int swz(int r, int q, int nq) {
 // 16 grp + n16 (a row past the item reads edge 0's query and is dropped later).
 template <int D>
 __device__ __forceinline__ void load_q(const SparseArgs &a, const int4_t *er, int grp, int nrows,
-                                       int h, int lane, float4_t (&nq)[D / 32][2]) {
+                                       int h, int lane, float qinv, float4_t (&nq)[D / 32][2]) {
     const int g16 = lane >> 4, n16 = lane & 15;
     const int r = 16 * grp + n16;
-    const int ix = r < nrows ? r / a.qhead : 0;
-    const long long qrow = (long long)er[ix][1] * (a.hkv * a.qhead) + h * a.qhead + (r % a.qhead);
+    const RowIx x = row_split(r < nrows ? r : 0, a.qhead, qinv);
+    const long long qrow = (long long)er[x.ix][1] * (a.hkv * a.qhead) + h * a.qhead + x.qh;
     const float *src = a.q + qrow * D + 8 * g16;
     for (int kb = 0; kb < D / 32; ++kb) {
         nq[kb][0] = gload<float4_t>(src + 32 * kb);
@@ -226,7 +248,8 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
                                             const half_t *Vlo, float *slab, const float *s_vmul,
                                             const int4_t *er, int nrows, int h, int eK,
                                             const uint64_t (&mmask)[(16 * NT + 63) / 64],
-                                            int lane, int wave, float4_t (&nq)[D / 32][2]) {
+                                            int lane, int wave, float qinv,
+                                            float4_t (&nq)[D / 32][2]) {
     constexpr int BSP = 16 * NT;             // padded keys per block (NT even)
     constexpr int KB = D / 32;               // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;              // 16-dim output tiles
@@ -234,6 +257,11 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
     constexpr int KQ = D / 8;                // 16-byte chunks per K row (8 halfs)
     constexpr int VC = BSP / 8;              // 16-byte chunks per V^T row (8 halfs)
     constexpr int MW = (BSP + 63) / 64;      // 64-bit key-mask words
+    bool mfull = true;  // every key of the padded block sits on a mapped page
+    for (int hw = 0; hw < MW; ++hw) {
+        const int nb = BSP - 64 * hw;
+        mfull = mfull && mmask[hw] == (nb >= 64 ? ~0ull : (1ull << nb) - 1);
+    }
     for (int grp = wave; 16 * grp < nrows; grp += NW) {
         // the lane index through an empty asm statement, once per group: the ~32 per-lane LDS
         // operand offsets are then recomputed in each group rather than held in registers
@@ -243,16 +271,18 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         const int g16 = ln >> 4, n16 = ln & 15;
         const int row = 16 * grp + n16;
         const bool vrow = row < nrows;
-        const int ix = vrow ? row / a.qhead : 0;  // rows past the item read edge 0, then drop it
-        const int qh = row % a.qhead;
+        const RowIx rx = row_split(row, a.qhead, qinv);
+        const int ix = vrow ? rx.ix : 0;  // rows past the item read edge 0, then drop it
+        const int qh = rx.qh;
         const int e = er[ix][0];
         const int len = vrow ? er[ix][2] : 0;
         if (!kPrefetch) {
-            load_q<D>(a, er, grp, nrows, h, ln, nq);
+            load_q<D>(a, er, grp, nrows, h, ln, qinv, nq);
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         }
         // the row's largest magnitude (its D dims lie in the 4 lanes g16 = 0..3 of column n16),
-        // the power of two eQ that brings it into [0.5, 1), and the row scaled and split
+        // the power of two eQ that brings it into [0.5, 1), and the row scaled by 2^(11 - eQ)
+        // and split
         float qmx = 0.f;
         for (int kb = 0; kb < KB; ++kb)
             for (int c = 0; c < 2; ++c)
@@ -260,33 +290,31 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         qmx = wave_max_xor(qmx, 16);
         qmx = wave_max_xor(qmx, 32);
         const int eQ = pow2_exp(qmx);
+        const float qf = ldexpf(1.f, kOpExp - eQ);
         half8_t qhi[KB], qlo[KB];
         for (int kb = 0; kb < KB; ++kb)
             for (int c = 0; c < 2; ++c)
-                for (int i = 0; i < 4; ++i) {
-                    const HiLo v = split16r(ldexpf(nq[kb][c][i], -eQ));
-                    qhi[kb][4 * c + i] = v.hi;
-                    qlo[kb][4 * c + i] = v.lo;
+                for (int i = 0; i < 4; i += 2) {
+                    half2_t h2, l2;
+                    split16x2(nq[kb][c][i], nq[kb][c][i + 1], qf, h2, l2);
+                    qhi[kb][4 * c + i] = h2[0];
+                    qhi[kb][4 * c + i + 1] = h2[1];
+                    qlo[kb][4 * c + i] = l2[0];
+                    qlo[kb][4 * c + i + 1] = l2[1];
                 }
-        const float mult = ldexpf(a.scale_log2, eQ + eK);
+        // a score in log2 units is its product sum times mult (> 0)
+        const float mult = ldexpf(a.scale_log2, eQ + eK - 2 * kOpExp);
         // The next group's query operands are loaded here, and the one wait for them sits right
         // before this group's stores. A wait for a load while stores are outstanding has to
         // drain the stores too (loads and stores share the counter and may complete out of
         // order), so loading later would make the next group's first use of its query wait
         // for this group's partial stores to reach memory.
-        if (kPrefetch && 16 * (grp + NW) < nrows)
-            load_q<D>(a, er, grp + NW, nrows, h, ln, nq);
-        // keys this lane scores (16j + 4g16 + i) that are mapped and below the edge's length
-        uint64_t lm[MW];
-        for (int hw = 0; hw < MW; ++hw) {
-            const int rem = len - 64 * hw;
-            const uint64_t lenm = rem >= 64 ? ~0ull : (rem <= 0 ? 0ull : (1ull << rem) - 1);
-            lm[hw] = (mmask[hw] & lenm) >> (4 * g16);
-        }
-
-        // S^T tiles: lane holds keys 16j + 4g16 + i of row n16 (log2 units).
+        // (unconditionally: past the last group it reads edge 0's rows, which go unused; a
+        // conditional load would make the compiler copy all of nq on both paths)
+        if (kPrefetch) load_q<D>(a, er, grp + NW, nrows, h, ln, qinv, nq);
+        // S^T tiles: lane holds keys 16j + 4g16 + i of row n16, as product sums (hi.hi in acc,
+        // the cross terms hi.lo + lo.hi in acx).
         float s[NT][4];
-        float mx = -INFINITY;
         for (int j = 0; j < NT; ++j) {
             // hi.hi in acc, the scaled cross terms hi.lo + lo.hi in acx
             float4_t acc = {0.f, 0.f, 0.f, 0.f}, acx = {0.f, 0.f, 0.f, 0.f};
@@ -299,28 +327,51 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
                 acx = mfma16x16x32(klo, qhi[kb], acx);
                 acc = mfma16x16x32(khi, qhi[kb], acc);
             }
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = (lm[j >> 2] >> (16 * (j & 3) + i)) & 1;
-                s[j][i] = ok ? __builtin_fmaf(acx[i], kLoUnscale, acc[i]) * mult : -INFINITY;
-                mx = fmaxf(mx, s[j][i]);
-            }
+            for (int i = 0; i < 4; ++i) s[j][i] = acc[i] + acx[i];
             // keep the next tile's LDS operand reads from being hoisted over this tile (each
             // hoisted read holds 4 registers)
             __builtin_amdgcn_sched_barrier(0);
         }
+        // Keys past the edge's length or on unmapped pages are excluded (-inf). The test is
+        // skipped when every key of the block is mapped and every row of the group sees all of
+        // them (the common case; the branch is uniform over the wave).
+        if (!(mfull && __ballot(vrow && len < BSP) == 0)) {
+            uint64_t lm[MW];  // keys this lane scores (16j + 4g16 + i), mapped and in length
+            for (int hw = 0; hw < MW; ++hw) {
+                const int rem = len - 64 * hw;
+                const uint64_t lenm = rem >= 64 ? ~0ull : (rem <= 0 ? 0ull : (1ull << rem) - 1);
+                lm[hw] = (mmask[hw] & lenm) >> (4 * g16);
+            }
+            for (int j = 0; j < NT; ++j)
+                for (int i = 0; i < 4; ++i)
+                    if (!((lm[j >> 2] >> (16 * (j & 3) + i)) & 1)) s[j][i] = -INFINITY;
+        }
+        float mx = -INFINITY;
+        for (int j = 0; j < NT; ++j)
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
         mx = wave_max_xor(mx, 16);
         mx = wave_max_xor(mx, 32);
-        const float mu = (mx == -INFINITY) ? 0.f : mx;
+        // the row maximum in log2 units (0 when every key is excluded)
+        const float mu = (mx == -INFINITY) ? 0.f : mx * mult;
         float ls = 0.f;
+        float one = 1.f;
+        asm volatile("" : "+v"(one));
         half8_t phi[KK], plo[KK];
         for (int j = 0; j < NT; ++j)
-            for (int i = 0; i < 4; ++i) {
-                // a NaN score counts as excluded, as the page's "score > NEG_LARGE/2" test does
-                const float pv = (s[j][i] > -INFINITY) ? __builtin_amdgcn_exp2f(s[j][i] - mu) : 0.f;
-                ls += pv;
-                const HiLo v = split16(pv);
-                phi[j >> 1][4 * (j & 1) + i] = v.hi;
-                plo[j >> 1][4 * (j & 1) + i] = v.lo;
+            for (int i = 0; i < 4; i += 2) {
+                // p = 2^(s mult - mu): an excluded key's exp2(-inf) is 0, and the max with 0 turns
+                // a NaN score into 0 (a NaN counts as excluded, as the page's "score >
+                // NEG_LARGE/2" test does)
+                const float p0 = fmaxf(__builtin_amdgcn_exp2f(fmaf(s[j][i], mult, -mu)), 0.f);
+                const float p1 = fmaxf(__builtin_amdgcn_exp2f(fmaf(s[j][i + 1], mult, -mu)), 0.f);
+                ls += p0;
+                ls += p1;
+                half2_t h2, l2;
+                split16x2u(p0, p1, one, h2, l2);
+                phi[j >> 1][4 * (j & 1) + i] = h2[0];
+                phi[j >> 1][4 * (j & 1) + i + 1] = h2[1];
+                plo[j >> 1][4 * (j & 1) + i] = l2[0];
+                plo[j >> 1][4 * (j & 1) + i + 1] = l2[1];
             }
         ls += __shfl_xor(ls, 16, 64);
         ls += __shfl_xor(ls, 32, 64);
@@ -350,14 +401,14 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next group's query loads (above)
         if (vrow && g16 == 0) {
             const long long p = (long long)e * a.qhead + qh;
-            a.m[p] = (mx == -INFINITY) ? kNegLarge : mx * kLn2;
+            a.m[p] = (mx == -INFINITY) ? kNegLarge : mu * kLn2;
             a.l[p] = ls;
         }
         for (int h = 0; h < 2; ++h) {
             const int r = 16 * grp + 8 * h + (ln >> 3);  // the item row this lane stores
             const bool rvalid = r < nrows;
-            const long long pr =
-                (long long)er[rvalid ? r / a.qhead : 0][0] * a.qhead + r % a.qhead;
+            const RowIx sx = row_split(rvalid ? r : 0, a.qhead, qinv);
+            const long long pr = (long long)er[sx.ix][0] * a.qhead + sx.qh;
             float *dst = a.o + pr * D + 4 * (ln & 7);
             for (int j = 0; j < NDT / 2; ++j) {
                 // slab row r (128 bytes) holds its 16-byte chunk c at c ^ ((r >> 1) & 3): the
@@ -511,13 +562,17 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     }
     __syncthreads();
     if (has_task) {
+        const float kf = ldexpf(1.f, kOpExp - eK);
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * t4 + r;
             half8_t hi, lo;
-            for (int x = 0; x < 8; ++x) {
-                const HiLo v = split16r(ldexpf(kr[r][x], -eK));
-                hi[x] = v.hi;
-                lo[x] = v.lo;
+            for (int x = 0; x < 8; x += 2) {
+                half2_t h2, l2;
+                split16x2(kr[r][x], kr[r][x + 1], kf, h2, l2);
+                hi[x] = h2[0];
+                hi[x + 1] = h2[1];
+                lo[x] = l2[0];
+                lo[x + 1] = l2[1];
             }
             // dims 4q .. are chunk q/2, dims D/2 + 4q .. chunk KQ/2 + q/2, at half (q & 1)
             const int off0 = t * D + 8 * swz(t, q >> 1, KQ) + 4 * (q & 1);
@@ -532,12 +587,15 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
         const int vq = 4 * (t4 >> 3) + (t4 & 3), vh = 4 * ((t4 >> 2) & 1);
         for (int x = 0; x < 8; ++x) {
             const int d = x < 4 ? 4 * q + x : D / 2 + 4 * q + (x - 4);
-            const int ed = s_ev[d];
+            const float vf = ldexpf(1.f, -s_ev[d]);
             half4_t hi, lo;
-            for (int r = 0; r < 4; ++r) {
-                const HiLo v = split16(ldexpf(vr[r][x], -ed));
-                hi[r] = v.hi;
-                lo[r] = v.lo;
+            for (int r = 0; r < 4; r += 2) {
+                half2_t h2, l2;
+                split16x2(vr[r][x], vr[r + 1][x], vf, h2, l2);
+                hi[r] = h2[0];
+                hi[r + 1] = h2[1];
+                lo[r] = l2[0];
+                lo[r + 1] = l2[1];
             }
             const int off = d * BSP + 8 * swz(d, vq, VC) + vh;
             *(half4_t *)(Vhi + off) = hi;
@@ -551,10 +609,11 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     constexpr bool kPrefetchQ = D <= 128;
     const int nrows = nE * a.qhead;
     float4_t nq[D / 32][2];
-    if (kPrefetchQ && 16 * wave < nrows) load_q<D>(a, s_er, wave, nrows, h, lane, nq);
+    const float qinv = 1.f / (float)a.qhead;
+    if (kPrefetchQ && 16 * wave < nrows) load_q<D>(a, s_er, wave, nrows, h, lane, qinv, nq);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     edge_groups<D, NT, NW, kPrefetchQ>(a, Khi, Klo, Vhi, Vlo, slab, s_vmul, s_er, nrows, h, eK,
-                                       mmask, lane, wave, nq);
+                                       mmask, lane, wave, qinv, nq);
 }
 
 }  // namespace
