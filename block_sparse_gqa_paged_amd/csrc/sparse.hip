@@ -392,41 +392,43 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
                 if (dt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // Stores, o scaled back by 2^eV of each dim. Lane (g16, n16) holds dims 16dt + 4g16 .. +3 of row
-        // n16, so a direct store instruction would write 64 bytes into each of 16 rows; at this
-        // occupancy that writes HBM about 20% slower than whole 128-byte lines. Each 128-byte
-        // line j of 8 rows goes through the wave's 1 KB LDS slab instead and leaves as one
-        // store of 8 whole lines (lane l: row 8h + l/8, dims 32j + 4(l%8) ..), non-temporal (the
-        // 2 GB of partials are read back only by the merge). m and l come from g16 == 0.
+        // Stores, o scaled back by 2^eV of each dim. Lane (g16, n16) holds dims 16dt + 4g16 .. +3
+        // of row n16, so a direct store instruction would write 64 bytes into each of 16 rows; at
+        // this occupancy that writes HBM about 20% slower than whole 128-byte lines. Each
+        // 128-byte line j of 8 rows goes through the wave's 1 KB LDS slab instead and leaves as
+        // one store of 8 whole lines (lane l: row 8h + l/8, dims 32j + 4(l%8) ..), non-temporal
+        // (the 2 GB of partials are read back only by the merge), scaled on the way out. m and
+        // l come from g16 == 0.
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next group's query loads (above)
         if (vrow && g16 == 0) {
             const long long p = (long long)e * a.qhead + qh;
             a.m[p] = (mx == -INFINITY) ? kNegLarge : mu * kLn2;
             a.l[p] = ls;
         }
+        const int lr = ln >> 3;  // the slab row this lane reads: row 8h + lr of the group
+        float *dst[2];
+        bool rvalid[2];
         for (int h = 0; h < 2; ++h) {
-            const int r = 16 * grp + 8 * h + (ln >> 3);  // the item row this lane stores
-            const bool rvalid = r < nrows;
-            const RowIx sx = row_split(rvalid ? r : 0, a.qhead, qinv);
-            const long long pr = (long long)er[sx.ix][0] * a.qhead + sx.qh;
-            float *dst = a.o + pr * D + 4 * (ln & 7);
-            for (int j = 0; j < NDT / 2; ++j) {
-                // slab row r (128 bytes) holds its 16-byte chunk c at c ^ ((r >> 1) & 3): the
-                // 8 rows written at one chunk, and the two rows read per 16 lanes, then cover
-                // distinct banks (rows r and r + 2 start on the same bank)
+            const int r = 16 * grp + 8 * h + lr;  // the item row this lane stores
+            rvalid[h] = r < nrows;
+            const RowIx rs = row_split(rvalid[h] ? r : 0, a.qhead, qinv);
+            dst[h] = a.o + ((long long)er[rs.ix][0] * a.qhead + rs.qh) * D + 4 * (ln & 7);
+        }
+        // slab row r (128 bytes) holds its 16-byte chunk c at c ^ ((r >> 1) & 3): the 8 rows
+        // written at one chunk, and the two rows read per 16 lanes, then cover distinct banks
+        // (rows r and r + 2 start on the same bank)
+        const int wr = n16 & 7, wx = (wr >> 1) & 3;  // the slab row this lane writes
+        for (int j = 0; j < NDT / 2; ++j) {
+            // 2^eV of the 4 dims this lane stores in line j
+            const float4_t mj = *(const float4_t *)(s_vmul + 32 * j + 4 * (ln & 7));
+            for (int h = 0; h < 2; ++h) {
                 if ((n16 >> 3) == h) {
-                    const int sr = n16 & 7, sx = (sr >> 1) & 3;
-                    float *rowp = slab + sr * 32;
-                    const float4_t m0 = *(const float4_t *)(s_vmul + 32 * j + 4 * g16);
-                    const float4_t m1 = *(const float4_t *)(s_vmul + 32 * j + 16 + 4 * g16);
-                    const float4_t v0 = o[2 * j] * m0, v1 = o[2 * j + 1] * m1;
-                    *(float4_t *)(rowp + 4 * (g16 ^ sx)) = v0;
-                    *(float4_t *)(rowp + 16 + 4 * (g16 ^ sx)) = v1;
+                    *(float4_t *)(slab + wr * 32 + 4 * (g16 ^ wx)) = o[2 * j];
+                    *(float4_t *)(slab + wr * 32 + 16 + 4 * (g16 ^ wx)) = o[2 * j + 1];
                 }
-                const int lr = ln >> 3;
                 const float4_t v =
                     *(const float4_t *)(slab + lr * 32 + 4 * ((ln & 7) ^ ((lr >> 1) & 3)));
-                if (rvalid) __builtin_nontemporal_store(v, (float4_t *)(dst + 32 * j));
+                if (rvalid[h]) __builtin_nontemporal_store(v * mj, (float4_t *)(dst[h] + 32 * j));
             }
         }
     }
@@ -551,6 +553,13 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
         }
     }
     __syncthreads();
+    // the first group's query rows, loaded while the block is split (the edge records are in
+    // LDS since the barrier above)
+    constexpr bool kPrefetchQ = D <= 128;
+    const int nrows = nE * a.qhead;
+    float4_t nq[D / 32][2];
+    const float qinv = 1.f / (float)a.qhead;
+    if (kPrefetchQ && 16 * wave < nrows) load_q<D>(a, s_er, wave, nrows, h, lane, qinv, nq);
     for (int i = 0; i < NW; ++i) mk = fmaxf(mk, s_kmax[i]);
     const int eK = pow2_exp(mk);
     if ((int)threadIdx.x < D) {
@@ -604,13 +613,9 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     }
     __syncthreads();
 
-    // With D <= 128 each group's query operands are loaded one group ahead (the first here). At
-    // D = 256 the second set of query registers does not fit: each group loads its own rows.
-    constexpr bool kPrefetchQ = D <= 128;
-    const int nrows = nE * a.qhead;
-    float4_t nq[D / 32][2];
-    const float qinv = 1.f / (float)a.qhead;
-    if (kPrefetchQ && 16 * wave < nrows) load_q<D>(a, s_er, wave, nrows, h, lane, qinv, nq);
+    // With D <= 128 each group's query operands are loaded one group ahead (the first during
+    // the split above). At D = 256 the second set of query registers does not fit: each group
+    // loads its own rows.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     edge_groups<D, NT, NW, kPrefetchQ>(a, Khi, Klo, Vhi, Vlo, slab, s_vmul, s_er, nrows, h, eK,
                                        mmask, lane, wave, qinv, nq);
