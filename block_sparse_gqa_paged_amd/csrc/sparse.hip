@@ -465,6 +465,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     float *slab = slabs + (threadIdx.x >> 6) * 256;
     static_assert(NW * D <= NW * 256, "per-wave |V| maxima fit the store slabs");
     __shared__ float s_kmax[NW];                        // per-wave maxima of |K|
+    __shared__ int s_len[NW];                           // per-wave longest edge
     __shared__ int s_ev[D];                             // per-dimension exponent of V
     // 2^s_ev: output scale per dimension, read as float4 (16-byte aligned)
     __shared__ __attribute__((aligned(16))) float s_vmul[D];
@@ -532,6 +533,13 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
         }
     }
     if (has_edge) s_er[threadIdx.x] = erec;
+    // Keys at or past the item's longest edge serve none of its edges; past a sequence's used
+    // length a mapped page may hold stale rows, NaN included. Those keys' rows are stored as
+    // zeros in the planes (the maxima below skip NaN), so that nothing of them reaches the
+    // output, not even as 0 * NaN in the PV products.
+    int lmax = has_edge ? erec[2] : 0;
+    for (int o = 32; o > 0; o >>= 1) lmax = max(lmax, __shfl_xor(lmax, o, 64));
+    if (lane == 0) s_len[wave] = lmax;
     float mk = 0.f, mv[8];
     for (int x = 0; x < 8; ++x) {
         mv[x] = 0.f;
@@ -572,6 +580,13 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     __syncthreads();
     if (has_task) {
         const float kf = ldexpf(1.f, kOpExp - eK);
+        lmax = 0;
+        for (int i = 0; i < NW; ++i) lmax = max(lmax, s_len[i]);
+        lmax = __builtin_amdgcn_readfirstlane(lmax);  // uniform
+        if (lmax < BSP)  // uniform: some keys of the block serve no edge
+            for (int r = 0; r < 4; ++r)
+                if (4 * t4 + r >= lmax)
+                    for (int x = 0; x < 8; ++x) { kr[r][x] = 0.f; vr[r][x] = 0.f; }
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * t4 + r;
             half8_t hi, lo;

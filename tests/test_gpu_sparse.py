@@ -130,6 +130,46 @@ def test_wide_dynamic_range(case, causal):
     assert_sparse_out_close(out, merged, "wide merged", terms=terms)
 
 
+def _poison_past_used(sw):
+    """Copy of sw whose cache rows at key positions >= each batch's used length (on mapped
+    pages) hold NaN: rows that no edge reads (block_len stops before them)."""
+    k, v = sw["k_pages"].copy(), sw["v_pages"].copy()
+    ps, n = sw["page_size"], 0
+    for b in range(sw["batch"]):
+        used = int(sw["used_kv_lens"][b])
+        for t in range(used, sw["max_pages"] * ps):
+            pid = int(sw["block_tables"][b, t // ps])
+            if pid < 0:
+                continue
+            k[pid, :, t % ps, :] = np.nan
+            v[pid, :, t % ps, :] = np.nan
+            n += 1
+    assert n > 0
+    return dict(sw, k_pages=k, v_pages=v)
+
+
+@pytest.mark.parametrize("seed,kw", [(214, {}), (215, dict(head_dim=64, block_size=32,
+                                                            page_size=8, qhead=2))],
+                         ids=["d128", "d64"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_poison_past_used_length(seed, kw, causal):
+    """Rows past the used length do not reach the partials: the result equals the oracle's on
+    the clean cache (the oracle never reads those rows, so its result is the same either way)."""
+    sw = _tiny(seed, **kw)
+    q_pos = sw["q_pos"] if causal else None
+    ref = oracle.sparse_forward(sw, q_pos=q_pos)
+    bad = _poison_past_used(sw)
+    ref_bad = oracle.sparse_forward(bad, q_pos=q_pos)
+    for x, y in zip(ref, ref_bad):
+        np.testing.assert_array_equal(x, y)
+    c = dev.SparseCase(bad)
+    got = c.forward(causal=causal)
+    torch.cuda.synchronize()
+    for t in got:
+        assert torch.isfinite(t).all()
+    assert_sparse_partials_close(got, ref, "poisoned partials")
+
+
 def test_sentinels_and_out_of_range_edges():
     sw = _tiny(210)
     em = sw["edge_meta"].copy()
