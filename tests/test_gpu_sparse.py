@@ -43,6 +43,10 @@ TINY = [
     # q-head lanes beyond one 16-row group: an edge's rows span groups
     dict(seed=212, qhead=32, hkv=1, head_dim=64, block_size=32, page_size=8),
     dict(seed=213, qhead=24, hkv=2, head_dim=128),
+    # more key blocks (17002) than the LDS histogram of the chunked edge sort holds: the sort
+    # takes its global-atomic form
+    dict(seed=216, hkv=1, qhead=2, head_dim=64, block_size=16, page_size=16,
+         key_capacity=16 * 8500, p_random=0.02),
 ]
 
 
