@@ -8,11 +8,13 @@
 //
 // MI355X design:
 //  * Edges are grouped by their (batch, h, blk) key block with a counting sort on the device:
-//    a histogram whose atomic returns each edge's rank, a scan that also writes one record per
-//    work item, and a scatter of packed edge records (id, query, final key count) into sorted
-//    order. One workgroup then stages a key block in LDS once and reuses it for up to kChunk
-//    edges; results per edge do not depend on the grouping or the order. A work item starts
-//    with three dependent loads (its record; its edge records and block table entries; K and V).
+//    per-chunk LDS histograms that give each edge its rank (no global atomics; a global-atomic
+//    histogram for shapes with more key blocks than LDS holds), scans that also write one record
+//    per work item, and a scatter of packed edge records (id, query, final key count) into
+//    sorted order. One workgroup then stages a key block in LDS once and reuses it for up to
+//    kChunk edges; results per edge do not depend on the grouping or the order. A work item
+//    starts with three dependent loads (its record; its edge records and block table entries;
+//    K and V).
 //  * fp32 products run as three fp16 MFMAs (v_mfma_f32_16x16x32_f16) on split operands. Before
 //    the split, each query row, the block's K and each dimension of the block's V are scaled by
 //    a power of two that brings their largest magnitude into [0.5, 1) (exact; folded back into
@@ -36,7 +38,7 @@
 //
 // Edges whose batch, head, block or query index lie outside the shapes write the sentinel.
 // With q_pos (the causal entry), an edge sees only keys at positions <= q_pos[q_idx]: its length
-// is cut to that prefix when the item's edge list is staged.
+// is cut to that prefix in its sorted record.
 #include "common.h"
 
 namespace pa {
