@@ -18,7 +18,8 @@
 //  * fp32 products run as three fp16 MFMAs (v_mfma_f32_16x16x32_f16) on split operands. Before
 //    the split, each query row, the block's K and each dimension of the block's V are scaled by
 //    a power of two that brings their largest magnitude into [0.5, 1) (exact; folded back into
-//    the scores and, per dimension, into the output). Q and K are scaled by another 2^11 and
+//    the scores and, per dimension, into the output; capped at 2^126 for maxima far below
+//    2^-100, so that the factor stays finite). Q and K are scaled by another 2^11 and
 //    split as x = hi + lo, hi = fp16(x), lo = fp16(x - hi): lo stays a normal fp16 number for
 //    elements down to 2^-14 of the maximum, so each operand keeps 22 significant bits over that
 //    range; 2^22 q.k ~ hi.hi + (hi.lo + lo.hi), the two sums in separate fp32 accumulators that
@@ -345,6 +346,11 @@ __device__ __forceinline__ void split16x2u(float x0, float x1, float one, half2_
 // with no separate scaling of the remainder.
 constexpr int kOpExp = 11;
 
+// Scaling shift 2^sh for a maximum of exponent e (pow2_exp): top - e, capped at 126 so that 2^sh
+// stays a finite float (only elements far below 2^-100 reach the cap; they then scale to less
+// than the top, which they keep as fp16 subnormals).
+__device__ __forceinline__ int scale_shift(int top, int e) { return min(top - e, 126); }
+
 // Item row r -> (edge within the item, q-head lane), r = ix * d + qh, with inv = 1 / d. Rows
 // number at most 128 d + 15, so the quotient is at most 143 and its float estimate is off by
 // less than 1e-4: truncation is the quotient or one away from it, and one step either way
@@ -397,9 +403,10 @@ __device__ __forceinline__ void load_q(const SparseArgs &a, const int4_t *er, in
 // row r = edge r / qhead, lane r mod qhead; a wave takes 16 consecutive rows at a time (groups
 // wave, wave + NW, ...; 16 / qhead whole edges when qhead divides 16). Lane (g16, n16) serves
 // row n16 of the group. K (row-major) and V (transposed) are the block's fp16 hi/lo planes, er
-// the item's edge records, mmask the mapped-key bits, eK the block's K exponent and s_vmul the
-// per-dimension V scales; lane and wave are the thread's (a caller may pass values the compiler
-// cannot see through, to keep the per-lane offsets from being hoisted out of its loop).
+// the item's edge records, mmask the mapped-key bits, kshift the block's K scaling shift (K was
+// multiplied by 2^kshift) and s_vmul the per-dimension output scales (2^-shift of each V
+// dimension); lane and wave are the thread's (a caller may pass values the compiler cannot see
+// through, to keep the per-lane offsets from being hoisted out of its loop).
 //
 // On entry nq holds the query operands of the wave's first group when kPrefetch (loaded and
 // waited for by the caller). Each group waits for all of the wave's outstanding memory
@@ -408,7 +415,7 @@ template <int D, int NT, int NW, bool kPrefetch>
 __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *Khi,
                                             const half_t *Klo, const half_t *Vhi,
                                             const half_t *Vlo, float *slab, const float *s_vmul,
-                                            const int4_t *er, int nrows, int h, int eK,
+                                            const int4_t *er, int nrows, int h, int kshift,
                                             const uint64_t (&mmask)[(16 * NT + 63) / 64],
                                             int lane, int wave, float qinv,
                                             float4_t (&nq)[D / 32][2]) {
@@ -452,7 +459,8 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         qmx = wave_max_xor(qmx, 16);
         qmx = wave_max_xor(qmx, 32);
         const int eQ = pow2_exp(qmx);
-        const float qf = ldexpf(1.f, kOpExp - eQ);
+        const int qshift = scale_shift(kOpExp, eQ);
+        const float qf = ldexpf(1.f, qshift);
         half8_t qhi[KB], qlo[KB];
         for (int kb = 0; kb < KB; ++kb)
             for (int c = 0; c < 2; ++c)
@@ -465,7 +473,7 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
                     qlo[kb][4 * c + i + 1] = l2[1];
                 }
         // a score in log2 units is its product sum times mult (> 0)
-        const float mult = ldexpf(a.scale_log2, eQ + eK - 2 * kOpExp);
+        const float mult = ldexpf(a.scale_log2, -qshift - kshift);
         // The next group's query operands are loaded here, and the one wait for them sits right
         // before this group's stores. A wait for a load while stores are outstanding has to
         // drain the stores too (loads and stores share the counter and may complete out of
@@ -554,7 +562,7 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
                 if (dt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // Stores, o scaled back by 2^eV of each dim. Lane (g16, n16) holds dims 16dt + 4g16 .. +3
+        // Stores, o scaled back by each dim's s_vmul. Lane (g16, n16) holds dims 16dt + 4g16 .. +3
         // of row n16, so a direct store instruction would write 64 bytes into each of 16 rows; at
         // this occupancy that writes HBM about 20% slower than whole 128-byte lines. Each
         // 128-byte line j of 8 rows goes through the wave's 1 KB LDS slab instead and leaves as
@@ -581,7 +589,7 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         // (rows r and r + 2 start on the same bank)
         const int wr = n16 & 7, wx = (wr >> 1) & 3;  // the slab row this lane writes
         for (int j = 0; j < NDT / 2; ++j) {
-            // 2^eV of the 4 dims this lane stores in line j
+            // the output scales of the 4 dims this lane stores in line j
             const float4_t mj = *(const float4_t *)(s_vmul + 32 * j + 4 * (ln & 7));
             for (int h = 0; h < 2; ++h) {
                 if ((n16 >> 3) == h) {
@@ -628,8 +636,8 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     static_assert(NW * D <= NW * 256, "per-wave |V| maxima fit the store slabs");
     __shared__ float s_kmax[NW];                        // per-wave maxima of |K|
     __shared__ int s_len[NW];                           // per-wave longest edge
-    __shared__ int s_ev[D];                             // per-dimension exponent of V
-    // 2^s_ev: output scale per dimension, read as float4 (16-byte aligned)
+    __shared__ int s_ev[D];                             // per-dimension scaling shift of V
+    // 2^-s_ev: output scale per dimension, read as float4 (16-byte aligned)
     __shared__ __attribute__((aligned(16))) float s_vmul[D];
     __shared__ __attribute__((aligned(16))) int4_t s_er[kChunk];  // the item's edge records
 
@@ -731,17 +739,18 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     const float qinv = 1.f / (float)a.qhead;
     if (kPrefetchQ && 16 * wave < nrows) load_q<D>(a, s_er, wave, nrows, h, lane, qinv, nq);
     for (int i = 0; i < NW; ++i) mk = fmaxf(mk, s_kmax[i]);
-    const int eK = pow2_exp(mk);
+    const int kshift = scale_shift(kOpExp, pow2_exp(mk));
     if ((int)threadIdx.x < D) {
         float m = 0.f;
         for (int i = 0; i < NW; ++i) m = fmaxf(m, slabs[i * D + threadIdx.x]);
         const int e = pow2_exp(m);
-        s_ev[threadIdx.x] = e;
-        s_vmul[threadIdx.x] = ldexpf(1.f, e);
+        const int vsh = scale_shift(0, e);
+        s_ev[threadIdx.x] = vsh;
+        s_vmul[threadIdx.x] = ldexpf(1.f, -vsh);
     }
     __syncthreads();
     if (has_task) {
-        const float kf = ldexpf(1.f, kOpExp - eK);
+        const float kf = ldexpf(1.f, kshift);
         lmax = 0;
         for (int i = 0; i < NW; ++i) lmax = max(lmax, s_len[i]);
         lmax = __builtin_amdgcn_readfirstlane(lmax);  // uniform
@@ -773,7 +782,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
         const int vq = 4 * (t4 >> 3) + (t4 & 3), vh = 4 * ((t4 >> 2) & 1);
         for (int x = 0; x < 8; ++x) {
             const int d = x < 4 ? 4 * q + x : D / 2 + 4 * q + (x - 4);
-            const float vf = ldexpf(1.f, -s_ev[d]);
+            const float vf = ldexpf(1.f, s_ev[d]);
             half4_t hi, lo;
             for (int r = 0; r < 4; r += 2) {
                 half2_t h2, l2;
@@ -794,8 +803,8 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     // the split above). At D = 256 the second set of query registers does not fit: each group
     // loads its own rows.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    edge_groups<D, NT, NW, kPrefetchQ>(a, Khi, Klo, Vhi, Vlo, slab, s_vmul, s_er, nrows, h, eK,
-                                       mmask, lane, wave, qinv, nq);
+    edge_groups<D, NT, NW, kPrefetchQ>(a, Khi, Klo, Vhi, Vlo, slab, s_vmul, s_er, nrows, h,
+                                       kshift, mmask, lane, wave, qinv, nq);
 }
 
 }  // namespace

@@ -174,6 +174,26 @@ def test_poison_past_used_length(seed, kw, causal):
     assert_sparse_partials_close(got, ref, "poisoned partials")
 
 
+def test_magnitudes_far_below_one():
+    """Query rows and key blocks near 1e-36 and values near 1e-39 (fp32 subnormals): the power
+    of two that scales each row, block or value dimension up before the fp16 split is capped so
+    that it stays finite. Scores underflow to 0 on both sides (uniform weights); the partials
+    stay finite and o matches the oracle's relative to its largest element."""
+    sw = _tiny(217, head_dim=64, block_size=32, page_size=8, qhead=2)
+    sw = dict(sw, q_buf=sw["q_buf"] * np.float32(1e-36), k_pages=sw["k_pages"] * np.float32(1e-36),
+              v_pages=sw["v_pages"] * np.float32(1e-39))
+    ref = oracle.sparse_forward(sw)
+    c = dev.SparseCase(sw)
+    o, m, l = (t.cpu().numpy() for t in c.forward())
+    for t in (o, m, l):
+        assert np.isfinite(t).all()
+    np.testing.assert_allclose(m, ref[1], atol=1e-4)
+    np.testing.assert_allclose(l, ref[2], rtol=1e-5, atol=1e-5)
+    scale = np.abs(ref[0]).max()
+    assert scale > 0
+    assert np.abs(o - ref[0]).max() <= 1e-3 * scale, np.abs(o - ref[0]).max() / scale
+
+
 def test_sentinels_and_out_of_range_edges():
     sw = _tiny(210)
     em = sw["edge_meta"].copy()
