@@ -68,9 +68,11 @@ bool sort_chunked(int E, int units) {
     return units <= kHistUnits && chunks * units <= kMaxChunkCounts;
 }
 
-// Work-item record: its key block (unit), first edge in the sorted order, and edge count.
+// Work-item record, two 16-byte words: its key block (unit), first edge in the sorted order and
+// edge count; then, for blocks of up to 4 pages, the block's page ids (checked: -1 for an
+// unmapped or out-of-range entry), so that the forward kernel reads no table entry itself.
 // Sorted edge record: edge id, query index and the edge's key count (clamped to the block,
-// cut to the query's causal limit). Each is one 16-byte load for the forward kernel.
+// cut to the query's causal limit). One 16-byte load for the forward kernel.
 struct SparseWs {
     int32_t *counts, *rank, *offs, *nitems;
     int32_t *chunk_counts;  // chunked sort: [chunks][units], then offsets within each block
@@ -94,7 +96,7 @@ size_t layout(SparseWs *w, int32_t *ws, int E, int units) {
     o[1] = off; off = al(off + E);                 // rank
     o[2] = off; off = al(off + units + 1);         // offs
     o[3] = off; off = al(off + 1);                 // nitems
-    o[4] = off; off = al(off + 4 * max_items);     // items
+    o[4] = off; off = al(off + 8 * max_items);     // items (two 16-byte records each)
     o[5] = off; off = al(off + 4 * (size_t)E);     // edges (sorted)
     o[6] = off; off = al(off + chunks * units);    // chunk counts
     o[7] = off; off = al(off + (chunked ? 2 * (size_t)units : 0));   // lo
@@ -121,6 +123,27 @@ __device__ __forceinline__ bool decode_edge(const SparseArgs &a, int e, int &q, 
     len = min(len, a.block_size);
     unit = (b * a.hkv + h) * a.nblk + blk;
     return true;
+}
+
+// Block-table page of key t of the block at (b, blk), or -1 (past the block, past the table row,
+// or an unmapped or out-of-range entry).
+__device__ __forceinline__ int block_page(const SparseArgs &a, const int32_t *btrow, int blk,
+                                          int t) {
+    const int slot = blk * a.ppb + t / a.page_size;
+    int pid = -1;
+    if (t < a.block_size && slot < a.max_pages) pid = btrow[slot];
+    return (pid >= 0 && pid < a.num_pages) ? pid : -1;
+}
+
+// The page ids of key block u's page slots 0..3 (-1 past the block's pages) when a block has at
+// most 4 pages; all -1 otherwise (the forward kernel then reads the table).
+__device__ int4_t item_pages(const SparseArgs &a, int u) {
+    int4_t p = {-1, -1, -1, -1};
+    if (a.ppb > 4) return p;
+    const int blk = u % a.nblk, b = u / a.nblk / a.hkv;
+    const int32_t *btrow = a.bt + (long long)b * a.max_pages;
+    for (int sl = 0; sl < a.ppb; ++sl) p[sl] = block_page(a, btrow, blk, sl * a.page_size);
+    return p;
 }
 
 __global__ void sp_zero(int32_t *p, int n) {
@@ -259,8 +282,14 @@ __global__ void sp_cscatter(SparseArgs a, SparseWs w) {
         const int s = i / kUnitsPerScan;
         const int ebase = w.wtot[2 * s] + w.lo[2 * i], ibase = w.wtot[2 * s + 1] + w.lo[2 * i + 1];
         const int c = w.counts[i];
-        for (int k = 0; k * kChunk < c; ++k)
-            w.items[ibase + k] = int4_t{i, ebase + k * kChunk, min(kChunk, c - k * kChunk), 0};
+        if (c > 0) {
+            const int4_t pg = item_pages(a, i);
+            for (int k = 0; k * kChunk < c; ++k) {
+                w.items[2 * (ibase + k)] =
+                    int4_t{i, ebase + k * kChunk, min(kChunk, c - k * kChunk), 0};
+                w.items[2 * (ibase + k) + 1] = pg;
+            }
+        }
     }
     if (i >= a.E) return;
     int q, h, blk, b, len, unit;
@@ -302,8 +331,13 @@ __global__ __launch_bounds__(1024) void sp_scan(SparseArgs a, SparseWs w) {
     for (int u = u0; u < u1; ++u) {
         const int c = w.counts[u], ni = (c + kChunk - 1) / kChunk;
         w.offs[u] = oe;
-        for (int k = 0; k < ni; ++k)
-            w.items[oi + k] = int4_t{u, oe + k * kChunk, min(kChunk, c - k * kChunk), 0};
+        if (ni > 0) {
+            const int4_t pg = item_pages(a, u);
+            for (int k = 0; k < ni; ++k) {
+                w.items[2 * (oi + k)] = int4_t{u, oe + k * kChunk, min(kChunk, c - k * kChunk), 0};
+                w.items[2 * (oi + k) + 1] = pg;
+            }
+        }
         oe += c;
         oi += ni;
     }
@@ -604,15 +638,6 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
     }
 }
 
-// Block-table page of key t of the block at (b, blk), or -1 (past the block, past the table row,
-// or an unmapped or out-of-range entry).
-__device__ __forceinline__ int block_page(const SparseArgs &a, const int32_t *btrow, int blk,
-                                          int t) {
-    const int slot = blk * a.ppb + t / a.page_size;
-    int pid = -1;
-    if (t < a.block_size && slot < a.max_pages) pid = btrow[slot];
-    return (pid >= 0 && pid < a.num_pages) ? pid : -1;
-}
 
 // Workgroup per work item: stages its key block from HBM into the fp16 planes, then runs the
 // edge groups. For the shapes whose planes and raw rows do not both fit in LDS (D = 256, or
@@ -645,7 +670,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     // workspace; a record past the count holds no defined value and is not used).
     const int item = blockIdx.x;
     const int nitems = w.nitems[0];
-    const int4_t rec = w.items[item];
+    const int4_t rec = w.items[2 * item], pg = w.items[2 * item + 1];
     if (item >= nitems) return;
     const int u = rec[0], ebeg = rec[1], nE = rec[2];
     const int blk = u % a.nblk;
@@ -655,9 +680,10 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     const int32_t *btrow = a.bt + (long long)b * a.max_pages;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-    // The item's sorted edge records (id, query index, key count) are loaded first, beside the
-    // block table entries; the K and V loads follow as soon as the page ids arrive, and the edge
-    // records go to LDS after them (loads return in order: this waits for the records only).
+    // The item's sorted edge records (id, query index, key count) are loaded first; the K and V
+    // loads follow at once (page ids from the item record; for blocks of more than 4 pages they
+    // wait for the table entries), and the edge records go to LDS after them (loads return in
+    // order: this waits for the records only).
     const bool has_edge = (int)threadIdx.x < nE;
     int4_t erec = {0, 0, 0, 0};
     if (has_edge) erec = w.edges[ebeg + threadIdx.x];
@@ -679,13 +705,20 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     const int task = threadIdx.x;
     const bool has_task = task < TASKS;
     const int t4 = task / KQ, q = task - t4 * KQ;
+    // page of key t: from the item record (blocks of up to 4 pages) or the table
+    auto page_of = [&](int t) {
+        if (a.ppb > 4) return block_page(a, btrow, blk, t);
+        if (t >= a.block_size) return -1;
+        const int sl = t / a.page_size;
+        return sl == 0 ? pg[0] : (sl == 1 ? pg[1] : (sl == 2 ? pg[2] : pg[3]));
+    };
     int pids[4];
-    for (int r = 0; r < 4; ++r) pids[r] = has_task ? block_page(a, btrow, blk, 4 * t4 + r) : -1;
+    for (int r = 0; r < 4; ++r) pids[r] = has_task ? page_of(4 * t4 + r) : -1;
     // mapped-key masks (wave-uniform): bit t set when key t sits on a mapped page
     uint64_t mmask[MW];
     for (int hw = 0; hw < MW; ++hw) {
         const int t = 64 * hw + lane;
-        mmask[hw] = __ballot(t < BSP && block_page(a, btrow, blk, t) >= 0);
+        mmask[hw] = __ballot(t < BSP && page_of(t) >= 0);
     }
     for (int r = 0; r < 4; ++r) {
         const int t = 4 * t4 + r;
