@@ -608,8 +608,9 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next group's query loads (above)
         if (vrow && g16 == 0) {
             const long long p = (long long)e * a.qhead + qh;
-            a.m[p] = (mx == -INFINITY) ? kNegLarge : mu * kLn2;
-            a.l[p] = ls;
+            // 16 bytes per edge and array, scattered: non-temporal, like the o rows
+            __builtin_nontemporal_store((mx == -INFINITY) ? kNegLarge : mu * kLn2, a.m + p);
+            __builtin_nontemporal_store(ls, a.l + p);
         }
         const int lr = ln >> 3;  // the slab row this lane reads: row 8h + lr of the group
         float *dst[2];
