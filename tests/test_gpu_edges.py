@@ -41,6 +41,9 @@ CASES = [
     dict(seed=309, tq=200, hkv=8, nblk=512, batch=2, density=0.06),
     dict(seed=311, tq=45, hkv=3, nblk=256, batch=2, density=0.1),    # 4 rows per load
     dict(seed=312, tq=300, hkv=8, nblk=64, batch=3, density=0.08),   # many workgroups
+    # denser rows at the workload's nblk: about 490 and 320 edges per 8 rows
+    dict(seed=313, tq=64, hkv=8, nblk=512, batch=2, density=0.12),
+    dict(seed=314, tq=64, hkv=8, nblk=512, batch=2, density=0.078),
 ]
 
 
