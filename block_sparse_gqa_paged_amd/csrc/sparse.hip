@@ -17,16 +17,20 @@
 //    block has at most 4 pages, else the table entries are a third), then its edge records
 //    beside the block's K and V rows.
 //  * fp32 products run as three fp16 MFMAs (v_mfma_f32_16x16x32_f16) on split operands. Before
-//    the split, each query row, the block's K and each dimension of the block's V are scaled by
-//    a power of two that brings their largest magnitude into [0.5, 1) (exact; folded back into
-//    the scores and, per dimension, into the output; capped at 2^126 for maxima far below
-//    2^-100, so that the factor stays finite). Q and K are scaled by another 2^11 and
-//    split as x = hi + lo, hi = fp16(x), lo = fp16(x - hi): lo stays a normal fp16 number for
-//    elements down to 2^-14 of the maximum, so each operand keeps 22 significant bits over that
-//    range; 2^22 q.k ~ hi.hi + (hi.lo + lo.hi), the two sums in separate fp32 accumulators that
-//    are added once per score. V and P: x = hi + lo with lo = fp16(x - hi) (V per dimension and
-//    P <= 1 need no wider range), and p.v ~ hi.hi + hi.lo + lo.hi. The dropped lo.lo terms are
-//    ~2^-22 of each product.
+//    the split, each query row and the block's K are scaled by a power of two that brings their
+//    largest magnitude into [0.5, 1), and so is each dimension of the block's V whose largest
+//    magnitude is below 0.5 or at least 2^15 (exact; folded back into the scores and, per
+//    dimension, into the output, which needs no scaling when no dimension is scaled; capped at
+//    2^126 for maxima far below 2^-100, so that the factor stays finite). Q and K are scaled by
+//    another 2^11 and split as x = hi + lo, hi = fp16(x), lo = fp16(x - hi): lo stays a normal
+//    fp16 number for elements down to 2^-14 of the maximum, so each operand keeps 22
+//    significant bits over that range; 2^22 q.k ~ hi.lo + lo.hi + hi.hi, summed in one fp32
+//    accumulator. V and P: x = hi + lo with lo = fp16(x - hi), and p.v ~ hi.hi + hi.lo + lo.hi;
+//    each element keeps 22 significant bits or an absolute error below 2^-25 in the units of its
+//    scaled dimension (half of fp16's subnormal step), which for a V dimension split as it is
+//    (largest magnitude in [0.5, 2^15)) is at least as fine as after scaling it down; P <= 1
+//    needs no scaling.
+//    The dropped lo.lo terms are ~2^-22 of each product.
 //  * S^T = K . Q^T has 16 keys as rows and 16 query rows as columns; its accumulator gives each
 //    lane 8 keys of one row across two key tiles, exactly the k-slots of the P operand of
 //    O^T = V^T . P^T, so P never leaves registers, and O^T gives each lane four consecutive
@@ -42,6 +46,7 @@
 // With q_pos (the causal entry), an edge sees only keys at positions <= q_pos[q_idx]: its length
 // is cut to that prefix in its sorted record.
 #include "common.h"
+#include <type_traits>
 
 namespace pa {
 namespace {
@@ -454,7 +459,7 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
                                             const int4_t *er, int nrows, int h, int kshift,
                                             const uint64_t (&mmask)[(16 * NT + 63) / 64],
                                             int lane, int wave, float qinv,
-                                            float4_t (&nq)[D / 32][2]) {
+                                            float4_t (&nq)[D / 32][2], bool vone) {
     constexpr int BSP = 16 * NT;             // padded keys per block (NT even)
     constexpr int KB = D / 32;               // 32-dim k-blocks of QK^T
     constexpr int NDT = D / 16;              // 16-dim output tiles
@@ -522,18 +527,18 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         // the cross terms hi.lo + lo.hi in acx).
         float s[NT][4];
         for (int j = 0; j < NT; ++j) {
-            // hi.hi in acc, the scaled cross terms hi.lo + lo.hi in acx
-            float4_t acc = {0.f, 0.f, 0.f, 0.f}, acx = {0.f, 0.f, 0.f, 0.f};
+            // the cross terms hi.lo + lo.hi and hi.hi of each k-block, in one accumulator
+            float4_t acc = {0.f, 0.f, 0.f, 0.f};
             const int t = 16 * j + n16;
             for (int kb = 0; kb < KB; ++kb) {
                 const int off = t * D + 8 * swz(t, 4 * kb + g16, KQ);
                 const half8_t khi = *(const half8_t *)(Khi + off);
                 const half8_t klo = *(const half8_t *)(Klo + off);
-                acx = mfma16x16x32(khi, qlo[kb], acx);
-                acx = mfma16x16x32(klo, qhi[kb], acx);
+                acc = mfma16x16x32(khi, qlo[kb], acc);
+                acc = mfma16x16x32(klo, qhi[kb], acc);
                 acc = mfma16x16x32(khi, qhi[kb], acc);
             }
-            for (int i = 0; i < 4; ++i) s[j][i] = acc[i] + acx[i];
+            for (int i = 0; i < 4; ++i) s[j][i] = acc[i];
             // keep the next tile's LDS operand reads from being hoisted over this tile (each
             // hoisted read holds 4 registers)
             __builtin_amdgcn_sched_barrier(0);
@@ -565,11 +570,14 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         half8_t phi[KK], plo[KK];
         for (int j = 0; j < NT; ++j)
             for (int i = 0; i < 4; i += 2) {
-                // p = 2^(s mult - mu): an excluded key's exp2(-inf) is 0, and the max with 0 turns
-                // a NaN score into 0 (a NaN counts as excluded, as the page's "score >
+                // p = 2^(s mult - mu): an excluded key's exp2(-inf) is 0, and the clamp to [0, 1]
+                // (the exp instruction's clamp modifier; p <= 1 up to the rounding of mu) turns a
+                // NaN score into 0 (a NaN counts as excluded, as the page's "score >
                 // NEG_LARGE/2" test does)
-                const float p0 = fmaxf(__builtin_amdgcn_exp2f(fmaf(s[j][i], mult, -mu)), 0.f);
-                const float p1 = fmaxf(__builtin_amdgcn_exp2f(fmaf(s[j][i + 1], mult, -mu)), 0.f);
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[j][i], mult, -mu));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[j][i + 1], mult, -mu));
+                const float p0 = fminf(fmaxf(e0, 0.f), 1.f);
+                const float p1 = fminf(fmaxf(e1, 0.f), 1.f);
                 ls += p0;
                 ls += p1;
                 half2_t h2, l2;
@@ -625,19 +633,30 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         // written at one chunk, and the two rows read per 16 lanes, then cover distinct banks
         // (rows r and r + 2 start on the same bank)
         const int wr = n16 & 7, wx = (wr >> 1) & 3;  // the slab row this lane writes
-        for (int j = 0; j < NDT / 2; ++j) {
-            // the output scales of the 4 dims this lane stores in line j
-            const float4_t mj = *(const float4_t *)(s_vmul + 32 * j + 4 * (ln & 7));
-            for (int h = 0; h < 2; ++h) {
-                if ((n16 >> 3) == h) {
-                    *(float4_t *)(slab + wr * 32 + 4 * (g16 ^ wx)) = o[2 * j];
-                    *(float4_t *)(slab + wr * 32 + 16 + 4 * (g16 ^ wx)) = o[2 * j + 1];
+        // (two copies of the loop: with the per-dimension scales, and without them when no
+        // dimension of V is scaled)
+        auto lines = [&](auto scaled) {
+            for (int j = 0; j < NDT / 2; ++j) {
+                // the output scales of the 4 dims this lane stores in line j
+                float4_t mj;
+                if constexpr (decltype(scaled)::value)
+                    mj = *(const float4_t *)(s_vmul + 32 * j + 4 * (ln & 7));
+                for (int h = 0; h < 2; ++h) {
+                    if ((n16 >> 3) == h) {
+                        *(float4_t *)(slab + wr * 32 + 4 * (g16 ^ wx)) = o[2 * j];
+                        *(float4_t *)(slab + wr * 32 + 16 + 4 * (g16 ^ wx)) = o[2 * j + 1];
+                    }
+                    float4_t v =
+                        *(const float4_t *)(slab + lr * 32 + 4 * ((ln & 7) ^ ((lr >> 1) & 3)));
+                    if constexpr (decltype(scaled)::value) v = v * mj;
+                    if (rvalid[h]) __builtin_nontemporal_store(v, (float4_t *)(dst[h] + 32 * j));
                 }
-                const float4_t v =
-                    *(const float4_t *)(slab + lr * 32 + 4 * ((ln & 7) ^ ((lr >> 1) & 3)));
-                if (rvalid[h]) __builtin_nontemporal_store(v * mj, (float4_t *)(dst[h] + 32 * j));
             }
-        }
+        };
+        if (vone)
+            lines(std::false_type{});
+        else
+            lines(std::true_type{});
     }
 }
 
@@ -665,6 +684,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     __shared__ float s_kmax[NW];                        // per-wave maxima of |K|
     __shared__ int s_len[NW];                           // per-wave longest edge
     __shared__ int s_ev[D];                             // per-dimension scaling shift of V
+    __shared__ int s_vscaled;                           // some dimension of V is scaled
     // 2^-s_ev: output scale per dimension, read as float4 (16-byte aligned)
     __shared__ __attribute__((aligned(16))) float s_vmul[D];
     __shared__ __attribute__((aligned(16))) int4_t s_er[kChunk];  // the item's edge records
@@ -739,6 +759,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
         }
     }
     if (has_edge) s_er[threadIdx.x] = erec;
+    if (threadIdx.x == 0) s_vscaled = 0;
     // Keys at or past the item's longest edge serve none of its edges; past a sequence's used
     // length a mapped page may hold stale rows, NaN included. Those keys' rows are stored as
     // zeros in the planes (the maxima below skip NaN), so that nothing of them reaches the
@@ -780,11 +801,14 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
         float m = 0.f;
         for (int i = 0; i < NW; ++i) m = fmaxf(m, slabs[i * D + threadIdx.x]);
         const int e = pow2_exp(m);
-        const int vsh = scale_shift(0, e);
+        int vsh = scale_shift(0, e);
+        if (e <= 15) vsh = max(vsh, 0);  // from 0.5 up to 2^15: split as it is
         s_ev[threadIdx.x] = vsh;
         s_vmul[threadIdx.x] = ldexpf(1.f, -vsh);
+        if (vsh != 0) s_vscaled = 1;
     }
     __syncthreads();
+    const bool vone = s_vscaled == 0;  // uniform: no dimension of V is scaled
     if (has_task) {
         const float kf = ldexpf(1.f, kshift);
         lmax = 0;
@@ -840,7 +864,7 @@ __global__ __launch_bounds__(kThreads, (NT * D <= 512 && D <= 128) ? 4 : 2) void
     // loads its own rows.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     edge_groups<D, NT, NW, kPrefetchQ>(a, Khi, Klo, Vhi, Vlo, slab, s_vmul, s_er, nrows, h,
-                                       kshift, mmask, lane, wave, qinv, nq);
+                                       kshift, mmask, lane, wave, qinv, nq, vone);
 }
 
 }  // namespace
