@@ -11,6 +11,8 @@
 //    writes the edge count into group_ptr[tq*hkv].
 //  * emit: the rows are read again, each row's offset is formed, and every kept block writes
 //    its edge at the row offset plus its rank within the row.
+// On the 16-byte path with at most kEbOwnPrefix workgroups, emit forms its workgroup offset from
+// the totals itself and eb_scan is not launched (two passes).
 // Power-of-two nblk from 16 to 1024 (16-byte aligned mask): a lane reads 16 mask bytes, a wave
 // covers 64*16/nblk rows per load, nonzero bytes are counted four at a time in a register, and
 // ranks come from a segmented scan over each row's lanes. Other nblk: a wave reads a row 64
@@ -169,14 +171,28 @@ __global__ __launch_bounds__(kEbThreads) void eb_count_vec(EdgeArgs a, int lcpr)
     if (threadIdx.x == 0) a.wg[blockIdx.x] = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
 }
 
+// A grid of at most kEbOwnPrefix workgroups runs without eb_scan: each emit workgroup adds up
+// the totals of the workgroups before it (at most 16 KB of reads, issued with its mask loads)
+// and the last one writes the edge count; a launch boundary costs more than that.
+constexpr int kEbOwnPrefix = 4096;
+
 template <int G>
-__global__ __launch_bounds__(kEbThreads) void eb_emit_vec(EdgeArgs a, int lcpr) {
-    __shared__ int s_tot[4];
+__global__ __launch_bounds__(kEbThreads) void eb_emit_vec(EdgeArgs a, int lcpr, int own_prefix) {
+    __shared__ int s_tot[4], s_pre[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cpr = 1 << lcpr;
     const int wrows = G * (64 >> lcpr);
     const long long w0 = ((long long)blockIdx.x * 4 + wave) * wrows;
     const VecRows<G> r = vec_load<G>(a, w0, lcpr, lane);
+    long long wg0;  // this workgroup's first edge
+    if (own_prefix) {
+        int part = 0;  // a.wg holds the workgroups' totals
+        for (int i = threadIdx.x; i < (int)blockIdx.x; i += kEbThreads) part += a.wg[i];
+        for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+        if (lane == 0) s_pre[wave] = part;  // published by the barrier below
+    } else {
+        wg0 = a.wg[blockIdx.x];  // a.wg holds exclusive offsets (eb_scan)
+    }
     int cnt[G];
     int wt = 0;
     for (int g = 0; g < G; ++g) {
@@ -186,7 +202,12 @@ __global__ __launch_bounds__(kEbThreads) void eb_emit_vec(EdgeArgs a, int lcpr) 
     for (int o = 32; o > 0; o >>= 1) wt += __shfl_xor(wt, o, 64);
     if (lane == 0) s_tot[wave] = wt;
     __syncthreads();
-    long long e = a.wg[blockIdx.x];  // offset of this wave's first row
+    if (own_prefix) {
+        wg0 = (long long)s_pre[0] + s_pre[1] + s_pre[2] + s_pre[3];
+        if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0)
+            a.group_ptr[a.rows] = (int32_t)(wg0 + s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3]);
+    }
+    long long e = wg0;  // offset of this wave's first row
     for (int w = 0; w < wave; ++w) e += s_tot[w];
     const int seg = lane & (cpr - 1);  // lane's place inside its row
     for (int g = 0; g < G; ++g) {
@@ -252,7 +273,6 @@ pa_status launch_build_edges(const EdgeArgs &a, hipStream_t stream) {
         scope.launch(eb_scan, dim3(1), dim3(1024), 0, a, 0);
         return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
     }
-    LaunchScope scope("build_edges", stream, 3);
     int lcpr = -1;  // 16-byte path when nblk = 16 * 2^lcpr <= 1024 and the mask is aligned
     for (int l = 0; l <= 6; ++l)
         if (a.nblk == 16 << l) lcpr = l;
@@ -261,16 +281,19 @@ pa_status launch_build_edges(const EdgeArgs &a, hipStream_t stream) {
         const int G = rpl >= 4 ? 2 : 8 / rpl;  // G * rpl >= 8
         const long long wg_rows = 4LL * G * rpl;  // >= kEbRows: nv <= nwg, the workspace fits
         const long long nv = (a.rows + wg_rows - 1) / wg_rows;
+        const int own = nv <= kEbOwnPrefix;
+        LaunchScope scope("build_edges", stream, own ? 2 : 3);
         const dim3 grid((unsigned)nv), block(kEbThreads);
         if (G == 2) scope.launch(eb_count_vec<2>, grid, block, 0, a, lcpr);
         else if (G == 4) scope.launch(eb_count_vec<4>, grid, block, 0, a, lcpr);
         else scope.launch(eb_count_vec<8>, grid, block, 0, a, lcpr);
-        scope.launch(eb_scan, dim3(1), dim3(1024), 0, a, (int)nv);
-        if (G == 2) scope.launch(eb_emit_vec<2>, grid, block, 0, a, lcpr);
-        else if (G == 4) scope.launch(eb_emit_vec<4>, grid, block, 0, a, lcpr);
-        else scope.launch(eb_emit_vec<8>, grid, block, 0, a, lcpr);
+        if (!own) scope.launch(eb_scan, dim3(1), dim3(1024), 0, a, (int)nv);
+        if (G == 2) scope.launch(eb_emit_vec<2>, grid, block, 0, a, lcpr, own);
+        else if (G == 4) scope.launch(eb_emit_vec<4>, grid, block, 0, a, lcpr, own);
+        else scope.launch(eb_emit_vec<8>, grid, block, 0, a, lcpr, own);
         return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
     }
+    LaunchScope scope("build_edges", stream, 3);
     scope.launch(eb_count, dim3((unsigned)nwg), dim3(kEbThreads), 0, a);
     scope.launch(eb_scan, dim3(1), dim3(1024), 0, a, (int)nwg);
     scope.launch(eb_emit, dim3((unsigned)nwg), dim3(kEbThreads), 0, a);

@@ -44,6 +44,10 @@ CASES = [
     # denser rows at the workload's nblk: about 490 and 320 edges per 8 rows
     dict(seed=313, tq=64, hkv=8, nblk=512, batch=2, density=0.12),
     dict(seed=314, tq=64, hkv=8, nblk=512, batch=2, density=0.078),
+    # 16 blocks per row, 32 rows per workgroup: 4096 workgroups (each emit workgroup sums the
+    # totals before it) and 4100 (the separate offset scan)
+    dict(seed=315, tq=16384, hkv=8, nblk=16, batch=3, density=0.3),
+    dict(seed=316, tq=16400, hkv=8, nblk=16, batch=3, density=0.3),
 ]
 
 
