@@ -314,6 +314,11 @@ size_t pa_sparse_forward_workspace_size(const pa_sparse_shape *shape);
  *   workspace  at least pa_sparse_forward_workspace_size(shape) bytes, 256-byte aligned
  * Edges may come in any order; the kernel groups them by (batch, h, blk) so each block of keys
  * is read once per group. Merge the partials with pa_split_combine.
+ * Accuracy: the products run on fp16 matrix instructions over hi + lo splits of operands
+ * scaled by powers of two (each query row, each key block, each value dimension outside
+ * [0.5, 2^15)), 22 significant bits per element, or an absolute error bound for elements far
+ * below their group's maximum; the partials are tested against an fp64 evaluation at 1e-4
+ * (relative to max(1, |value|)), including outlier channels and magnitudes down to 1e-39.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (causal != 0, D not 64/128/256,
  * block_size > 128, or > 64 at D = 256), PA_ERR_WORKSPACE, PA_ERR_HIP.
  */
