@@ -523,8 +523,7 @@ __device__ __forceinline__ void edge_groups(const SparseArgs &a, const half_t *K
         // (unconditionally: past the last group it reads edge 0's rows, which go unused; a
         // conditional load would make the compiler copy all of nq on both paths)
         if (kPrefetch) load_q<D>(a, er, grp + NW, nrows, h, ln, qinv, nq);
-        // S^T tiles: lane holds keys 16j + 4g16 + i of row n16, as product sums (hi.hi in acc,
-        // the cross terms hi.lo + lo.hi in acx).
+        // S^T tiles: lane holds keys 16j + 4g16 + i of row n16, as product sums.
         float s[NT][4];
         for (int j = 0; j < NT; ++j) {
             // the cross terms hi.lo + lo.hi and hi.hi of each k-block, in one accumulator
