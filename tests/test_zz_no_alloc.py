@@ -1,7 +1,7 @@
 """GPU check of pa_paged_attention_noalloc (the entry point whose scratch is the library's static
 device array): on consecutive calls, the second with a smaller input, its output equals
 pa_paged_attention's with a workspace of the caller's, bit for bit, and the oracle's within the
-attention bar."""
+attention bar; captured into a HIP graph, every replay equals the eager result."""
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -57,3 +57,48 @@ def test_noalloc_matches_workspace_entry_on_consecutive_calls(num_splits):
     torch.cuda.synchronize()
     assert_bits_equal(again, outs[0], "larger case after the smaller one")
 
+
+
+@pytest.mark.parametrize("num_splits", [pa.PA_SPLITS_AUTO, 3], ids=lambda s: f"S{s}")
+def test_noalloc_graph_replays_match_eager(num_splits):
+    """The no-allocation entry captured into a HIP graph (its scratch address looked up by an
+    eager call first): every replay is bit-identical to the eager result, also after an eager
+    call of another shape has overwritten the shared scratch between replays."""
+    cs = []
+    for case in CASES:
+        case = dict(case)
+        w = W.paged_workload(case.pop("seed"), table="pool", slack=0.2, name="noalloc", **case)
+        c = dev.PagedCase(w)
+        c.append()
+        cs.append(c)
+    big, small = cs
+    torch.cuda.synchronize()
+    ref = _noalloc(big, num_splits)
+    ref_small = _noalloc(small, num_splits)
+    torch.cuda.synchronize()
+    out = torch.empty_like(big.output)
+    w = big.w
+
+    def call():
+        pa.pa_paged_attention_noalloc(big.shape, big.query, big.key_cache, big.value_cache,
+                                      big.cu, big.past, big.block_table, w["scale"], w["causal"],
+                                      num_splits, out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(out, ref, f"replay {i}")
+        other = _noalloc(small, num_splits)  # eager, same scratch, another shape
+        torch.cuda.synchronize()
+        assert_bits_equal(other, ref_small, f"eager smaller call after replay {i}")
